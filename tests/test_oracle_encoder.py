@@ -1,0 +1,212 @@
+"""Pins of the reference encoder (scalar C loop and pure-Python twin).
+
+* hand-derived closed forms (tests/golden/encoding_closed_forms.json): tile
+  counts, nnz and inner-tile bitmap words of the causal, window, Longformer,
+  BigBird and long-sequence masks;
+* hand-built single-element, full and empty masks;
+* round trip: decoding the encoding (decoder written here, independently)
+  gives the mask back;
+* counting identity nnz = 4096 * n_full + popcount of all partial bitmaps;
+* structure: row pointers monotone, column indices strictly ascending and
+  disjoint between the lists, partial tiles neither empty nor full;
+* the C loop and the Python twin agree on small masks.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.encode import encode_c, encode_py
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                   "encoding_closed_forms.json")))
+LOWER = int(GOLD["it_lower_incl_diag"]["value"], 16)
+UPPER = int(GOLD["it_upper_incl_diag"]["value"], 16)
+ONES = (1 << 64) - 1
+
+
+def decode(enc, S):
+    """Independent inverse of the format: rebuild the dense mask."""
+    n = S // 64
+    m = np.zeros((S, S), bool)
+    for I in range(n):
+        for t in range(enc["full_row_ptr"][I], enc["full_row_ptr"][I + 1]):
+            J = int(enc["full_col_idx"][t])
+            m[64 * I:64 * I + 64, 64 * J:64 * J + 64] = True
+        for t in range(enc["part_row_ptr"][I], enc["part_row_ptr"][I + 1]):
+            J = int(enc["part_col_idx"][t])
+            words = enc["part_bitmaps"][t]
+            for it in range(64):
+                w = int(words[it])
+                ir, ic = divmod(it, 8)
+                for bit in range(64):
+                    if (w >> bit) & 1:
+                        r, c = divmod(bit, 8)
+                        m[64 * I + 8 * ir + r, 64 * J + 8 * ic + c] = True
+    return m
+
+
+def check_structure(enc, S):
+    n = S // 64
+    frp, prp = enc["full_row_ptr"], enc["part_row_ptr"]
+    assert frp[0] == 0 and prp[0] == 0
+    assert (np.diff(frp) >= 0).all() and (np.diff(prp) >= 0).all()
+    assert frp[-1] == enc["n_full"] and prp[-1] == enc["n_partial"]
+    for I in range(n):
+        f = enc["full_col_idx"][frp[I]:frp[I + 1]]
+        p = enc["part_col_idx"][prp[I]:prp[I + 1]]
+        assert (np.diff(f) > 0).all() and (np.diff(p) > 0).all()
+        assert not set(f.tolist()) & set(p.tolist())
+        assert ((f >= 0) & (f < n)).all() and ((p >= 0) & (p < n)).all()
+    pc = popcounts(enc["part_bitmaps"])
+    assert ((pc > 0) & (pc < 4096)).all()
+    assert enc["nnz"] == 4096 * enc["n_full"] + int(pc.sum())
+
+
+def popcounts(bm):
+    b = np.ascontiguousarray(bm).view(np.uint8).reshape(len(bm), -1)
+    return np.unpackbits(b, axis=1).sum(axis=1).astype(np.int64)
+
+
+def same(a, b):
+    for key in ("full_row_ptr", "full_col_idx", "part_row_ptr",
+                "part_col_idx", "part_bitmaps"):
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+    for key in ("nnz", "n_full", "n_partial", "n_empty_rows"):
+        assert a[key] == b[key], key
+
+
+def test_single_element():
+    for (r, c) in [(0, 0), (5, 62), (63, 63), (17, 9)]:
+        m = np.zeros((64, 64), bool)
+        m[r, c] = True
+        for enc in (encode_c(m), encode_py(m)):
+            assert enc["n_full"] == 0 and enc["n_partial"] == 1
+            assert enc["nnz"] == 1 and enc["n_empty_rows"] == 63
+            words = [0] * 64
+            words[(r // 8) * 8 + c // 8] = 1 << (8 * (r % 8) + (c % 8))
+            assert enc["part_bitmaps"][0].tolist() == words
+            assert enc["part_col_idx"].tolist() == [0]
+            assert enc["part_row_ptr"].tolist() == [0, 1]
+
+
+def test_full_and_empty():
+    enc = encode_c(np.ones((128, 128), bool))
+    assert enc["n_full"] == 4 and enc["n_partial"] == 0
+    assert enc["full_row_ptr"].tolist() == [0, 2, 4]
+    assert enc["full_col_idx"].tolist() == [0, 1, 0, 1]
+    assert enc["nnz"] == 128 * 128 and enc["n_empty_rows"] == 0
+    enc = encode_c(np.zeros((192, 192), bool))
+    assert enc["n_full"] == 0 and enc["n_partial"] == 0 and enc["nnz"] == 0
+    assert enc["full_row_ptr"].tolist() == [0] * 4
+    assert enc["n_empty_rows"] == 192
+
+
+def test_rejects_ragged():
+    with pytest.raises(ValueError):
+        encode_c(np.ones((100, 100), bool))
+    with pytest.raises(ValueError):
+        encode_py(np.ones((65, 65), bool))
+
+
+@pytest.mark.parametrize("S", [64, 256, 1024])
+def test_causal_closed_form(S):
+    m = np.tril(np.ones((S, S), bool))
+    enc = encode_c(m)
+    n = S // 64
+    assert enc["n_full"] == n * (n - 1) // 2 and enc["n_partial"] == n
+    assert enc["nnz"] == S * (S + 1) // 2
+    assert enc["part_col_idx"].tolist() == list(range(n))
+    for I in range(n):
+        assert enc["full_col_idx"][enc["full_row_ptr"][I]:
+                                   enc["full_row_ptr"][I + 1]].tolist() \
+            == list(range(I))
+    for p in range(n):
+        for it in range(64):
+            ir, ic = divmod(it, 8)
+            want = ONES if ic < ir else (0 if ic > ir else LOWER)
+            assert int(enc["part_bitmaps"][p, it]) == want
+    if S == 256:
+        g = GOLD["causal"]["S256"]
+        for key in g:
+            assert enc[key] == g[key]
+
+
+def test_window_closed_form(config_mask):
+    m = config_mask(2)
+    enc = encode_c(m)
+    g = GOLD["window64_S512"]
+    for key in ("nnz", "n_full", "n_partial", "n_empty_rows"):
+        assert enc[key] == g[key]
+    n = 8
+    p = 0
+    for I in range(n):
+        cols = enc["part_col_idx"][enc["part_row_ptr"][I]:
+                                   enc["part_row_ptr"][I + 1]].tolist()
+        assert cols == [J for J in (I - 1, I + 1) if 0 <= J < n]
+        assert enc["full_col_idx"][enc["full_row_ptr"][I]:
+                                   enc["full_row_ptr"][I + 1]].tolist() == [I]
+        for J in cols:
+            w = enc["part_bitmaps"][p]
+            for ir in range(8):
+                if J == I + 1:
+                    assert int(w[ir * 8 + ir]) == LOWER
+                else:
+                    assert int(w[ir * 8 + ir]) == UPPER
+            if J == I + 1:
+                assert int(w[1]) == 0 and int(w[8]) == ONES
+            p += 1
+
+
+@pytest.mark.parametrize("cid,key", [(3, "longformer_S2048"),
+                                     (4, "bigbird_S4096"),
+                                     (5, "long_random_S16384")])
+def test_workload_closed_forms(cid, key, config_encoding):
+    enc = config_encoding(cid)
+    for k, v in GOLD[key].items():
+        if k != "derivation":
+            assert enc[k] == v, k
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_workload_structure_and_roundtrip(cid, config_mask, config_encoding):
+    m, enc = config_mask(cid), config_encoding(cid)
+    check_structure(enc, m.shape[0])
+    assert enc["nnz"] == int(m.sum())
+    if m.shape[0] <= 2048:
+        assert np.array_equal(decode(enc, m.shape[0]), m)
+
+
+def test_long_sequence_structure(config_mask, config_encoding):
+    m, enc = config_mask(5), config_encoding(5)
+    check_structure(enc, m.shape[0])
+    assert enc["nnz"] == int(np.count_nonzero(m))
+
+
+@pytest.mark.parametrize("seed,p", [(1, 0.01), (2, 0.3), (3, 0.97),
+                                    (4, 0.5)])
+def test_random_roundtrip_and_twin(seed, p):
+    rng = np.random.default_rng(seed)
+    S = 192
+    m = rng.random((S, S)) < p
+    m[:, 64:128] = False                        # an empty OT column
+    m[0:64, 128:192] = True                     # a full OT
+    m[130] = False                              # an empty row
+    enc = encode_c(m)
+    check_structure(enc, S)
+    assert np.array_equal(decode(enc, S), m)
+    same(enc, encode_py(m))
+    assert enc["n_empty_rows"] == int((~m.any(axis=1)).sum())
+
+
+def test_structured_twin(config_mask):
+    same(encode_c(config_mask(1)), encode_py(config_mask(1)))
+    from workloads import mask_family
+    for fam, kw in [("window", {"w": 3}), ("random", {"p": 0.02}),
+                    ("bigbird", {})]:
+        m = mask_family(fam, 256, seed=9, **kw) if fam != "bigbird" else \
+            mask_family("bigbird", 512, seed=9)[:256, :256]
+        enc = encode_c(m)
+        check_structure(enc, 256)
+        same(enc, encode_py(m))
