@@ -1,0 +1,212 @@
+#!/usr/bin/env python
+"""Throughput of the sparse masked MHA forward path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input
+already resident in device memory:
+    encode the [S, S] mask (GPU)  ->  read its statistics (one small copy,
+    synchronises)  ->  pick the kernel (host cost model)  ->  attention
+    forward (GPU, row-wise or block-wise kernel).
+The headline value is effective TFLOP/s: 4*d FLOPs per valid (query, key)
+pair, summed over every (batch, head), divided by the step time.
+
+Default workload: BERT-base-shaped sliding window (B=8, H=12, S=512, d=64,
+fp16, |i-j| <= 64).  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # dense, MI355X
+HBM_PEAK_GBS = 8000.0
+RIDGE = MFMA_PEAK_TFLOPS["f16"] * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload id 1..5 (default 2)")
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "rowwise", "blockwise"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle baseline (0 disables)")
+    ap.add_argument("--out-dtype", default="auto",
+                    choices=["auto", "in", "f32"],
+                    help="output type; auto = input type for fp16, f32 for "
+                         "bf16")
+    return ap.parse_args()
+
+
+def encoding_bytes(st, n):
+    return 4 * 2 * (n + 1) + 4 * (st["n_full"] + st["n_partial"]) + \
+        512 * st["n_partial"]
+
+
+def cpu_baseline(cfg, mask, qkv, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload.
+
+    The dense fp64 oracle costs the same for every query row, so the time
+    of the whole workload is the encoder's time plus the attention time of
+    the sampled rows scaled by (all rows / sampled rows)."""
+    import numpy as np
+    from oracle.attention import attention_rows
+    from oracle.encode import encode_c
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    encode_c(mask)
+    t_enc = time.perf_counter() - t0
+    rows_done = 0
+    t_attn = 0.0
+    blk = min(cfg.S, 1024)
+    q, k, v = qkv
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            for r0 in range(0, cfg.S, blk):
+                t1 = time.perf_counter()
+                attention_rows(q, k, v, mask, b, h, np.arange(r0, r0 + blk))
+                t_attn += time.perf_counter() - t1
+                rows_done += blk
+                if t_attn >= budget_s:
+                    break
+            if t_attn >= budget_s:
+                break
+        if t_attn >= budget_s:
+            break
+    total_rows = cfg.B * cfg.H * cfg.S
+    t_total = t_enc + t_attn * total_rows / rows_done
+    flops = 4.0 * cfg.d * cfg.B * cfg.H * float(mask.sum())
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": (f"scalar C encoder on the full mask + fp64 dense "
+                       f"attention oracle on {rows_done} of {total_rows} "
+                       f"query rows ({rows_done // cfg.S} heads), "
+                       f"extrapolated per row; {t_total:.2f} s estimated "
+                       f"for the whole workload")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus "
+              f"{args.gpus} is not supported (the path needs no collective; "
+              f"run --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import sparse_masked_head_amd as smh
+    from workloads import get_config, make_mask, make_qkv
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.config)
+    mask = make_mask(cfg)
+    qkv = make_qkv(cfg.B, cfg.H, cfg.S, cfg.d, cfg.dtype, seed=cfg.cid)
+    q, k, v = (x.to(dev) for x in qkv)
+    mask_d = torch.from_numpy(mask).to(dev)
+    out_dt = {"auto": torch.float32 if cfg.dtype == "bf16" else q.dtype,
+              "in": q.dtype, "f32": torch.float32}[args.out_dtype]
+    ws = torch.empty(smh.encode_workspace_bytes(cfg.S), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty(q.shape, dtype=out_dt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        enc = smh.encode_mask(mask_d, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        st = smh.mask_stats_get(enc)
+        which = args.kernel if args.kernel != "auto" else smh.select_kernel(
+            st, cfg.B, cfg.H, cfg.d, q.dtype)
+        if ev is not None:
+            ev[2].record(stream)
+        smh.sparse_mha_fwd(q, k, v, enc, kernel=which, out_dtype=out_dt,
+                           stats=st, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+        return st, which
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st, which = step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    fwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    nnz = st["nnz"]
+    BH = cfg.B * cfg.H
+    flops = 4.0 * cfg.d * BH * nnz
+    value = flops / step_s / 1e12
+    eb_in = 2
+    eb_out = out.element_size()
+    n = cfg.S // 64
+    attn_bytes = BH * cfg.S * cfg.d * (3 * eb_in + eb_out) + \
+        encoding_bytes(st, n)
+    ai = flops / attn_bytes
+    fwd_s = fwd_ms / 1e3
+    if ai < RIDGE:
+        roof = {"bound": "hbm", "achieved": attn_bytes / fwd_s / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / fwd_s / 1e12,
+                "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"{which}_fwd"
+    pred_row, pred_blk = smh.select_costs(st, cfg.B, cfg.H, cfg.d, q.dtype)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, mask, qkv, args.cpu_seconds)
+
+    line = {
+        "metric": "effective TFLOP/s on valid QK pairs (4*d FLOPs per valid "
+                  "(query,key) pair) + % of MI355X dense MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded mask)",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S,
+                   "d": cfg.d, "mask": cfg.desc,
+                   "out_dtype": str(out_dt).replace("torch.", ""),
+                   "parallelism": "single GPU"},
+        "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[cfg.dtype],
+        "kernel": which,
+        "encode_ms": enc_ms, "fwd_ms": fwd_ms,
+        "fwd_tflops": flops / fwd_s / 1e12,
+        "fwd_pct_mfma_peak": 100.0 * flops / fwd_s / 1e12 /
+        MFMA_PEAK_TFLOPS[cfg.dtype],
+        "selector_pred_us": {"rowwise": pred_row, "blockwise": pred_blk},
+        "mask_stats": st,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+"""smh: sparse masked multi-head attention forward for AMD MI355X (gfx950).
+
+Python binding of libsmh.so (include/smh.h), argument marshalling only:
+every step runs in the library's HIP kernels.  torch provides device memory
+and the current stream.  Function names are the C names without the
+``smh_`` prefix.
+
+    enc = encode_mask(mask)                 # mask: cuda bool/uint8 [S, S]
+    st = mask_stats_get(enc)                # host statistics (syncs)
+    which = select_kernel(st, B, H, d, torch.float16)
+    o = sparse_mha_fwd(q, k, v, enc, kernel="auto", stats=st)
+"""
+import ctypes
+
+import torch
+
+from ._lib import (SMH_AUTO, SMH_BF16, SMH_BLOCKWISE, SMH_F16, SMH_F32,
+                   SMH_MAX_S, SMH_OK, SMH_ROWWISE, MaskEnc, MaskStats,
+                   SmhError, check, lib, status_string)
+
+__all__ = ["encode_mask", "encode_workspace_bytes", "mask_stats_get",
+           "select_kernel", "select_costs", "sparse_mha_fwd", "version",
+           "MaskEncoding", "SmhError", "KERNELS"]
+
+KERNELS = {"auto": SMH_AUTO, "rowwise": SMH_ROWWISE,
+           "blockwise": SMH_BLOCKWISE}
+_KNAME = {v: k for k, v in KERNELS.items()}
+_DT = {torch.float16: SMH_F16, torch.bfloat16: SMH_BF16,
+       torch.float32: SMH_F32}
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dt(x):
+    if x not in _DT:
+        raise TypeError(f"unsupported dtype {x}")
+    return _DT[x]
+
+
+def version():
+    return lib().smh_version().decode()
+
+
+def encode_workspace_bytes(S):
+    return int(lib().smh_encode_workspace_bytes(int(S)))
+
+
+class MaskEncoding:
+    """A mask's encoding: the device workspace that holds it and the C
+    struct of pointers into that workspace."""
+
+    def __init__(self, workspace, enc, S):
+        self.workspace = workspace
+        self.enc = enc
+        self.S = S
+        self.device = workspace.device
+
+    def arrays(self, stats=None):
+        """Views of the encoding arrays (device tensors), trimmed to their
+        used length (needs the host statistics)."""
+        st = stats if stats is not None else mask_stats_get(self)
+        n = self.S // 64
+        base = self.workspace.data_ptr()
+
+        def view(ptr, count, dtype, width):
+            off = ptr - base
+            return self.workspace[off:off + count * width].view(dtype)
+        e = self.enc
+        return dict(
+            full_row_ptr=view(e.full_row_ptr, n + 1, torch.int32, 4),
+            full_col_idx=view(e.full_col_idx, st["n_full"], torch.int32, 4),
+            part_row_ptr=view(e.part_row_ptr, n + 1, torch.int32, 4),
+            part_col_idx=view(e.part_col_idx, st["n_partial"], torch.int32, 4),
+            part_bitmaps=view(e.part_bitmaps, st["n_partial"] * 64,
+                              torch.int64, 8).view(-1, 64),
+            row_order=view(e.row_order, n, torch.int32, 4))
+
+
+def encode_mask(mask, workspace=None):
+    """Encode a [S, S] device mask (bool or uint8, nonzero = attend)."""
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise TypeError("mask must be bool or uint8")
+    if not mask.is_cuda:
+        raise ValueError("mask must be a device tensor")
+    if mask.dim() != 2 or mask.shape[0] != mask.shape[1]:
+        raise ValueError("mask must be square [S, S]")
+    mask = mask.contiguous()
+    S = int(mask.shape[0])
+    nbytes = encode_workspace_bytes(S)
+    if nbytes == 0:
+        check(lib().smh_encode_mask(None, S, None, 0, ctypes.byref(MaskEnc()),
+                                    None), "smh_encode_mask")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=mask.device)
+    enc = MaskEnc()
+    st = lib().smh_encode_mask(
+        ctypes.c_void_p(mask.data_ptr()), S,
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+        ctypes.byref(enc), _stream(mask.device))
+    check(st, "smh_encode_mask")
+    return MaskEncoding(workspace, enc, S)
+
+
+def mask_stats_get(enc):
+    """Host statistics of an encoding (synchronises the current stream)."""
+    out = MaskStats()
+    check(lib().smh_mask_stats_get(ctypes.byref(enc.enc), ctypes.byref(out),
+                                   _stream(enc.device)), "smh_mask_stats_get")
+    return out.as_dict()
+
+
+def _stats_struct(st):
+    s = MaskStats()
+    for k, _ in MaskStats._fields_:
+        setattr(s, k, int(st[k]))
+    return s
+
+
+def select_kernel(stats, B, H, d, dtype):
+    """'rowwise' or 'blockwise' for this mask and shape (host only)."""
+    out = ctypes.c_int()
+    check(lib().smh_select_kernel(ctypes.byref(_stats_struct(stats)), B, H, d,
+                                  _dt(dtype), ctypes.byref(out)),
+          "smh_select_kernel")
+    return _KNAME[out.value]
+
+
+def select_costs(stats, B, H, d, dtype):
+    """The selector's predicted (rowwise_us, blockwise_us)."""
+    a, b = ctypes.c_double(), ctypes.c_double()
+    check(lib().smh_select_costs(ctypes.byref(_stats_struct(stats)), B, H, d,
+                                 _dt(dtype), ctypes.byref(a), ctypes.byref(b)),
+          "smh_select_costs")
+    return a.value, b.value
+
+
+def sparse_mha_fwd(q, k, v, enc, kernel="auto", out_dtype=None, scale=0.0,
+                   stats=None, out=None):
+    """Masked attention forward over [B, H, S, d] device tensors."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share a [B, H, S, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, S, d = (int(x) for x in q.shape)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, S, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or \
+            not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, S, d] tensor of "
+                         "out_dtype")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    if kernel == "auto" and stats is None:
+        stats = mask_stats_get(enc)
+    st = ctypes.byref(_stats_struct(stats)) if stats is not None else None
+    rc = lib().smh_sparse_mha_fwd(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        B, H, S, d, _dt(q.dtype), _dt(out_dtype), float(scale),
+        ctypes.byref(enc.enc), KERNELS[kernel], st, _stream(q.device))
+    check(rc, "smh_sparse_mha_fwd")
+    return out

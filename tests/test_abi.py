@@ -1,0 +1,164 @@
+"""The C-ABI library loads, exports every symbol include/smh.h declares, and
+rejects bad arguments on the host before touching a device (no GPU needed:
+every call below returns from validation, which makes no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_masked_head_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smh.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smh_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared()
+    assert names == sorted(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert L.status_string(L.SMH_OK) == "ok"
+    assert "workspace" in L.status_string(L.SMH_ENOSPACE)
+    assert L.lib().smh_version().decode().startswith("smh")
+    assert L.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    f = L.lib().smh_encode_workspace_bytes
+    assert f(-64) == 0 and f(65) == 0 and f(L.SMH_MAX_S + 64) == 0
+    assert f(0) > 0
+    small, big = f(64), f(16384)
+    assert 0 < small < big
+    n = 16384 // 64
+    # encoding + scratch: at least two bitmap areas of n^2 * 512 bytes
+    assert big >= 2 * n * n * 512
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # never dereferenced: validation fails first
+
+
+def encode(mask, S, ws, nbytes, enc=True):
+    e = L.MaskEnc()
+    return L.lib().smh_encode_mask(mask, S, ws, nbytes,
+                                   ctypes.byref(e) if enc else None, None)
+
+
+def test_encode_validation():
+    f = L.lib().smh_encode_workspace_bytes
+    assert encode(FAKE, 100, FAKE, 1 << 30) == L.SMH_EUNSUPPORTED
+    assert encode(FAKE, -64, FAKE, 1 << 30) == L.SMH_EINVAL
+    assert encode(FAKE, L.SMH_MAX_S + 64, FAKE, 1 << 40) == L.SMH_EINVAL
+    assert encode(FAKE, 128, FAKE, f(128), enc=False) == L.SMH_EINVAL
+    assert encode(None, 128, FAKE, f(128)) == L.SMH_EINVAL
+    assert encode(FAKE, 128, None, f(128)) == L.SMH_EINVAL
+    assert encode(FAKE, 128, FAKE, f(128) - 1) == L.SMH_ENOSPACE
+    assert encode(ctypes.c_void_p((1 << 20) + 8), 128, FAKE, f(128)) \
+        == L.SMH_EINVAL                       # mask not 16-byte aligned
+    assert encode(FAKE, 128, ctypes.c_void_p((1 << 20) + 16), f(128)) \
+        == L.SMH_EINVAL                       # workspace not 256-byte aligned
+    # mask inside the workspace
+    ws = 1 << 24
+    assert encode(ctypes.c_void_p(ws + 4096), 128, ctypes.c_void_p(ws),
+                  f(128)) == L.SMH_EINVAL
+
+
+def stats(**kw):
+    s = L.MaskStats()
+    base = dict(nnz=61888, S=512, n_full=8, n_partial=14, n_empty_rows=0,
+                max_row_tiles=3)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(s, k, v)
+    return s
+
+
+def select(st, B=8, H=12, d=64, dt=L.SMH_F16):
+    out = ctypes.c_int(-1)
+    rc = L.lib().smh_select_kernel(ctypes.byref(st) if st is not None else
+                                   None, B, H, d, dt, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_select_validation_and_choice():
+    rc, k = select(stats())
+    assert rc == L.SMH_OK and k in (L.SMH_ROWWISE, L.SMH_BLOCKWISE)
+    assert select(None)[0] == L.SMH_EINVAL
+    assert select(stats(), d=96)[0] == L.SMH_EUNSUPPORTED
+    assert select(stats(), dt=L.SMH_F32)[0] == L.SMH_EUNSUPPORTED
+    assert select(stats(), B=-1)[0] == L.SMH_EINVAL
+    assert select(stats(S=500))[0] == L.SMH_EUNSUPPORTED
+    assert select(stats(n_full=100))[0] == L.SMH_EINVAL       # > n_ot^2
+    assert select(stats(nnz=512 * 512 + 1))[0] == L.SMH_EINVAL
+    assert select(stats(max_row_tiles=9))[0] == L.SMH_EINVAL
+    a, b = ctypes.c_double(), ctypes.c_double()
+    assert L.lib().smh_select_costs(ctypes.byref(stats()), 8, 12, 64,
+                                    L.SMH_F16, ctypes.byref(a),
+                                    ctypes.byref(b)) == L.SMH_OK
+    assert a.value > 0 and b.value > 0
+    assert L.lib().smh_select_costs(ctypes.byref(stats()), 8, 12, 64,
+                                    L.SMH_F16, None, None) == L.SMH_OK
+
+
+def test_select_cost_model_monotone():
+    def costs(st, B=8, H=12, d=64):
+        a, b = ctypes.c_double(), ctypes.c_double()
+        assert L.lib().smh_select_costs(ctypes.byref(st), B, H, d, L.SMH_F16,
+                                        ctypes.byref(a), ctypes.byref(b)) == 0
+        return a.value, b.value
+    r1, b1 = costs(stats())
+    r2, b2 = costs(stats(), B=16)
+    assert r2 >= r1 and b2 >= b1
+    r3, b3 = costs(stats(), d=128)
+    assert r3 >= r1 and b3 >= b1
+
+
+def fwd(q=FAKE, k=FAKE, v=FAKE, o=ctypes.c_void_p(1 << 30), B=1, H=1, S=128,
+        d=64, in_dt=L.SMH_F16, out_dt=L.SMH_F16, scale=0.0, enc="ok",
+        which=L.SMH_BLOCKWISE, st=None):
+    e = L.MaskEnc()
+    e.S, e.n_ot = 128, 2
+    for name in ("full_row_ptr", "full_col_idx", "part_row_ptr",
+                 "part_col_idx", "part_bitmaps", "stats", "row_order"):
+        setattr(e, name, 1 << 28)
+    return L.lib().smh_sparse_mha_fwd(
+        q, k, v, o, B, H, S, d, in_dt, out_dt, scale,
+        ctypes.byref(e) if enc == "ok" else None, which,
+        ctypes.byref(st) if st is not None else None, None)
+
+
+def test_fwd_validation():
+    assert fwd(enc=None) == L.SMH_EINVAL
+    assert fwd(S=256) == L.SMH_EINVAL                 # enc->S mismatch
+    assert fwd(S=100) == L.SMH_EUNSUPPORTED
+    assert fwd(d=96) == L.SMH_EUNSUPPORTED
+    assert fwd(in_dt=L.SMH_F32, out_dt=L.SMH_F32) == L.SMH_EUNSUPPORTED
+    assert fwd(out_dt=L.SMH_BF16) == L.SMH_EUNSUPPORTED
+    assert fwd(scale=float("nan")) == L.SMH_EINVAL
+    assert fwd(scale=-1.0) == L.SMH_EINVAL
+    assert fwd(which=7) == L.SMH_EINVAL
+    assert fwd(which=L.SMH_AUTO) == L.SMH_EINVAL      # no statistics
+    assert fwd(which=L.SMH_AUTO, st=stats()) == L.SMH_EINVAL   # S differs
+    assert fwd(B=-1) == L.SMH_EINVAL
+    assert fwd(q=None) == L.SMH_EINVAL
+    assert fwd(q=ctypes.c_void_p((1 << 20) + 2)) == L.SMH_EINVAL  # alignment
+    assert fwd(o=FAKE) == L.SMH_EINVAL                # o overlaps q, k, v
+    # empty batch: a valid no-op that enqueues nothing
+    assert fwd(B=0) == L.SMH_OK and fwd(H=0, q=None) == L.SMH_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libsmh.so"))
+    with pytest.raises(ImportError):
+        L.lib()

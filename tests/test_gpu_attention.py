@@ -1,0 +1,179 @@
+"""GPU attention (both kernels, through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element over the whole output; the
+five workloads at full size are compared on sampled rows that the oracle
+computes one by one.  Bars: max abs error 2e-3 (fp16 inputs) and 1e-2
+(bf16 inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_masked_head_amd as smh
+from oracle.attention import attention, attention_rows
+from tests.gpu_util import TDT, TOL, need_gpu
+from workloads import get_config, make_qkv, mask_family
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = ["blockwise", "rowwise"]
+
+
+def run(q, k, v, mask_np, kernel, out_dtype=None, dev=None):
+    m = torch.from_numpy(np.ascontiguousarray(mask_np)).to(dev)
+    enc = smh.encode_mask(m)
+    st = smh.mask_stats_get(enc)
+    o = smh.sparse_mha_fwd(q.to(dev), k.to(dev), v.to(dev), enc,
+                           kernel=kernel, out_dtype=out_dtype, stats=st)
+    torch.cuda.synchronize()
+    return o
+
+
+def maxerr(o, ref):
+    return float(np.abs(o.double().cpu().numpy() - ref).max())
+
+
+CASES = [  # (B, H, S, d, dtype, family, kw)
+    (1, 2, 64, 64, "f16", "full", {}),
+    (2, 3, 192, 64, "f16", "causal", {}),
+    (1, 2, 320, 128, "f16", "window", {"w": 40}),
+    (1, 3, 256, 64, "bf16", "random", {"p": 0.03}),
+    (2, 1, 384, 128, "bf16", "random", {"p": 0.6}),
+    (1, 2, 512, 64, "f16", "bigbird", {}),
+    (1, 1, 256, 128, "bf16", "longformer", {}),
+]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[5]}-S{c[2]}-d{c[3]}-{c[4]}")
+def test_small_full_output(case, kernel):
+    dev = need_gpu()
+    B, H, S, d, dt, fam, kw = case
+    print(f"attention {kernel} {case}", flush=True)
+    mask = mask_family(fam, S, seed=S + d, **kw)
+    q, k, v = make_qkv(B, H, S, d, dt, seed=S)
+    ref = attention(q, k, v, mask)
+    out_dt = torch.float32 if dt == "bf16" else None
+    o = run(q, k, v, mask, kernel, out_dt, dev)
+    err = maxerr(o, ref)
+    assert err <= TOL[dt], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_edge_rows(kernel, dt):
+    """Empty rows give exactly 0; single-key rows give that V row; the
+    all-masked tile row of a partial pattern is skipped."""
+    dev = need_gpu()
+    S, d = 256, 64
+    rng = np.random.default_rng(11)
+    mask = rng.random((S, S)) < 0.1
+    mask[0:8] = False                  # empty rows
+    mask[70] = False
+    mask[70, 200] = True               # exactly one key
+    mask[128:192] = False              # a whole empty outer-tile row
+    mask[:, 64:128] = False            # an empty outer-tile column
+    q, k, v = make_qkv(1, 2, S, d, dt, seed=12)
+    o = run(q, k, v, mask, kernel, torch.float32, dev).cpu()
+    assert torch.isfinite(o).all()
+    assert (o[:, :, 0:8] == 0).all() and (o[:, :, 128:192] == 0).all()
+    assert torch.allclose(o[:, :, 70], v[:, :, 200].float(), rtol=0,
+                          atol=1e-5)
+    ref = attention(q, k, v, mask)
+    assert float((o.double().numpy() - ref).__abs__().max()) <= TOL[dt]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_in_dtype_output(kernel):
+    """Outputs in the input type: the rounding of O itself is included."""
+    dev = need_gpu()
+    S, d = 256, 128
+    mask = mask_family("causal", S)
+    for dt in ("f16", "bf16"):
+        q, k, v = make_qkv(1, 4, S, d, dt, seed=21)
+        o = run(q, k, v, mask, kernel, None, dev)
+        assert o.dtype == TDT[dt]
+        err = maxerr(o, attention(q, k, v, mask))
+        assert err <= TOL[dt], f"{dt}: max abs err {err}"
+
+
+def test_kernels_agree_and_deterministic():
+    dev = need_gpu()
+    S, d = 512, 64
+    mask = mask_family("random", S, seed=4, p=0.05)
+    q, k, v = make_qkv(2, 2, S, d, "f16", seed=4)
+    a1 = run(q, k, v, mask, "blockwise", torch.float32, dev)
+    a2 = run(q, k, v, mask, "blockwise", torch.float32, dev)
+    b1 = run(q, k, v, mask, "rowwise", torch.float32, dev)
+    b2 = run(q, k, v, mask, "rowwise", torch.float32, dev)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2)
+    assert float((a1 - b1).abs().max()) <= TOL["f16"]
+
+
+def test_scale_argument():
+    dev = need_gpu()
+    S, d = 128, 64
+    mask = mask_family("random", S, seed=5, p=0.4)
+    q, k, v = make_qkv(1, 1, S, d, "f16", seed=5)
+    m = torch.from_numpy(mask).to(dev)
+    enc = smh.encode_mask(m)
+    for kern in KERNELS:
+        o = smh.sparse_mha_fwd(q.to(dev), k.to(dev), v.to(dev), enc,
+                               kernel=kern, out_dtype=torch.float32,
+                               scale=0.05)
+        ref = attention(q, k, v, mask, scale=0.05)
+        assert maxerr(o, ref) <= TOL["f16"]
+
+
+def test_empty_batch_is_noop():
+    dev = need_gpu()
+    enc = smh.encode_mask(torch.ones((64, 64), dtype=torch.bool, device=dev))
+    q = torch.empty((0, 2, 64, 64), dtype=torch.float16, device=dev)
+    o = smh.sparse_mha_fwd(q, q, q, enc, kernel="blockwise")
+    assert o.shape == q.shape
+
+
+_DATA = {}
+
+
+def workload(cid, dev, config_mask):
+    if cid not in _DATA:
+        cfg = get_config(cid)
+        mask = config_mask(cid)
+        q, k, v = make_qkv(cfg.B, cfg.H, cfg.S, cfg.d, cfg.dtype, seed=cid)
+        m = torch.from_numpy(mask).to(dev)
+        enc = smh.encode_mask(m)
+        st = smh.mask_stats_get(enc)
+        _DATA.clear()
+        _DATA[cid] = (cfg, mask, (q, k, v), tuple(x.to(dev) for x in (q, k, v)),
+                      enc, st)
+    return _DATA[cid]
+
+
+def sample_rows(S, mask, rng, n=48):
+    rows = {0, S - 1, 63, 64}
+    rows |= set(rng.integers(0, S, n).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("kernel", ["auto", "blockwise", "rowwise"])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workloads_sampled(cid, kernel, config_mask):
+    dev = need_gpu()
+    cfg, mask, host, devt, enc, st = workload(cid, dev, config_mask)
+    print(f"workload {cid} kernel {kernel}", flush=True)
+    out_dt = torch.float32 if cfg.dtype == "bf16" else None
+    o = smh.sparse_mha_fwd(*devt, enc, kernel=kernel, out_dtype=out_dt,
+                           stats=st)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cid * 7 + len(kernel))
+    heads = [(0, 0), (cfg.B - 1, cfg.H - 1)] + [
+        (int(rng.integers(cfg.B)), int(rng.integers(cfg.H)))]
+    worst = 0.0
+    for b, h in heads:
+        rows = sample_rows(cfg.S, mask, rng)
+        ref = attention_rows(*host, mask, b, h, rows)
+        got = o[b, h, torch.as_tensor(rows, device=dev)].double().cpu().numpy()
+        worst = max(worst, float(np.abs(got - ref).max()))
+    print(f"  max abs err {worst:.3e}", flush=True)
+    assert worst <= TOL[cfg.dtype]
+    assert torch.isfinite(o).all()

@@ -1,0 +1,96 @@
+"""GPU encoder against the scalar C reference encoder: bit-exact equality of
+every array and statistic (integer work)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_masked_head_amd as smh
+from oracle.encode import encode_c
+from tests.gpu_util import (assert_same_encoding, enc_to_host,
+                            expected_row_order, need_gpu)
+from workloads import mask_family
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_encode(mask_np, dev):
+    m = torch.from_numpy(np.ascontiguousarray(mask_np)).to(dev)
+    enc = smh.encode_mask(m)
+    st = smh.mask_stats_get(enc)
+    return enc, st, enc_to_host(enc, st)
+
+
+def check(mask_np, dev):
+    enc, st, got = gpu_encode(mask_np, dev)
+    ref = encode_c(mask_np)
+    assert_same_encoding(got, ref)
+    order, mrt = expected_row_order(ref)
+    assert got["row_order"].tolist() == order
+    assert st["max_row_tiles"] == mrt
+    return enc, st, got
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload_masks_bit_exact(cid, config_mask, config_encoding):
+    dev = need_gpu()
+    print(f"encoder workload {cid}", flush=True)
+    m = config_mask(cid)
+    enc, st, got = gpu_encode(m, dev)
+    ref = config_encoding(cid)
+    assert_same_encoding(got, ref)
+    order, mrt = expected_row_order(ref)
+    assert got["row_order"].tolist() == order and st["max_row_tiles"] == mrt
+
+
+@pytest.mark.parametrize("fam,S,kw", [
+    ("empty", 256, {}), ("full", 256, {}), ("causal", 64, {}),
+    ("window", 320, {"w": 5}), ("random", 512, {"p": 0.001}),
+    ("random", 512, {"p": 0.5}), ("random", 448, {"p": 0.999}),
+    ("bigbird", 1024, {})])
+def test_corner_and_random_masks(fam, S, kw):
+    dev = need_gpu()
+    check(mask_family(fam, S, seed=S, **kw), dev)
+
+
+def test_single_elements_and_diagonal():
+    dev = need_gpu()
+    S = 192
+    m = np.zeros((S, S), bool)
+    for (i, j) in [(0, 0), (63, 64), (100, 191), (191, 0), (130, 77)]:
+        m[i, j] = True
+    check(m, dev)
+    check(np.eye(S, dtype=bool), dev)
+
+
+def test_nonzero_bytes_count_as_valid():
+    dev = need_gpu()
+    S = 128
+    rng = np.random.default_rng(5)
+    vals = rng.choice(np.array([0, 1, 2, 127, 128, 255], np.uint8), (S, S))
+    enc_u8, _, got = gpu_encode(vals, dev)
+    assert_same_encoding(got, encode_c(vals != 0))
+
+
+def test_empty_sequence_and_ragged():
+    dev = need_gpu()
+    enc = smh.encode_mask(torch.zeros((0, 0), dtype=torch.bool, device=dev))
+    st = smh.mask_stats_get(enc)
+    assert st["nnz"] == 0 and st["n_full"] == 0 and st["n_partial"] == 0
+    with pytest.raises(smh.SmhError) as e:
+        smh.encode_mask(torch.ones((100, 100), dtype=torch.bool, device=dev))
+    assert e.value.status == 2
+
+
+def test_deterministic_and_reusable_workspace():
+    dev = need_gpu()
+    m = mask_family("random", 640, seed=3, p=0.2)
+    _, _, a = gpu_encode(m, dev)
+    # a dirty, reused workspace gives the same result
+    ws = torch.full((smh.encode_workspace_bytes(640),), 0xAB,
+                    dtype=torch.uint8, device=dev)
+    enc = smh.encode_mask(torch.from_numpy(m).to(dev), workspace=ws)
+    b = enc_to_host(enc, smh.mask_stats_get(enc))
+    assert_same_encoding(b, a)
+    enc = smh.encode_mask(torch.from_numpy(~m).to(dev), workspace=ws)
+    c = enc_to_host(enc, smh.mask_stats_get(enc))
+    assert_same_encoding(c, encode_c(~m))
