@@ -157,8 +157,12 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
  *   B, H >= 0 (0 is a no-op); S == enc->S; d in {64, 128}.
  *   scale: score multiplier, finite and >= 0; 0 means 1/sqrt(d).
  *   enc: encoding of the [S][S] mask shared by every (b, h).
- *   which: SMH_ROWWISE, SMH_BLOCKWISE, or SMH_AUTO (then st is required and
- *          smh_select_kernel decides).
+ *   which: SMH_ROWWISE, SMH_BLOCKWISE, or SMH_AUTO.  With SMH_AUTO and st
+ *          non-NULL the host decides (smh_select_kernel).  With SMH_AUTO and
+ *          st NULL the same model is evaluated on the device from the
+ *          statistics the encoder wrote: both kernels are enqueued and the
+ *          one not chosen returns before reading or writing anything, so no
+ *          host synchronisation is needed.
  * Arithmetic: fp32 scores, softmax statistics and accumulators.  The
  * block-wise kernel rounds the probabilities to in_dt for its matrix-core
  * probability-times-V product (the row sums use the rounded values); the

@@ -138,7 +138,11 @@ def select_costs(stats, B, H, d, dtype):
 
 def sparse_mha_fwd(q, k, v, enc, kernel="auto", out_dtype=None, scale=0.0,
                    stats=None, out=None):
-    """Masked attention forward over [B, H, S, d] device tensors."""
+    """Masked attention forward over [B, H, S, d] device tensors.
+
+    kernel="auto" with stats=None lets the device decide from the
+    encoding's statistics (no host synchronisation); with host stats the
+    host decides.  kernel="rowwise" / "blockwise" forces one kernel."""
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share a [B, H, S, d] shape")
     if not (q.dtype == k.dtype == v.dtype):
@@ -156,8 +160,6 @@ def sparse_mha_fwd(q, k, v, enc, kernel="auto", out_dtype=None, scale=0.0,
                          "out_dtype")
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
-    if kernel == "auto" and stats is None:
-        stats = mask_stats_get(enc)
     st = ctypes.byref(_stats_struct(stats)) if stats is not None else None
     rc = lib().smh_sparse_mha_fwd(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),

@@ -15,7 +15,7 @@ OUT = os.path.join(HERE, "libsmh.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["encode.hip", "blockwise.hip", "rowwise.hip", "select.cpp",
+SOURCES = ["encode.hip", "blockwise.hip", "rowwise.hip", "select.hip",
            "api.hip"]
 
 COMMON = [

@@ -86,7 +86,8 @@ smh_status smh_encode_mask(const uint8_t *mask, int32_t S, void *workspace,
         e.part_bitmaps = (uint64_t *)(ws + L.part_bitmaps);
         e.stats = (int64_t *)(ws + L.stats);
         e.row_order = (int32_t *)(ws + L.row_order);
-        if (launch_encode(mask, S, ws, L, (hipStream_t)stream) != hipSuccess)
+        if (launch_encode(mask, S, ws, L, e, (hipStream_t)stream) !=
+            hipSuccess)
             return SMH_EHIP;
         *enc_out = e;
         return SMH_OK;
@@ -157,7 +158,7 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
         // block-wise kernel, one wavefront per (head, 8 query rows) for the
         // row-wise kernel
         if (BH * (S / 8) > (int64_t)INT32_MAX) return SMH_EINVAL;
-        if (which == SMH_AUTO) {
+        if (which == SMH_AUTO && st) {
             smh_status s2 = check_select(st, B, H, d, in_dt);
             if (s2 != SMH_OK) return s2;
             if (st->S != S) return SMH_EINVAL;
@@ -176,16 +177,27 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
         if (overlaps(o, out_b, q, in_b) || overlaps(o, out_b, k, in_b) ||
             overlaps(o, out_b, v, in_b))
             return SMH_EINVAL;
+        const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
+        const hipStream_t hs = (hipStream_t)stream;
+        hipError_t e;
+        if (which == SMH_AUTO && !st) {
+            // decided on the device from the encoding's statistics: both
+            // kernels are launched and the one not chosen exits at once
+            e = launch_rowwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc, *enc,
+                               1, hs);
+            if (e == hipSuccess)
+                e = launch_blockwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
+                                     *enc, 1, hs);
+            return e == hipSuccess ? SMH_OK : SMH_EHIP;
+        }
         if (which == SMH_AUTO)
             which = select_kernel(*st, BH, d, in_dt, nullptr, nullptr);
-        const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
-        hipError_t e;
         if (which == SMH_ROWWISE)
             e = launch_rowwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc, *enc,
-                               (hipStream_t)stream);
+                               0, hs);
         else
             e = launch_blockwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
-                                 *enc, (hipStream_t)stream);
+                                 *enc, 0, hs);
         return e == hipSuccess ? SMH_OK : SMH_EHIP;
     } catch (...) {
         return SMH_EHIP;

@@ -19,8 +19,9 @@
 //     v_mfma_f32_16x16x32 (A = K rows from LDS, B = its Q rows held in
 //     registers for the whole loop).  In this accumulator layout lane l
 //     holds the scores of query l%16 against keys 16t + 4(l/16) + i;
-//   * partial tiles reset masked scores to -inf from the tile's bitmaps
-//     (staged into LDS as one 64-bit key mask per query row);
+//   * partial tiles reset masked scores to -inf from the tile's bitmaps,
+//     staged into LDS with the tile; each lane reads the four bytes (one
+//     per 16-key sub-tile) that hold its query row's bits;
 //   * online softmax in base 2 (running max m and running sum l per query);
 //     only the 4 lanes that share a query exchange values (2 shuffles);
 //   * O^T += V^T P^T with the same MFMA: P^T is the B operand straight from
@@ -28,6 +29,7 @@
 //     from LDS, so no probability ever goes through LDS, and the O rows a
 //     lane holds belong to the same query as its softmax state.
 // Epilogue: O / l (0 for a row with no valid key), stored in the output type.
+#include "select_model.h"
 #include "smh_internal.h"
 
 namespace smh {
@@ -36,6 +38,7 @@ namespace {
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 template <typename T> struct Frag;
 template <> struct Frag<_Float16> {
@@ -76,19 +79,102 @@ template <int D> struct Lds {
     static constexpr int STAGE_BYTES = 2 * (K_ELEMS + V_ELEMS) + 64 * 8;
 };
 
+// Row sum of two probabilities already rounded to the input type, exact
+// products with 1 accumulated in fp32 (v_dot2).
+template <typename T> __device__ inline float sum2(uint32_t pair, float acc);
+template <> __device__ inline float sum2<_Float16>(uint32_t pair, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 x, one = {(_Float16)1.0f, (_Float16)1.0f};
+    __builtin_memcpy(&x, &pair, 4);
+    return __builtin_amdgcn_fdot2(x, one, acc, false);
+}
+template <> __device__ inline float sum2<__bf16>(uint32_t pair, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    b2 x, one = {(__bf16)1.0f, (__bf16)1.0f};
+    __builtin_memcpy(&x, &pair, 4);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+
+// Registers that carry one K/V tile (and a partial tile's 64 words) from
+// global memory to LDS.
+template <int D> struct Staging {
+    static constexpr int KCH = 64 * D / 8 / 256;   // 16-byte K chunks/thread
+    static constexpr int VT = 32 * (D / 8) / 256;  // V transpose tasks/thread
+    u4_t kr[KCH], va[VT], vb[VT];
+    uint64_t bw;
+};
+
+// Issue the global loads of tile J (K rows contiguous: thread t takes
+// 16-byte chunks t, t+256, ...; V: thread t takes keys 2kp, 2kp+1 of
+// 8-column chunk dc for the transpose).
+template <int D, typename TIn>
+__device__ __attribute__((always_inline)) inline void fetch_tile(
+    Staging<D> &st, const TIn *__restrict__ Kh, const TIn *__restrict__ Vh,
+    int J, const uint64_t *__restrict__ words, int t) {
+    const TIn *kt = Kh + (size_t)J * 64 * D;
+    const TIn *vt = Vh + (size_t)J * 64 * D;
+#pragma unroll
+    for (int i = 0; i < Staging<D>::KCH; ++i)
+        st.kr[i] = *reinterpret_cast<const u4_t *>(kt + (t + 256 * i) * 8);
+#pragma unroll
+    for (int i = 0; i < Staging<D>::VT; ++i) {
+        const int e = t + 256 * i;
+        const int dc = e % (D / 8), kp = e / (D / 8);
+        st.va[i] = *reinterpret_cast<const u4_t *>(vt + (2 * kp) * D + 8 * dc);
+        st.vb[i] = *reinterpret_cast<const u4_t *>(vt + (2 * kp + 1) * D + 8 * dc);
+    }
+    if (words && t < 64) st.bw = words[t];
+}
+
+// Write a fetched tile into one LDS stage: K row-major (padded rows), V
+// transposed (row = output column, keys contiguous), the 64 words raw.
+template <int D, typename TIn>
+__device__ __attribute__((always_inline)) inline void stage_tile(
+    const Staging<D> &st, char *base, bool partial, int t) {
+    using L = Lds<D>;
+    TIn *ks = reinterpret_cast<TIn *>(base);
+    uint32_t *vs = reinterpret_cast<uint32_t *>(ks + L::K_ELEMS);
+    uint64_t *wd = reinterpret_cast<uint64_t *>(base + 2 * (L::K_ELEMS + L::V_ELEMS));
+#pragma unroll
+    for (int i = 0; i < Staging<D>::KCH; ++i) {
+        const int e = t + 256 * i;
+        const int row = e / (D / 8), col = (e % (D / 8)) * 8;
+        *reinterpret_cast<u4_t *>(ks + row * L::KLD + col) = st.kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Staging<D>::VT; ++i) {
+        const int e = t + 256 * i;
+        const int dc = e % (D / 8), kp = e / (D / 8);
+        const u4_t a = st.va[i], b = st.vb[i];
+        uint32_t *dst = vs + (8 * dc * L::VLD + 2 * kp) / 2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // elements 2k, 2k+1 of keys 2kp (low half) and 2kp+1 (high)
+            dst[(2 * k) * L::VLD / 2] = (a[k] & 0xFFFFu) | (b[k] << 16);
+            dst[(2 * k + 1) * L::VLD / 2] = (a[k] >> 16) | (b[k] & 0xFFFF0000u);
+        }
+    }
+    if (partial && t < 64) wd[t] = st.bw;
+}
+
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, 2) void blockwise_fwd(
     const TIn *__restrict__ Q, const TIn *__restrict__ K,
     const TIn *__restrict__ V, TOut *__restrict__ O, int S, int BH, float c,
     const int32_t *__restrict__ frp, const int32_t *__restrict__ fci,
     const int32_t *__restrict__ prp, const int32_t *__restrict__ pci,
-    const uint64_t *__restrict__ bm, const int32_t *__restrict__ row_order) {
+    const uint64_t *__restrict__ bm, const int32_t *__restrict__ row_order,
+    const int64_t *__restrict__ stats, int auto_select) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     using L = Lds<D>;
-    constexpr int KCH = 64 * D / 8 / 256;   // 16-byte K chunks per thread
-    constexpr int VT = 32 * (D / 8) / 256;  // V transpose tasks per thread
     extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    // SMH_AUTO without host statistics: run only if the cost model picks
+    // this kernel (every workgroup of both launches reaches the same answer)
+    if (auto_select &&
+        select_on_device(stats, BH, D, __is_same(TIn, __bf16) ? 1 : 0) != 2)
+        return;
 
     // heavy rows first across all heads; one head's rows are BH apart, so
     // with BH % 8 == 0 every workgroup of a head lands on the same XCD.
@@ -100,15 +186,16 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int lq = l & 15, g = l >> 4;
+    const int r = 16 * w + lq;  // this lane's query row inside the tile
 
     const int f0 = frp[I], nF = frp[I + 1] - f0;
     const int p0 = prp[I], nP = prp[I + 1] - p0;
     const int nT = nF + nP;
 
-    // this lane's Q rows as the B operand: query lq, d = 32s + 8g + 0..7
+    // this lane's Q rows as the B operand: query r, d = 32s + 8g + 0..7
     frag qf[D / 32];
     {
-        const TIn *qrow = Qh + (size_t)(64 * I + 16 * w + lq) * D;
+        const TIn *qrow = Qh + (size_t)(64 * I + r) * D;
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
             qf[s] = *reinterpret_cast<const frag *>(qrow + 32 * s + 8 * g);
@@ -119,80 +206,39 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(
     for (int i = 0; i < D / 16; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    uint4 kr[KCH], va[VT], vb[VT];
-    uint64_t bw = 0;
-
+    Staging<D> stg;
+    stg.bw = 0;
+    auto tile_words = [&](int idx) -> const uint64_t * {
+        return idx < nF ? nullptr : bm + (size_t)(p0 + idx - nF) * 64;
+    };
     auto tile_col = [&](int idx) {
         return idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
     };
-    auto fetch = [&](int idx) {
-        const int J = tile_col(idx);
-        const TIn *kt = Kh + (size_t)J * 64 * D;
-        const TIn *vt = Vh + (size_t)J * 64 * D;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i)
-            kr[i] = *reinterpret_cast<const uint4 *>(kt + (t + 256 * i) * 8);
-#pragma unroll
-        for (int i = 0; i < VT; ++i) {
-            const int e = t + 256 * i;
-            const int dc = e % (D / 8), kp = e / (D / 8);
-            va[i] = *reinterpret_cast<const uint4 *>(vt + (2 * kp) * D + 8 * dc);
-            vb[i] =
-                *reinterpret_cast<const uint4 *>(vt + (2 * kp + 1) * D + 8 * dc);
-        }
-        if (idx >= nF && t < 64) bw = bm[(size_t)(p0 + idx - nF) * 64 + t];
-    };
-    auto stage = [&](int buf, bool partial) {
-        char *base = smem + buf * L::STAGE_BYTES;
-        TIn *ks = reinterpret_cast<TIn *>(base);
-        TIn *vs = ks + L::K_ELEMS;
-        uint8_t *rm = reinterpret_cast<uint8_t *>(vs + L::V_ELEMS);
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int e = t + 256 * i;
-            const int row = e / (D / 8), col = (e % (D / 8)) * 8;
-            *reinterpret_cast<uint4 *>(ks + row * L::KLD + col) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VT; ++i) {
-            const int e = t + 256 * i;
-            const int dc = e % (D / 8), kp = e / (D / 8);
-            const uint32_t a[4] = {va[i].x, va[i].y, va[i].z, va[i].w};
-            const uint32_t b[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
-            uint32_t *dst = reinterpret_cast<uint32_t *>(vs);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                // element 2k and 2k+1 of keys 2kp (low half) and 2kp+1
-                dst[((8 * dc + 2 * k) * L::VLD + 2 * kp) / 2] =
-                    (a[k] & 0xFFFFu) | (b[k] << 16);
-                dst[((8 * dc + 2 * k + 1) * L::VLD + 2 * kp) / 2] =
-                    (a[k] >> 16) | (b[k] & 0xFFFF0000u);
-            }
-        }
-        if (partial && t < 64) {
-            // inner tile ir*8+ic -> byte ic of the key mask of row 8ir+r
-            const int ir = t >> 3, ic = t & 7;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                rm[(8 * ir + r) * 8 + ic] = (uint8_t)(bw >> (8 * r));
-        }
-    };
 
     if (nT > 0) {
-        fetch(0);
-        stage(0, nF == 0);
+        fetch_tile<D, TIn>(stg, Kh, Vh, tile_col(0), tile_words(0), t);
+        stage_tile<D, TIn>(stg, smem, nF == 0, t);
     }
     __syncthreads();
+
+    // per-lane LDS offsets (elements / bytes) shared by both buffers
+    const int k_off = lq * L::KLD + 8 * g;
+    const int v_off = lq * L::VLD + 4 * g;
+    const int b_off = ((r >> 3) * 8 + (g >> 1)) * 8 + (r & 7);
+    const int nib = 4 * (g & 1);
 
     for (int it = 0; it < nT; ++it) {
         const int buf = it & 1;
         const bool partial = it >= nF;
-        if (it + 1 < nT) fetch(it + 1);
+        if (it + 1 < nT)
+            fetch_tile<D, TIn>(stg, Kh, Vh, tile_col(it + 1),
+                               tile_words(it + 1), t);
 
         const char *base = smem + buf * L::STAGE_BYTES;
-        const TIn *ks = reinterpret_cast<const TIn *>(base);
-        const TIn *vs = ks + L::K_ELEMS;
-        const uint64_t *rm = reinterpret_cast<const uint64_t *>(vs + L::V_ELEMS);
+        const TIn *ks = reinterpret_cast<const TIn *>(base) + k_off;
+        const TIn *vs = reinterpret_cast<const TIn *>(base) + L::K_ELEMS + v_off;
+        const uint8_t *wbytes =
+            reinterpret_cast<const uint8_t *>(base + 2 * (L::K_ELEMS + L::V_ELEMS)) + b_off;
 
         // S^T = K Q^T: four 16-key sub-tiles
         f4_t sc[4];
@@ -202,58 +248,65 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
                 const frag a = *reinterpret_cast<const frag *>(
-                    ks + (16 * st + lq) * L::KLD + 32 * s + 8 * g);
+                    ks + 16 * st * L::KLD + 32 * s);
                 sc[st] = F::mfma(a, qf[s], sc[st]);
             }
         }
         if (partial) {
-            const uint64_t keys = rm[16 * w + lq];
+            // keys 16st + 4g + i of row r: bits 4(g&1)+i of byte r&7 of
+            // inner tile (r>>3, 2st + (g>>1))
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
+            for (int st = 0; st < 4; ++st) {
+                const uint32_t bits = (uint32_t)wbytes[16 * st] >> nib;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (!((keys >> (16 * st + 4 * g + i)) & 1))
-                        sc[st][i] = -INFINITY;
+                    if (!((bits >> i) & 1u)) sc[st][i] = -INFINITY;
+            }
         }
-        float mx = sc[0][0];
+        float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[st][i]);
+        for (int st = 1; st < 4; ++st)
+            mx = fmaxf(mx, fmaxf(fmaxf(sc[st][0], sc[st][1]),
+                                 fmaxf(sc[st][2], sc[st][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f((m_run - m_use) * c);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
         const float mc = m_use * c;
         m_run = m_new;
 
         // P^T as B operand: keys 32u + 4g + j (j < 4), 32u + 16 + 4g + j - 4
         frag pf[2];
-        float lsum = 0.f;
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const TIn p = (TIn)exp2f(fmaf(sc[st][i], c, -mc));
-                pf[st >> 1][(st & 1) * 4 + i] = p;
-                lsum += (float)p;
-            }
-        l_run = l_run * alpha + lsum;
+            for (int i = 0; i < 4; ++i)
+                pf[st >> 1][(st & 1) * 4 + i] =
+                    (TIn)__builtin_amdgcn_exp2f(fmaf(sc[st][i], c, -mc));
+        float lsum = 0.f;
 #pragma unroll
-        for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+        for (int u = 0; u < 2; ++u) {
+            uint32_t pw[4];
+            __builtin_memcpy(pw, &pf[u], 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
+        }
+        l_run = l_run * alpha + lsum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+        }
 
         // O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-            const TIn *vrow = vs + (16 * dt + lq) * L::VLD;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-                const u2 lo =
-                    *reinterpret_cast<const u2 *>(vrow + 32 * u + 4 * g);
-                const u2 hi =
-                    *reinterpret_cast<const u2 *>(vrow + 32 * u + 16 + 4 * g);
+                const TIn *vp = vs + 16 * dt * L::VLD + 32 * u;
+                const u2 lo = *reinterpret_cast<const u2 *>(vp);
+                const u2 hi = *reinterpret_cast<const u2 *>(vp + 16);
                 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
                 const u4 packed = {lo[0], lo[1], hi[0], hi[1]};
                 frag a;
@@ -262,7 +315,9 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(
             }
         }
 
-        if (it + 1 < nT) stage(buf ^ 1, it + 1 >= nF);
+        if (it + 1 < nT)
+            stage_tile<D, TIn>(stg, smem + (buf ^ 1) * L::STAGE_BYTES,
+                               it + 1 >= nF, t);
         __syncthreads();
     }
 
@@ -271,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    TOut *orow = O + head + (size_t)(64 * I + 16 * w + lq) * D;
+    TOut *orow = O + head + (size_t)(64 * I + r) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
         store4<TOut>(orow + 16 * dt + 4 * g, acc[dt] * inv);
@@ -280,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(
 template <int D, typename TIn, typename TOut>
 hipError_t launch_t(const void *q, const void *k, const void *v, void *o,
                     int BH, int S, float scale, const smh_mask_enc &enc,
-                    hipStream_t stream) {
+                    int auto_select, hipStream_t stream) {
     const int n = enc.n_ot;
     const size_t smem = 2 * Lds<D>::STAGE_BYTES;
     auto kern = blockwise_fwd<D, TIn, TOut>;
@@ -296,28 +351,32 @@ hipError_t launch_t(const void *q, const void *k, const void *v, void *o,
                        stream, (const TIn *)q, (const TIn *)k, (const TIn *)v,
                        (TOut *)o, S, BH, scale * kLog2e, enc.full_row_ptr,
                        enc.full_col_idx, enc.part_row_ptr, enc.part_col_idx,
-                       enc.part_bitmaps, enc.row_order);
+                       enc.part_bitmaps, enc.row_order, enc.stats, auto_select);
     return hipGetLastError();
 }
 
 template <int D, typename TIn>
 hipError_t dispatch_out(int out_dt, const void *q, const void *k,
                         const void *v, void *o, int BH, int S, float scale,
-                        const smh_mask_enc &enc, hipStream_t stream) {
+                        const smh_mask_enc &enc, int auto_select,
+                        hipStream_t stream) {
     if (out_dt == SMH_F32)
-        return launch_t<D, TIn, float>(q, k, v, o, BH, S, scale, enc, stream);
-    return launch_t<D, TIn, TIn>(q, k, v, o, BH, S, scale, enc, stream);
+        return launch_t<D, TIn, float>(q, k, v, o, BH, S, scale, enc,
+                                       auto_select, stream);
+    return launch_t<D, TIn, TIn>(q, k, v, o, BH, S, scale, enc, auto_select,
+                                 stream);
 }
 
 template <int D>
 hipError_t dispatch_in(int in_dt, int out_dt, const void *q, const void *k,
                        const void *v, void *o, int BH, int S, float scale,
-                       const smh_mask_enc &enc, hipStream_t stream) {
+                       const smh_mask_enc &enc, int auto_select,
+                       hipStream_t stream) {
     if (in_dt == SMH_F16)
         return dispatch_out<D, _Float16>(out_dt, q, k, v, o, BH, S, scale, enc,
-                                         stream);
+                                         auto_select, stream);
     return dispatch_out<D, __bf16>(out_dt, q, k, v, o, BH, S, scale, enc,
-                                   stream);
+                                   auto_select, stream);
 }
 
 }  // namespace
@@ -325,13 +384,13 @@ hipError_t dispatch_in(int in_dt, int out_dt, const void *q, const void *k,
 hipError_t launch_blockwise(const void *q, const void *k, const void *v,
                             void *o, int B, int H, int S, int d, int in_dt,
                             int out_dt, float scale, const smh_mask_enc &enc,
-                            hipStream_t stream) {
+                            int auto_select, hipStream_t stream) {
     const int BH = B * H;
     if (d == 64)
         return dispatch_in<64>(in_dt, out_dt, q, k, v, o, BH, S, scale, enc,
-                               stream);
+                               auto_select, stream);
     return dispatch_in<128>(in_dt, out_dt, q, k, v, o, BH, S, scale, enc,
-                            stream);
+                            auto_select, stream);
 }
 
 }  // namespace smh

@@ -23,6 +23,7 @@
 //     wavefront's LDS slice, then the wavefront walks only the keys some
 //     row can see (the ballot of non-empty lanes) and accumulates p * V.
 // Probabilities stay in fp32 in this kernel.
+#include "select_model.h"
 #include "smh_internal.h"
 
 namespace smh {
@@ -95,11 +96,17 @@ __global__ __launch_bounds__(256) void rowwise_fwd(
     long long n_groups, float c, const int32_t *__restrict__ frp,
     const int32_t *__restrict__ fci, const int32_t *__restrict__ prp,
     const int32_t *__restrict__ pci, const uint64_t *__restrict__ bm,
-    const int32_t *__restrict__ row_order) {
+    const int32_t *__restrict__ row_order, const int64_t *__restrict__ stats,
+    int auto_select) {
     constexpr int E = D / 64;  // output columns per lane
     __shared__ __attribute__((aligned(16))) float pbuf[4][64][R];
     __shared__ __attribute__((aligned(16))) uint32_t qbuf[4][R][D / 2];
 
+    // SMH_AUTO without host statistics: run only if the cost model picks
+    // this kernel (every workgroup of both launches reaches the same answer)
+    if (auto_select &&
+        select_on_device(stats, BH, D, __is_same(TIn, __bf16) ? 1 : 0) != 1)
+        return;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long long gw = (long long)blockIdx.x * 4 + w;
     if (gw >= n_groups) return;  // whole wavefront leaves; no barriers follow
@@ -231,35 +238,40 @@ __global__ __launch_bounds__(256) void rowwise_fwd(
 template <int D, typename TIn, typename TOut>
 hipError_t launch_t(const void *q, const void *k, const void *v, void *o,
                     int BH, int S, float scale, const smh_mask_enc &enc,
-                    hipStream_t stream) {
+                    int auto_select, hipStream_t stream) {
     const long long n_groups = (long long)BH * (S / 8);
     const unsigned blocks = (unsigned)((n_groups + 3) / 4);
     hipLaunchKernelGGL((rowwise_fwd<D, TIn, TOut>), dim3(blocks), dim3(256), 0,
                        stream, (const TIn *)q, (const TIn *)k, (const TIn *)v,
                        (TOut *)o, S, BH, n_groups, scale * 1.4426950408889634f,
                        enc.full_row_ptr, enc.full_col_idx, enc.part_row_ptr,
-                       enc.part_col_idx, enc.part_bitmaps, enc.row_order);
+                       enc.part_col_idx, enc.part_bitmaps, enc.row_order,
+                       enc.stats, auto_select);
     return hipGetLastError();
 }
 
 template <int D, typename TIn>
 hipError_t dispatch_out(int out_dt, const void *q, const void *k,
                         const void *v, void *o, int BH, int S, float scale,
-                        const smh_mask_enc &enc, hipStream_t stream) {
+                        const smh_mask_enc &enc, int auto_select,
+                        hipStream_t stream) {
     if (out_dt == SMH_F32)
-        return launch_t<D, TIn, float>(q, k, v, o, BH, S, scale, enc, stream);
-    return launch_t<D, TIn, TIn>(q, k, v, o, BH, S, scale, enc, stream);
+        return launch_t<D, TIn, float>(q, k, v, o, BH, S, scale, enc,
+                                       auto_select, stream);
+    return launch_t<D, TIn, TIn>(q, k, v, o, BH, S, scale, enc, auto_select,
+                                 stream);
 }
 
 template <int D>
 hipError_t dispatch_in(int in_dt, int out_dt, const void *q, const void *k,
                        const void *v, void *o, int BH, int S, float scale,
-                       const smh_mask_enc &enc, hipStream_t stream) {
+                       const smh_mask_enc &enc, int auto_select,
+                       hipStream_t stream) {
     if (in_dt == SMH_F16)
         return dispatch_out<D, _Float16>(out_dt, q, k, v, o, BH, S, scale, enc,
-                                         stream);
+                                         auto_select, stream);
     return dispatch_out<D, __bf16>(out_dt, q, k, v, o, BH, S, scale, enc,
-                                   stream);
+                                   auto_select, stream);
 }
 
 }  // namespace
@@ -267,13 +279,13 @@ hipError_t dispatch_in(int in_dt, int out_dt, const void *q, const void *k,
 hipError_t launch_rowwise(const void *q, const void *k, const void *v,
                           void *o, int B, int H, int S, int d, int in_dt,
                           int out_dt, float scale, const smh_mask_enc &enc,
-                          hipStream_t stream) {
+                          int auto_select, hipStream_t stream) {
     const int BH = B * H;
     if (d == 64)
         return dispatch_in<64>(in_dt, out_dt, q, k, v, o, BH, S, scale, enc,
-                               stream);
+                               auto_select, stream);
     return dispatch_in<128>(in_dt, out_dt, q, k, v, o, BH, S, scale, enc,
-                            stream);
+                            auto_select, stream);
 }
 
 }  // namespace smh

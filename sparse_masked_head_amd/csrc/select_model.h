@@ -1,0 +1,107 @@
+// Cost model that chooses between the row-wise and the block-wise kernel.
+//
+// The pages state that an analytical model picks the kernel from the mask's
+// sparsity and the sequence length ("Accelerating Sparse Transformer
+// Inference on GPU", gist.science explainer, Technical summary >
+// Methodology > 1. Unified MHA module, kernel-selection item; arXiv
+// catalogue record, abstract) but give no formula.  This model predicts
+// the time of each kernel from the encoding statistics and the problem
+// shape and returns the cheaper one.
+//
+//   block-wise: one workgroup per (head, outer-tile row), one 64 x 64 x d
+//     tile per step.  Work = stored tiles * heads; partial tiles add a
+//     masking cost.  When the launch fits in one wave of workgroups it runs
+//     for the length of its heaviest row instead:
+//       T_blk = c0 + max(W_blk, max_row_tiles * t_tile_serial).
+//   row-wise: one wavefront per (head, 8 query rows); each stored tile
+//     costs a fixed score pass plus a probability-times-V pass over the
+//     keys any of the 8 rows can see:
+//       T_row = c0 + max(visits * t_visit + live_keys * t_key,
+//                        max_row_tiles * t_visit_serial).
+// Sparsity enters through the tile counts and the expected number of live
+// keys of a partial tile (from the partial tiles' mean density); sequence
+// length through the tile counts and the serial term.  The coefficients are
+// microseconds measured on MI355X.
+//
+// The same function runs on the host (smh_select_kernel) and inside both
+// kernels (SMH_AUTO without host statistics), so it is written without
+// library calls and with contraction off: both sides round identically.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#define SMH_HD __host__ __device__
+
+namespace smh {
+
+struct SelectInput {
+    int64_t nnz, n_full, n_partial, max_row_tiles;
+    int64_t BH;
+    int d, bf16;
+};
+
+struct SelectCoef {
+    double launch_us;      // fixed cost of a launch
+    double blk_tile_us;    // block-wise: one 64x64 tile, whole chip busy
+    double blk_part_us;    // block-wise: extra per partial tile
+    double blk_serial_us;  // block-wise: one tile on one workgroup
+    double row_visit_us;   // row-wise: one (8 rows, tile) visit, chip busy
+    double row_key_us;     // row-wise: one live key of a visit
+    double row_serial_us;  // row-wise: one visit on one wavefront
+};
+
+#pragma clang fp contract(off)
+SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
+                                   double *t_blk) {
+    // [d == 128]; fp16 and bf16 share coefficients
+    const SelectCoef k64 = {4.0, 1.2e-3, 0.2e-3, 0.35, 4.0e-4, 2.0e-5, 0.9};
+    const SelectCoef k128 = {4.0, 2.2e-3, 0.2e-3, 0.6, 7.0e-4, 3.0e-5, 1.6};
+    const SelectCoef &k = in.d == 128 ? k128 : k64;
+    const double tiles = (double)in.n_full + (double)in.n_partial;
+    const double heads = (double)in.BH;
+    const double w_blk =
+        heads * (tiles * k.blk_tile_us + (double)in.n_partial * k.blk_part_us);
+    const double crit_blk = (double)in.max_row_tiles * k.blk_serial_us;
+    *t_blk = k.launch_us + (w_blk > crit_blk ? w_blk : crit_blk);
+    double live = 64.0 * (double)in.n_full;
+    if (in.n_partial > 0) {
+        double rho = ((double)in.nnz - 4096.0 * (double)in.n_full) /
+                     (4096.0 * (double)in.n_partial);
+        rho = rho < 0.0 ? 0.0 : (rho > 1.0 ? 1.0 : rho);
+        double miss = 1.0 - rho;   // (1 - rho)^8: no row of 8 sees the key
+        miss = miss * miss;
+        miss = miss * miss;
+        miss = miss * miss;
+        live += (double)in.n_partial * 64.0 * (1.0 - miss);
+    }
+    const double w_row =
+        heads * 8.0 * (tiles * k.row_visit_us + live * k.row_key_us);
+    const double crit_row = (double)in.max_row_tiles * k.row_serial_us;
+    *t_row = k.launch_us + (w_row > crit_row ? w_row : crit_row);
+}
+
+// 1 = row-wise, 2 = block-wise (the smh_kernel values).
+SMH_HD inline int select_model(const SelectInput &in) {
+    double tr, tb;
+    select_costs_us(in, &tr, &tb);
+    return tr < tb ? 1 : 2;
+}
+#pragma clang fp contract(on)
+
+// Device side: read the statistics the encoder wrote and decide.
+__device__ inline int select_on_device(const int64_t *stats, int64_t BH,
+                                       int d, int bf16) {
+    SelectInput in;
+    in.nnz = stats[0];
+    in.n_full = stats[1];
+    in.n_partial = stats[2];
+    in.max_row_tiles = stats[4];
+    in.BH = BH;
+    in.d = d;
+    in.bf16 = bf16;
+    return select_model(in);
+}
+
+}  // namespace smh

@@ -17,7 +17,8 @@ struct EncLayout {
     int64_t n;  // outer tiles per side
     size_t full_row_ptr, part_row_ptr, full_col_idx, part_col_idx,
         part_bitmaps, stats, row_order;
-    size_t tile_cnt, tile_rowany, tile_pos, tile_bitmaps;
+    size_t row_nf, row_np, row_empty, row_nnz, full_local, part_local,
+        tile_words;
     size_t total;
 };
 
@@ -41,29 +42,36 @@ inline EncLayout enc_layout(int32_t S) {
     L.part_bitmaps = take(sizeof(uint64_t) * 64 * n2);
     L.stats = take(sizeof(int64_t) * 8);
     L.row_order = take(sizeof(int32_t) * n);
-    L.tile_cnt = take(sizeof(int32_t) * n2);
-    L.tile_rowany = take(sizeof(uint64_t) * n2);
-    L.tile_pos = take(sizeof(int32_t) * n2);
-    L.tile_bitmaps = take(sizeof(uint64_t) * 64 * n2);
+    L.row_nf = take(sizeof(int32_t) * n);
+    L.row_np = take(sizeof(int32_t) * n);
+    L.row_empty = take(sizeof(int32_t) * n);
+    L.row_nnz = take(sizeof(int64_t) * n);
+    L.full_local = take(sizeof(int32_t) * n2);
+    L.part_local = take(sizeof(int32_t) * n2);
+    L.tile_words = take(sizeof(uint64_t) * 64 * n2);
     L.total = off;
     return L;
 }
 
-// Encoder: three launches on `stream` (tile scan, list scan, compaction).
+// Encoder: two launches on `stream` (row strips, then placement).
 hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
-                         const EncLayout &L, hipStream_t stream);
+                         const EncLayout &L, const smh_mask_enc &enc,
+                         hipStream_t stream);
 
 // Block-wise kernel launcher.  in_dt: 0 f16, 1 bf16; out_dt: 0/1/2 (f32).
+// auto_select != 0: every workgroup first evaluates the cost model on the
+// encoding's device statistics and leaves at once unless it picks this
+// kernel.
 hipError_t launch_blockwise(const void *q, const void *k, const void *v,
                             void *o, int B, int H, int S, int d, int in_dt,
-                            int out_dt, float scale,
-                            const smh_mask_enc &enc, hipStream_t stream);
+                            int out_dt, float scale, const smh_mask_enc &enc,
+                            int auto_select, hipStream_t stream);
 
 // Row-wise kernel launcher, same conventions.
 hipError_t launch_rowwise(const void *q, const void *k, const void *v,
                           void *o, int B, int H, int S, int d, int in_dt,
                           int out_dt, float scale, const smh_mask_enc &enc,
-                          hipStream_t stream);
+                          int auto_select, hipStream_t stream);
 
 // Cost model of the selector (host only).
 smh_kernel select_kernel(const smh_mask_stats &st, int64_t BH, int d,

@@ -147,7 +147,6 @@ def test_fwd_validation():
     assert fwd(scale=float("nan")) == L.SMH_EINVAL
     assert fwd(scale=-1.0) == L.SMH_EINVAL
     assert fwd(which=7) == L.SMH_EINVAL
-    assert fwd(which=L.SMH_AUTO) == L.SMH_EINVAL      # no statistics
     assert fwd(which=L.SMH_AUTO, st=stats()) == L.SMH_EINVAL   # S differs
     assert fwd(B=-1) == L.SMH_EINVAL
     assert fwd(q=None) == L.SMH_EINVAL

@@ -177,3 +177,16 @@ def test_workloads_sampled(cid, kernel, config_mask):
     print(f"  max abs err {worst:.3e}", flush=True)
     assert worst <= TOL[cfg.dtype]
     assert torch.isfinite(o).all()
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_device_auto_matches_host_choice(cid, config_mask):
+    """SMH_AUTO without host statistics runs the kernel the host model
+    picks; the output is bitwise that kernel's output."""
+    dev = need_gpu()
+    cfg, mask, host, devt, enc, st = workload(cid, dev, config_mask)
+    which = smh.select_kernel(st, cfg.B, cfg.H, cfg.d, devt[0].dtype)
+    a = smh.sparse_mha_fwd(*devt, enc, kernel="auto")
+    b = smh.sparse_mha_fwd(*devt, enc, kernel=which)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
