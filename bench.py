@@ -3,10 +3,13 @@
 
 One step is one pass of the whole path over one batch of synthetic input
 already resident in device memory:
-    encode the [S, S] mask (GPU, 2 launches)  ->  attention forward with
-    the kernel chosen by the cost model on the device from the encoding's
-    statistics (both kernels are enqueued; the one not chosen exits at its
-    first instructions).  No host synchronisation inside a step.
+    encode the [S, S] mask (GPU, 2 launches)  ->  attention forward in one
+    launch that picks the row-wise or block-wise algorithm with the cost
+    model evaluated on the device from the encoding's statistics.
+No host synchronisation inside a step, so steps are captured into a HIP
+graph and replayed (--eager launches every step from the host instead).
+Kernel durations (encode_ms, fwd_ms, and the roofline's) come from HIP
+events around graphs of back-to-back launches of that part alone.
 The headline value is effective TFLOP/s: 4*d FLOPs per valid (query, key)
 pair, summed over every (batch, head), divided by the step time.
 
@@ -39,6 +42,9 @@ def parse():
                     choices=["auto", "rowwise", "blockwise"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 disables)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from the host instead of "
+                         "replaying a captured HIP graph")
     ap.add_argument("--out-dtype", default="auto",
                     choices=["auto", "in", "f32"],
                     help="output type; auto = input type for fp16, f32 for "
@@ -132,31 +138,79 @@ def main():
     which = args.kernel if args.kernel != "auto" else smh.select_kernel(
         st, cfg.B, cfg.H, cfg.d, q.dtype)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         enc = smh.encode_mask(mask_d, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
         smh.sparse_mha_fwd(q, k, v, enc, kernel=args.kernel,
                            out_dtype=out_dt, out=out)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def encode_only():
+        smh.encode_mask(mask_d, workspace=ws)
+
+    def fwd_only():
+        smh.sparse_mha_fwd(q, k, v, enc0, kernel=args.kernel,
+                           out_dtype=out_dt, out=out)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
+
+    # A step enqueues three kernels and needs no host synchronisation, so
+    # it is captured once into a HIP graph and replayed (launch-bound
+    # otherwise at small sizes).  `per_graph` steps per replay.
+    per_graph = 1 if args.eager else max(1, min(10, args.steps))
+    if args.steps % per_graph:
+        per_graph = 1
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                step()
+        torch.cuda.synchronize()
+        graph.replay()          # warm replay
+        torch.cuda.synchronize()
+
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    if graph is None:
+        for _ in range(args.steps):
+            step()
+    else:
+        for _ in range(args.steps // per_graph):
+            graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    def kernel_us(fn, reps=20):
+        """Average duration of one launch of fn's kernels: `reps` launches
+        back to back in one graph, bracketed by events on their stream."""
+        if args.eager:
+            fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    enc_ms = kernel_us(encode_only) / 1e3
+    fwd_ms = kernel_us(fwd_only) / 1e3
 
     nnz = st["nnz"]
     BH = cfg.B * cfg.H
@@ -195,6 +249,8 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S,
                    "d": cfg.d, "mask": cfg.desc,
                    "out_dtype": str(out_dt).replace("torch.", ""),
+                   "launch": "eager" if args.eager else
+                   f"hip graph, {per_graph} steps per replay",
                    "parallelism": "single GPU"},
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[cfg.dtype],
         "kernel": which,

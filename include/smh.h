@@ -160,9 +160,8 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
  *   which: SMH_ROWWISE, SMH_BLOCKWISE, or SMH_AUTO.  With SMH_AUTO and st
  *          non-NULL the host decides (smh_select_kernel).  With SMH_AUTO and
  *          st NULL the same model is evaluated on the device from the
- *          statistics the encoder wrote: both kernels are enqueued and the
- *          one not chosen returns before reading or writing anything, so no
- *          host synchronisation is needed.
+ *          statistics the encoder wrote, inside one fused launch that then
+ *          runs the chosen algorithm, so no host synchronisation is needed.
  * Arithmetic: fp32 scores, softmax statistics and accumulators.  The
  * block-wise kernel rounds the probabilities to in_dt for its matrix-core
  * probability-times-V product (the row sums use the rounded values); the

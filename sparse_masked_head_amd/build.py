@@ -15,8 +15,8 @@ OUT = os.path.join(HERE, "libsmh.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["encode.hip", "blockwise.hip", "rowwise.hip", "select.hip",
-           "api.hip"]
+SOURCES = ["encode.hip", "blockwise.hip", "rowwise.hip", "auto_fwd.hip",
+           "select.hip", "api.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -1,0 +1,142 @@
+"""Measure both attention kernels over a grid of masks and shapes and fit
+the coefficients of the kernel-choice cost model (csrc/select_model.h).
+
+    python -m sparse_masked_head_amd.calibrate --out sweep.json   # on a GPU
+    python -m sparse_masked_head_amd.calibrate --fit sweep.json   # anywhere
+
+Each point times the forced row-wise and block-wise kernels with HIP events
+over back-to-back launches (inputs resident, mask encoded once) and records
+the encoding statistics the model sees.
+"""
+import argparse
+import json
+import sys
+import time
+
+import numpy as np
+
+MASKS = [("random", {"p": 0.001}), ("random", {"p": 0.01}),
+         ("random", {"p": 0.05}), ("random", {"p": 0.3}),
+         ("window", {"w": 4}), ("window", {"w": 64}), ("window", {"w": 256}),
+         ("causal", {}), ("full", {}), ("bigbird", {})]
+SIZES = [256, 512, 1024, 2048, 4096]
+HEADS = [1, 8, 64]
+DIMS = [64, 128]
+
+
+def _time(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps   # microseconds
+
+
+def sweep(out_path, quick=False):
+    import torch
+    import sparse_masked_head_amd as smh
+    from workloads import mask_family
+    dev = torch.device("cuda:0")
+    points = []
+    sizes = SIZES[:3] if quick else SIZES
+    t0 = time.time()
+    for fam, kw in MASKS:
+        for S in sizes:
+            if fam == "bigbird" and S < 1024:
+                continue    # needs enough 64-wide blocks for 3 random picks
+            mask = mask_family(fam, S, seed=S, **kw)
+            m = torch.from_numpy(mask).to(dev)
+            enc = smh.encode_mask(m)
+            st = smh.mask_stats_get(enc)
+            for d in DIMS:
+                for BH in HEADS:
+                    if BH * S * d * 2 * 4 > (1 << 31):
+                        continue
+                    q = torch.randn(1, BH, S, d, device=dev).half()
+                    k = torch.randn_like(q)
+                    v = torch.randn_like(q)
+                    o = torch.empty_like(q)
+                    reps = 20 if S * BH < 65536 else 5
+                    t = {}
+                    for kern in ("rowwise", "blockwise"):
+                        t[kern] = _time(lambda: smh.sparse_mha_fwd(
+                            q, k, v, enc, kernel=kern, out=o), reps)
+                    points.append(dict(family=fam, kw=kw, S=S, d=d, BH=BH,
+                                       stats=st, t_row_us=t["rowwise"],
+                                       t_blk_us=t["blockwise"]))
+                    print(f"{fam:8s} {str(kw):14s} S={S:5d} d={d:3d} "
+                          f"BH={BH:3d} row {t['rowwise']:9.1f} us  blk "
+                          f"{t['blockwise']:9.1f} us  [{time.time()-t0:.0f}s]",
+                          flush=True)
+    with open(out_path, "w") as f:
+        json.dump(points, f)
+    return points
+
+
+def model(coef, p):
+    """Python restatement of select_costs_us for fitting (same formula)."""
+    launch, bt, bp, bs, rv, rk, rs = coef
+    st = p["stats"]
+    tiles = st["n_full"] + st["n_partial"]
+    w_blk = p["BH"] * (tiles * bt + st["n_partial"] * bp)
+    t_blk = launch + max(w_blk, st["max_row_tiles"] * bs)
+    live = 64.0 * st["n_full"]
+    if st["n_partial"] > 0:
+        rho = (st["nnz"] - 4096.0 * st["n_full"]) / (4096.0 * st["n_partial"])
+        rho = min(max(rho, 0.0), 1.0)
+        live += st["n_partial"] * 64.0 * (1.0 - (1.0 - rho) ** 8)
+    w_row = p["BH"] * 8.0 * (tiles * rv + live * rk)
+    t_row = launch + max(w_row, st["max_row_tiles"] * rs)
+    return t_row, t_blk
+
+
+def fit(points):
+    from scipy.optimize import least_squares
+    out = {}
+    for d in DIMS:
+        pts = [p for p in points if p["d"] == d and
+               p["stats"]["n_full"] + p["stats"]["n_partial"] > 0]
+
+        def resid(c):
+            r = []
+            for p in pts:
+                tr, tb = model(np.abs(c), p)
+                r.append(np.log(tr / p["t_row_us"]))
+                r.append(np.log(tb / p["t_blk_us"]))
+            return np.array(r)
+        c0 = np.array([4.0, 1e-3, 2e-4, 0.3, 4e-4, 2e-5, 0.9])
+        res = least_squares(resid, c0, x_scale=c0)
+        c = np.abs(res.x)
+        agree = sum((model(c, p)[0] < model(c, p)[1]) ==
+                    (p["t_row_us"] < p["t_blk_us"]) for p in pts)
+        out[d] = dict(coef=c.tolist(), rms_log=float(np.sqrt(np.mean(
+            res.fun ** 2))), agree=agree, n=len(pts))
+        print(f"d={d}: coef {np.array2string(c, precision=4)}  rms log "
+              f"{out[d]['rms_log']:.3f}  choice agrees {agree}/{len(pts)}")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", help="run the sweep on the GPU, write JSON")
+    ap.add_argument("--fit", help="fit coefficients from a sweep JSON")
+    ap.add_argument("--quick", action="store_true")
+    a = ap.parse_args()
+    if a.out:
+        pts = sweep(a.out, a.quick)
+        fit(pts)
+    elif a.fit:
+        fit(json.load(open(a.fit)))
+    else:
+        ap.print_help()
+        sys.exit(2)
+
+
+if __name__ == "__main__":
+    main()

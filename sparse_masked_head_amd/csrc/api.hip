@@ -180,24 +180,18 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
         const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
         const hipStream_t hs = (hipStream_t)stream;
         hipError_t e;
-        if (which == SMH_AUTO && !st) {
-            // decided on the device from the encoding's statistics: both
-            // kernels are launched and the one not chosen exits at once
-            e = launch_rowwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc, *enc,
-                               1, hs);
-            if (e == hipSuccess)
+        if (which == SMH_AUTO && !st)  // decided on the device, one launch
+            e = launch_auto(q, k, v, o, B, H, S, d, in_dt, out_dt, sc, *enc, hs);
+        else {
+            if (which == SMH_AUTO)
+                which = select_kernel(*st, BH, d, in_dt, nullptr, nullptr);
+            if (which == SMH_ROWWISE)
+                e = launch_rowwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
+                                   *enc, hs);
+            else
                 e = launch_blockwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
-                                     *enc, 1, hs);
-            return e == hipSuccess ? SMH_OK : SMH_EHIP;
+                                     *enc, hs);
         }
-        if (which == SMH_AUTO)
-            which = select_kernel(*st, BH, d, in_dt, nullptr, nullptr);
-        if (which == SMH_ROWWISE)
-            e = launch_rowwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc, *enc,
-                               0, hs);
-        else
-            e = launch_blockwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
-                                 *enc, 0, hs);
         return e == hipSuccess ? SMH_OK : SMH_EHIP;
     } catch (...) {
         return SMH_EHIP;

@@ -1,0 +1,71 @@
+// Fused kernel for SMH_AUTO without host statistics: one launch whose
+// workgroups first evaluate the kernel-choice cost model on the statistics
+// the encoder wrote (the same function as smh_select_kernel) and then run
+// either algorithm.  Grid and workgroup shape are the block-wise kernel's
+// (one workgroup per (head, outer-tile row), 256 threads); under the
+// row-wise choice each of the 4 wavefronts takes inner-tile rows w and w+4
+// of that outer-tile row, independently and without barriers.
+#include "blockwise_body.h"
+#include "rowwise_body.h"
+
+namespace smh {
+namespace {
+
+template <int D, typename TIn, typename TOut>
+__global__ __launch_bounds__(256, 2) void auto_fwd(FwdArgs<TIn, TOut> a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int oi = blockIdx.x / a.BH;
+    const int bh = blockIdx.x - oi * a.BH;
+    const int I = a.row_order[oi];
+    if (device_choice<D>(a) == 2) {
+        blockwise_row<D, TIn, TOut>(a, smem, I, bh);
+    } else {
+        const int w = threadIdx.x >> 6;
+        char *slice = smem + w * RowLds<D>::BYTES;
+        rowwise_group<D, TIn, TOut>(a, slice, I, w, bh);
+        rowwise_group<D, TIn, TOut>(a, slice, I, w + 4, bh);
+    }
+}
+
+template <int D, typename TIn, typename TOut>
+hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
+                    int BH, int S, float scale, const smh_mask_enc &enc,
+                    hipStream_t stream) {
+    static_assert(4 * RowLds<D>::BYTES <= Lds<D>::BYTES, "LDS slices");
+    const int smem = Lds<D>::BYTES;
+    auto kern = auto_fwd<D, TIn, TOut>;
+    hipError_t e = ensure_lds_limit(kern, smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)enc.n_ot * BH)), dim3(256),
+                       smem, stream,
+                       make_args<TIn, TOut>(q, k, v, o, BH, S, scale, enc));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_auto(const void *q, const void *k, const void *v, void *o,
+                       int B, int H, int S, int d, int in_dt, int out_dt,
+                       float scale, const smh_mask_enc &enc,
+                       hipStream_t stream) {
+    const int BH = B * H;
+#define SMH_CASE(D_, TI, TO)                                                  \
+    return launch_d<D_, TI, TO>(q, k, v, o, BH, S, scale, enc, stream)
+    if (d == 64) {
+        if (in_dt == SMH_F16) {
+            if (out_dt == SMH_F32) SMH_CASE(64, _Float16, float);
+            SMH_CASE(64, _Float16, _Float16);
+        }
+        if (out_dt == SMH_F32) SMH_CASE(64, __bf16, float);
+        SMH_CASE(64, __bf16, __bf16);
+    }
+    if (in_dt == SMH_F16) {
+        if (out_dt == SMH_F32) SMH_CASE(128, _Float16, float);
+        SMH_CASE(128, _Float16, _Float16);
+    }
+    if (out_dt == SMH_F32) SMH_CASE(128, __bf16, float);
+    SMH_CASE(128, __bf16, __bf16);
+#undef SMH_CASE
+}
+
+}  // namespace smh

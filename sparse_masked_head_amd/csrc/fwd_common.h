@@ -1,0 +1,200 @@
+// Types and helpers shared by the attention kernels of libsmh (gfx950).
+#pragma once
+
+#include <atomic>
+
+#include "select_model.h"
+#include "smh_internal.h"
+
+namespace smh {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Everything an attention kernel reads: the tensors of one call and the
+// encoding of its mask.  c = scale * log2(e) (scores are exponentiated in
+// base 2).
+template <typename TIn, typename TOut> struct FwdArgs {
+    const TIn *Q, *K, *V;
+    TOut *O;
+    int S, BH;
+    float c;
+    const int32_t *frp, *fci, *prp, *pci;
+    const uint64_t *bm;
+    const int32_t *row_order;
+    const int64_t *stats;
+};
+
+template <typename TIn, typename TOut>
+inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
+                                    const void *v, void *o, int BH, int S,
+                                    float scale, const smh_mask_enc &enc) {
+    FwdArgs<TIn, TOut> a;
+    a.Q = (const TIn *)q;
+    a.K = (const TIn *)k;
+    a.V = (const TIn *)v;
+    a.O = (TOut *)o;
+    a.S = S;
+    a.BH = BH;
+    a.c = scale * kLog2e;
+    a.frp = enc.full_row_ptr;
+    a.fci = enc.full_col_idx;
+    a.prp = enc.part_row_ptr;
+    a.pci = enc.part_col_idx;
+    a.bm = enc.part_bitmaps;
+    a.row_order = enc.row_order;
+    a.stats = enc.stats;
+    return a;
+}
+
+template <typename T> constexpr int is_bf16() { return __is_same(T, __bf16) ? 1 : 0; }
+
+// MFMA 16x16x32 with fp32 accumulation for the two input types.
+template <typename T> struct Frag;
+template <> struct Frag<_Float16> {
+    typedef h8_t type;
+    static __device__ inline f4_t mfma(h8_t a, h8_t b, f4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Frag<__bf16> {
+    typedef b8_t type;
+    static __device__ inline f4_t mfma(b8_t a, b8_t b, f4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Packed pair dot product with fp32 accumulation (v_dot2).
+template <typename T> __device__ inline float dot2(uint32_t a, uint32_t b, float c);
+template <> __device__ inline float dot2<_Float16>(uint32_t a, uint32_t b, float c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 x, y;
+    __builtin_memcpy(&x, &a, 4);
+    __builtin_memcpy(&y, &b, 4);
+    return __builtin_amdgcn_fdot2(x, y, c, false);
+}
+template <> __device__ inline float dot2<__bf16>(uint32_t a, uint32_t b, float c) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    b2 x, y;
+    __builtin_memcpy(&x, &a, 4);
+    __builtin_memcpy(&y, &b, 4);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, y, c, false);
+}
+// Sum of a pair already in the input type: exact products with 1, fp32 sum.
+template <typename T> __device__ inline uint32_t ones2();
+template <> __device__ inline uint32_t ones2<_Float16>() { return 0x3C003C00u; }
+template <> __device__ inline uint32_t ones2<__bf16>() { return 0x3F803F80u; }
+template <typename T> __device__ inline float sum2(uint32_t pair, float acc) {
+    return dot2<T>(pair, ones2<T>(), acc);
+}
+
+// Four fp32 values to the output type, one store.
+template <typename T> __device__ inline void store4(T *p, f4_t x);
+template <> __device__ inline void store4<float>(float *p, f4_t x) {
+    *reinterpret_cast<f4_t *>(p) = x;
+}
+template <> __device__ inline void store4<_Float16>(_Float16 *p, f4_t x) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 y = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    *reinterpret_cast<h4 *>(p) = y;
+}
+template <> __device__ inline void store4<__bf16>(__bf16 *p, f4_t x) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    b4 y = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    *reinterpret_cast<b4 *>(p) = y;
+}
+
+template <typename T> __device__ inline void store1(T *p, float x) { *p = (T)x; }
+
+// DPP move of x within the wavefront (`ctrl` = row_shr / row_bcast code);
+// lanes whose source does not exist, or whose row is outside `rows`,
+// receive `fill`.
+template <int ctrl, int rows>
+__device__ inline float dpp(float x, float fill) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(
+        __float_as_int(fill), __float_as_int(x), ctrl, rows, 0xF, false));
+}
+
+// Max / sum over the 64 lanes, returned uniformly: an inclusive scan
+// within each row of 16 (row_shr 1, 2, 4, 8), then across rows
+// (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3), so lane
+// 63 holds the result; read it as a scalar.
+__device__ inline float wave_max(float x) {
+    const float f = -INFINITY;
+    x = fmaxf(x, dpp<0x111, 0xF>(x, f));
+    x = fmaxf(x, dpp<0x112, 0xF>(x, f));
+    x = fmaxf(x, dpp<0x114, 0xF>(x, f));
+    x = fmaxf(x, dpp<0x118, 0xF>(x, f));
+    x = fmaxf(x, dpp<0x142, 0xA>(x, f));
+    x = fmaxf(x, dpp<0x143, 0xC>(x, f));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ inline float wave_sum(float x) {
+    x += dpp<0x111, 0xF>(x, 0.f);
+    x += dpp<0x112, 0xF>(x, 0.f);
+    x += dpp<0x114, 0xF>(x, 0.f);
+    x += dpp<0x118, 0xF>(x, 0.f);
+    x += dpp<0x142, 0xA>(x, 0.f);
+    x += dpp<0x143, 0xC>(x, 0.f);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// Max / sum of x over lanes l and l^16 (then l^32) with the gfx950 row
+// swaps: swapping odd rows of one copy with even rows of the other leaves
+// the two partners' values side by side in every lane.
+__device__ inline float max_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Orders one wavefront's LDS accesses across its lanes: no memory operation
+// moves across it and outstanding LDS work is waited for.
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Raise a kernel's dynamic-LDS limit once per device (the attribute is
+// per device; repeated calls are cheap but are kept out of the launch path
+// so that launches can be captured into graphs).
+template <typename Kernel>
+inline hipError_t ensure_lds_limit(Kernel kern, int bytes) {
+    static std::atomic<int> done[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire) >= bytes)
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && dev >= 0 && dev < 64)
+        done[dev].store(bytes, std::memory_order_release);
+    return e;
+}
+
+// The launch's kernel choice when decided on the device: 1 row-wise,
+// 2 block-wise (same function as smh_select_kernel on the host).
+template <int D, typename TIn, typename TOut>
+__device__ inline int device_choice(const FwdArgs<TIn, TOut> &a) {
+    return select_on_device(a.stats, a.BH, D, is_bf16<TIn>());
+}
+
+}  // namespace smh

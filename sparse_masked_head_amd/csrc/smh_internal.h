@@ -59,19 +59,23 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
                          hipStream_t stream);
 
 // Block-wise kernel launcher.  in_dt: 0 f16, 1 bf16; out_dt: 0/1/2 (f32).
-// auto_select != 0: every workgroup first evaluates the cost model on the
-// encoding's device statistics and leaves at once unless it picks this
-// kernel.
 hipError_t launch_blockwise(const void *q, const void *k, const void *v,
                             void *o, int B, int H, int S, int d, int in_dt,
                             int out_dt, float scale, const smh_mask_enc &enc,
-                            int auto_select, hipStream_t stream);
+                            hipStream_t stream);
 
 // Row-wise kernel launcher, same conventions.
 hipError_t launch_rowwise(const void *q, const void *k, const void *v,
                           void *o, int B, int H, int S, int d, int in_dt,
                           int out_dt, float scale, const smh_mask_enc &enc,
-                          int auto_select, hipStream_t stream);
+                          hipStream_t stream);
+
+// Fused launcher: the cost model runs on the device on the statistics the
+// encoder wrote, then every workgroup runs the chosen algorithm.
+hipError_t launch_auto(const void *q, const void *k, const void *v, void *o,
+                       int B, int H, int S, int d, int in_dt, int out_dt,
+                       float scale, const smh_mask_enc &enc,
+                       hipStream_t stream);
 
 // Cost model of the selector (host only).
 smh_kernel select_kernel(const smh_mask_stats &st, int64_t BH, int d,

@@ -190,3 +190,92 @@ def test_device_auto_matches_host_choice(cid, config_mask):
     b = smh.sparse_mha_fwd(*devt, enc, kernel=which)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def _stats_candidates(S):
+    n = S // 64
+    for mrt in range(0, n + 1):
+        for nf in (0, n * n // 4):
+            for npart in (1, n, n * n // 2):
+                for nnz in (1, 64, 4096 * nf + 300 * npart):
+                    yield dict(nnz=nnz, S=S, n_full=nf, n_partial=npart,
+                               n_empty_rows=0, max_row_tiles=mrt)
+
+
+@pytest.mark.parametrize("d,dt", [(64, "f16"), (128, "bf16")])
+def test_fused_kernel_both_branches(d, dt):
+    """The single-launch SMH_AUTO kernel runs whichever algorithm the device
+    model picks.  The statistics words in the workspace are rewritten (they
+    feed only the decision) to steer it into each branch; each branch's
+    output is bitwise the forced kernel's."""
+    dev = need_gpu()
+    S, B, H = 256, 1, 3
+    mask = mask_family("random", S, seed=31, p=0.08)
+    q, k, v = make_qkv(B, H, S, d, dt, seed=31)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    enc = smh.encode_mask(torch.from_numpy(mask).to(dev))
+    off = enc.enc.stats - enc.workspace.data_ptr()
+    words = enc.workspace[off:off + 40].view(torch.int64)
+    seen = set()
+    for cand in _stats_candidates(S):
+        which = smh.select_kernel(cand, B, H, d, qd.dtype)
+        if which in seen:
+            continue
+        seen.add(which)
+        words.copy_(torch.tensor([cand["nnz"], cand["n_full"],
+                                  cand["n_partial"], 0,
+                                  cand["max_row_tiles"]], dtype=torch.int64))
+        a = smh.sparse_mha_fwd(qd, kd, vd, enc, kernel="auto",
+                               out_dtype=torch.float32)
+        b = smh.sparse_mha_fwd(qd, kd, vd, enc, kernel=which,
+                               out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), which
+        assert maxerr(a, attention(q, k, v, mask)) <= TOL[dt]
+    if "rowwise" not in seen:
+        pytest.skip("the fitted cost model never picks the row-wise kernel "
+                    "for this shape; its fused branch is unreachable")
+
+
+def test_graph_replay_matches_eager():
+    """Encode + auto forward captured into a HIP graph: every replay, with
+    eager work between replays, gives bitwise the eager encoding and
+    output (the captured launches contain no memset nodes)."""
+    dev = need_gpu()
+    cfg = get_config(2)
+    S, d = cfg.S, cfg.d
+    mask = mask_family("window64", S)
+    q, k, v = make_qkv(2, 3, S, d, "f16", seed=77)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    md = torch.from_numpy(mask).to(dev)
+    ws = torch.empty(smh.encode_workspace_bytes(S), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(qd)
+
+    def step():
+        e = smh.encode_mask(md, workspace=ws)
+        smh.sparse_mha_fwd(qd, kd, vd, e, kernel="auto", out=out)
+        return e
+    enc = step()
+    torch.cuda.synchronize()
+    want_out = out.clone()
+    st = smh.mask_stats_get(enc)
+    want_enc = {kk: vv.clone() for kk, vv in enc.arrays(st).items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xCD)                       # scribble between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), rep
+        got = enc.arrays(st)
+        for kk in want_enc:
+            assert torch.equal(got[kk], want_enc[kk]), (rep, kk)
+        eager = smh.sparse_mha_fwd(kd, qd, vd, enc, kernel="blockwise")
+        torch.cuda.synchronize()
+        assert torch.isfinite(eager).all()
+    err = maxerr(out, attention(q, k, v, mask))
+    assert err <= TOL["f16"]
