@@ -45,11 +45,103 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of "
                          "replaying a captured HIP graph")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy "
+                         "(the reference for scaling FETCH_SIZE/WRITE_SIZE "
+                         "counter readings to bytes)")
+    ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
+                    help="FETCH_SIZE and WRITE_SIZE counter CSVs of this "
+                         "bench (rocprofv3 --pmc, one counter per run), then "
+                         "those of --copy-reference; writes the HBM bytes "
+                         "per launch of the attention kernel to profiles/")
     ap.add_argument("--out-dtype", default="auto",
                     choices=["auto", "in", "f32"],
                     help="output type; auto = input type for fp16, f32 for "
                          "bf16")
     return ap.parse_args()
+
+
+COPY_REF_BYTES = 256 << 20
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def copy_reference():
+    """A plain copy of COPY_REF_BYTES, five times (one kernel each)."""
+    import torch
+    x = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": COPY_REF_BYTES}))
+
+
+def source_digest():
+    """Digest of the HIP sources: counter readings are valid only for the
+    kernels they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_masked_head_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from committed counter
+    readings (profiles/traffic_<kernel>_<workload>.json), or None when they
+    were taken on other sources."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def _counter_kib(path, name_part):
+    """Mean per-dispatch value of the one counter in a rocprofv3 counter CSV
+    over the dispatches of kernels whose name contains name_part."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if name_part in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + \
+                float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of *{name_part}* in {path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_traffic(args, cfg):
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.write_traffic
+    kern = "auto_fwd" if args.kernel == "auto" else f"{args.kernel}_fwd"
+    f_kib, nf = _counter_kib(fetch_csv, kern)
+    w_kib, nw = _counter_kib(write_csv, kern)
+    # torch runs a same-type contiguous copy as the runtime's copyBuffer
+    # kernel; the fill that creates the source is a different kernel
+    cf_kib, _ = _counter_kib(cfetch_csv, "copyBuffer")
+    cw_kib, _ = _counter_kib(cwrite_csv, "copyBuffer")
+    # counter KiB that one true byte reads as, for a plain copy
+    ff = cf_kib * 1024.0 / COPY_REF_BYTES
+    fw = cw_kib * 1024.0 / COPY_REF_BYTES
+    rec = {"kernel": kern, "workload": cfg.name,
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+           "dispatches": [nf, nw],
+           "copy_reference_bytes": COPY_REF_BYTES,
+           "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+           "fetch_scale": ff, "write_scale": fw,
+           "hbm_read_bytes_per_launch": f_kib * 1024.0 / ff,
+           "hbm_write_bytes_per_launch": w_kib * 1024.0 / fw,
+           "hbm_bytes_per_launch": f_kib * 1024.0 / ff + w_kib * 1024.0 / fw,
+           "source_digest": source_digest()}
+    os.makedirs(TRAFFIC_DIR, exist_ok=True)
+    out = os.path.join(TRAFFIC_DIR, f"traffic_{kern}_{cfg.name}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def encoding_bytes(st, n):
@@ -105,6 +197,13 @@ def cpu_baseline(cfg, mask, qkv, budget_s):
 
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference()
+        return
+    if args.write_traffic:
+        from workloads import get_config
+        write_traffic(args, get_config(args.config))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus "
               f"{args.gpus} is not supported (the path needs no collective; "
@@ -230,8 +329,10 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / fwd_s / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = f"{which}_fwd"
+    roof["kernel"] = "auto_fwd" if args.kernel == "auto" else f"{which}_fwd"
+    roof["algorithmic_bytes"] = attn_bytes
+    roof["algorithmic_flops"] = flops
+    roof["traffic"] = stored_traffic(roof["kernel"], cfg.name)
     pred_row, pred_blk = smh.select_costs(st, cfg.B, cfg.H, cfg.d, q.dtype)
 
     cpu = None

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256, 2) void auto_fwd(FwdArgs<TIn, TOut> a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int oi = blockIdx.x / a.BH;
     const int bh = blockIdx.x - oi * a.BH;
-    const int I = a.row_order[oi];
+    const int I = a.use_order ? a.row_order[oi] : oi;
     if (device_choice<D>(a) == 2) {
         blockwise_row<D, TIn, TOut>(a, smem, I, bh);
     } else {
@@ -36,9 +36,10 @@ hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
     auto kern = auto_fwd<D, TIn, TOut>;
     hipError_t e = ensure_lds_limit(kern, smem);
     if (e != hipSuccess) return e;
+    FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, BH, S, scale, enc);
+    a.use_order = (long long)enc.n_ot * BH > resident_workgroups(kern, smem);
     hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)enc.n_ot * BH)), dim3(256),
-                       smem, stream,
-                       make_args<TIn, TOut>(q, k, v, o, BH, S, scale, enc));
+                       smem, stream, a);
     return hipGetLastError();
 }
 

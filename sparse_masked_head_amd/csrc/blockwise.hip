@@ -12,15 +12,16 @@ __global__ __launch_bounds__(256, 2) void blockwise_fwd(FwdArgs<TIn, TOut> a) {
     // in launch order, so with BH % 8 == 0 they all land on one XCD
     const int oi = blockIdx.x / a.BH;
     const int bh = blockIdx.x - oi * a.BH;
-    blockwise_row<D, TIn, TOut>(a, smem, a.row_order[oi], bh);
+    blockwise_row<D, TIn, TOut>(a, smem, a.use_order ? a.row_order[oi] : oi, bh);
 }
 
 template <int D, typename TIn, typename TOut>
-hipError_t launch_t(const FwdArgs<TIn, TOut> &a, int n, hipStream_t stream) {
+hipError_t launch_t(FwdArgs<TIn, TOut> a, int n, hipStream_t stream) {
     const int smem = Lds<D>::BYTES;
     auto kern = blockwise_fwd<D, TIn, TOut>;
     hipError_t e = ensure_lds_limit(kern, smem);
     if (e != hipSuccess) return e;
+    a.use_order = (long long)n * a.BH > resident_workgroups(kern, smem);
     hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)n * a.BH)), dim3(256),
                        smem, stream, a);
     return hipGetLastError();

@@ -24,6 +24,10 @@ template <typename TIn, typename TOut> struct FwdArgs {
     TOut *O;
     int S, BH;
     float c;
+    // 1: visit outer-tile rows in row_order (heavy first); 0: in index
+    // order, used when every workgroup of the launch is resident at once
+    // and the order cannot matter (saves a dependent load per workgroup)
+    int use_order;
     const int32_t *frp, *fci, *prp, *pci;
     const uint64_t *bm;
     const int32_t *row_order;
@@ -42,6 +46,7 @@ inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
     a.S = S;
     a.BH = BH;
     a.c = scale * kLog2e;
+    a.use_order = 1;
     a.frp = enc.full_row_ptr;
     a.fci = enc.full_col_idx;
     a.prp = enc.part_row_ptr;
@@ -188,6 +193,26 @@ inline hipError_t ensure_lds_limit(Kernel kern, int bytes) {
     if (e == hipSuccess && dev >= 0 && dev < 64)
         done[dev].store(bytes, std::memory_order_release);
     return e;
+}
+
+// Workgroups of `kern` (256 threads, `lds` bytes of dynamic LDS) that the
+// current device holds at once; cached per kernel and device.
+template <typename Kernel>
+inline long long resident_workgroups(Kernel kern, int lds) {
+    static std::atomic<long long> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    long long v = cache[dev].load(std::memory_order_acquire);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(kern), 256, lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess)
+        return 0;
+    v = (long long)per_cu * cus;
+    cache[dev].store(v, std::memory_order_release);
+    return v;
 }
 
 // The launch's kernel choice when decided on the device: 1 row-wise,

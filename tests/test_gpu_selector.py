@@ -1,0 +1,55 @@
+"""The analytical selector picks the faster kernel on every workload.
+
+Both kernels are timed on the full workload (HIP events around a graph of
+back-to-back launches); the choice of smh_select_kernel must be the faster
+one, or the two must lie within 3% of each other (either choice passes)."""
+import pytest
+import torch
+
+import sparse_masked_head_amd as smh
+from tests.gpu_util import need_gpu
+from workloads import get_config, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+TIE = 0.03
+
+
+def _time_us(fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_selector_picks_faster_kernel(cid, config_mask):
+    dev = need_gpu()
+    cfg = get_config(cid)
+    print(f"selector workload {cid}", flush=True)
+    q, k, v = (x.to(dev) for x in make_qkv(cfg.B, cfg.H, cfg.S, cfg.d,
+                                           cfg.dtype, seed=cid))
+    enc = smh.encode_mask(torch.from_numpy(config_mask(cid)).to(dev))
+    st = smh.mask_stats_get(enc)
+    out_dt = torch.float32 if cfg.dtype == "bf16" else q.dtype
+    out = torch.empty(q.shape, dtype=out_dt, device=dev)
+    reps = 2 if cid == 5 else 10
+    t = {kern: _time_us(lambda: smh.sparse_mha_fwd(
+        q, k, v, enc, kernel=kern, out_dtype=out_dt, out=out), reps)
+        for kern in ("rowwise", "blockwise")}
+    choice = smh.select_kernel(st, cfg.B, cfg.H, cfg.d, q.dtype)
+    other = "rowwise" if choice == "blockwise" else "blockwise"
+    print(f"  rowwise {t['rowwise']:.1f} us  blockwise {t['blockwise']:.1f} us"
+          f"  choice {choice}", flush=True)
+    assert t[choice] <= t[other] * (1 + TIE), (choice, t)
