@@ -12,7 +12,7 @@ namespace smh {
 namespace {
 
 template <int D, typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 2) void auto_fwd(FwdArgs<TIn, TOut> a) {
+__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TOut> a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int oi = blockIdx.x / a.BH;
     const int bh = blockIdx.x - oi * a.BH;

@@ -6,7 +6,7 @@ namespace smh {
 namespace {
 
 template <int D, typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 2) void blockwise_fwd(FwdArgs<TIn, TOut> a) {
+__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TIn, TOut> a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // heavy rows first across all heads; one head's workgroups are BH apart
     // in launch order, so with BH % 8 == 0 they all land on one XCD

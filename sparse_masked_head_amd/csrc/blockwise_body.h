@@ -12,8 +12,9 @@
 //
 // The workgroup owns the 64 query rows of outer-tile row I of head bh and
 // walks the full tiles of the row, then its partial tiles.  Per tile J:
-//   * K (row-major, with the tile's 64 words) and V (transposed: row =
-//     output column, keys contiguous) sit in separate LDS double buffers;
+//   * K and V sit row-major in separate LDS double buffers (plain 16-byte
+//     writes; the transpose that V^T needs is done by ds_read_b64_tr_b16
+//     when the P V operand is read);
 //     K is staged two tiles ahead of its use and V one, so iteration t
 //     issues the QK^T MFMAs of tile t+1 before the softmax of tile t and
 //     the matrix cores work while the VALU does the softmax; one barrier
@@ -22,9 +23,10 @@
 //     v_mfma_f32_16x16x32 (A = K rows from LDS, B = its Q rows held in
 //     registers for the whole row).  In this accumulator layout lane l holds
 //     query l%16's scores against keys 16st + 4(l/16) + i;
-//   * partial tiles reset masked scores to -inf: the tile's 64 words are
-//     staged with it and each lane reads the four bytes (one per 16-key
-//     sub-tile) that hold its query row's bits;
+//   * partial tiles reset masked scores to -inf: each lane loads from the
+//     tile's 64 words the four bytes (one per 16-key sub-tile) that hold
+//     its query row's bits, together with the K tile, and carries its 16
+//     mask bits in a register until the tile's softmax;
 //   * online softmax in base 2 (running max and sum per query); only the
 //     4 lanes sharing a query exchange values (two gfx950 row swaps);
 //   * O^T += V^T P^T with the same MFMA: P^T is the B operand straight from
@@ -39,14 +41,12 @@
 namespace smh {
 
 template <int D> struct Lds {
-    // Row strides (elements), chosen on gfx950 so that the MFMA operand
-    // reads are conflict-free: K rows shifted by 32 bytes per row for the
-    // 16-byte reads, V^T rows by 8 bytes for the paired 8-byte reads.
+    // Row stride (elements) of the K and V tiles, chosen on gfx950 so that
+    // the operand reads are conflict-free: rows shifted by 32 bytes (a probe
+    // of the access patterns: 16-byte shifts conflict, 32-byte do not).
     static constexpr int KLD = D + 16;
-    static constexpr int VLD = 64 + 4;
-    static constexpr int K_BYTES = 64 * KLD * 2;
-    static constexpr int KBUF = K_BYTES + 64 * 8;  // K tile + its 64 words
-    static constexpr int VBUF = D * VLD * 2;       // V^T tile
+    static constexpr int KBUF = 64 * KLD * 2;  // K tile, row-major
+    static constexpr int VBUF = 64 * KLD * 2;  // V tile, row-major
     static constexpr int BYTES = 2 * KBUF + 2 * VBUF;
     static __device__ char *kbuf(char *smem, int i) { return smem + i * KBUF; }
     static __device__ char *vbuf(char *smem, int i) {
@@ -54,63 +54,63 @@ template <int D> struct Lds {
     }
 };
 
-// Registers carrying one K tile (and a partial tile's 64 words) or one V
-// tile from global memory to LDS.
+// Registers carrying one K tile (and, for a partial tile, the four mask
+// bytes this lane needs) or one V tile from global memory to LDS.
 template <int D> struct KRegs {
     static constexpr int N = 64 * D / 8 / 256;  // 16-byte chunks per thread
     u4_t kr[N];
-    uint64_t bw;
+    uint32_t mb[4];
 };
 template <int D> struct VRegs {
-    static constexpr int N = 32 * (D / 8) / 256;  // transpose tasks per thread
-    u4_t va[N], vb[N];
+    static constexpr int N = 64 * D / 8 / 256;  // 16-byte chunks per thread
+    u4_t vr[N];
 };
 
-// V transpose task e -> (8-column chunk dc, key pair kp).  Consecutive
-// lanes take consecutive key pairs, so a 32-bit LDS write instruction covers
-// 32 consecutive words per half-wavefront; the two half-wavefronts take
-// chunks two apart (16 V^T rows, 2176 bytes), which lands them on the other
-// half of the banks.  A probe of the write patterns on gfx950 measured this
-// 1.9x (d=64) and 3.7x (d=128) faster than chunk-fastest order.
-template <int D>
-__device__ inline void v_task(int e, int &dc, int &kp) {
-    kp = e & 31;
-    const int j = e >> 5, m = j >> 1;
-    dc = (m & 1) + 4 * (m >> 1) + 2 * (j & 1);
-}
-
 // Global loads of K tile J (one contiguous block: thread t takes 16-byte
-// chunks t, t+256, ...) and, for a partial tile, its 64 words.
+// chunks t, t+256, ...) and, for a partial tile, this lane's mask bytes:
+// keys 16st + 4g + i of query row r are bits 4(g&1)+i of byte r&7 of inner
+// tile (r>>3, 2st + (g>>1)); b_off is that byte's offset for st = 0, each
+// further st is two words (16 bytes) on.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void fetch_k(
     KRegs<D> &r, const TIn *__restrict__ Kh, int J,
-    const uint64_t *__restrict__ words, int t) {
+    const uint64_t *__restrict__ words, int b_off, int t) {
     const TIn *kt = Kh + (size_t)J * 64 * D;
 #pragma unroll
     for (int i = 0; i < KRegs<D>::N; ++i)
         r.kr[i] = *reinterpret_cast<const u4_t *>(kt + (t + 256 * i) * 8);
-    if (words && t < 64) r.bw = words[t];
+    if (words) {
+        const uint8_t *wb = reinterpret_cast<const uint8_t *>(words) + b_off;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) r.mb[st] = wb[16 * st];
+    }
 }
 
-// Global loads of V tile J: thread t takes keys 2kp and 2kp+1 of 8-column
-// chunk dc (v_task), ready for the transpose.
+// The lane's 16 mask bits of a fetched partial tile: bit 4st + i = key
+// 16st + 4g + i of its query row (nib = 4(g&1)).
+template <int D>
+__device__ __attribute__((always_inline)) inline uint32_t mask_bits(
+    const KRegs<D> &r, int nib) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) m |= ((r.mb[st] >> nib) & 0xFu) << (4 * st);
+    return m;
+}
+
+// Global loads of V tile J, the same contiguous chunks as K.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void fetch_v(
     VRegs<D> &r, const TIn *__restrict__ Vh, int J, int t) {
     const TIn *vt = Vh + (size_t)J * 64 * D;
 #pragma unroll
-    for (int i = 0; i < VRegs<D>::N; ++i) {
-        int dc, kp;
-        v_task<D>(t + 256 * i, dc, kp);
-        r.va[i] = *reinterpret_cast<const u4_t *>(vt + (2 * kp) * D + 8 * dc);
-        r.vb[i] = *reinterpret_cast<const u4_t *>(vt + (2 * kp + 1) * D + 8 * dc);
-    }
+    for (int i = 0; i < VRegs<D>::N; ++i)
+        r.vr[i] = *reinterpret_cast<const u4_t *>(vt + (t + 256 * i) * 8);
 }
 
-// K tile row-major into a K buffer (padded rows), words after it.
+// K tile row-major into a K buffer (padded rows).
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void stage_k(
-    const KRegs<D> &r, char *kb, bool partial, int t) {
+    const KRegs<D> &r, char *kb, int t) {
     using L = Lds<D>;
     TIn *ks = reinterpret_cast<TIn *>(kb);
 #pragma unroll
@@ -119,28 +119,20 @@ __device__ __attribute__((always_inline)) inline void stage_k(
         const int row = e / (D / 8), col = (e % (D / 8)) * 8;
         *reinterpret_cast<u4_t *>(ks + row * L::KLD + col) = r.kr[i];
     }
-    if (partial && t < 64) reinterpret_cast<uint64_t *>(kb + L::K_BYTES)[t] = r.bw;
 }
 
-// V tile transposed into a V buffer: row = output column, keys contiguous;
-// pairs of keys packed into one 32-bit write.
+// V tile row-major into a V buffer (padded rows, like K); the transpose
+// that the P V product needs is done by the transposing LDS reads.
 template <int D>
 __device__ __attribute__((always_inline)) inline void stage_v(
     const VRegs<D> &r, char *vb, int t) {
     using L = Lds<D>;
-    uint32_t *vs = reinterpret_cast<uint32_t *>(vb);
+    uint16_t *vs = reinterpret_cast<uint16_t *>(vb);
 #pragma unroll
     for (int i = 0; i < VRegs<D>::N; ++i) {
-        int dc, kp;
-        v_task<D>(t + 256 * i, dc, kp);
-        const u4_t a = r.va[i], b = r.vb[i];
-        uint32_t *dst = vs + (8 * dc * L::VLD + 2 * kp) / 2;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            // elements 2k, 2k+1 of keys 2kp (low half) and 2kp+1 (high)
-            dst[(2 * k) * L::VLD / 2] = (a[k] & 0xFFFFu) | (b[k] << 16);
-            dst[(2 * k + 1) * L::VLD / 2] = (a[k] >> 16) | (b[k] & 0xFFFF0000u);
-        }
+        const int e = t + 256 * i;
+        const int row = e / (D / 8), col = (e % (D / 8)) * 8;
+        *reinterpret_cast<u4_t *>(vs + row * L::KLD + col) = r.vr[i];
     }
 }
 
@@ -171,20 +163,8 @@ __device__ __attribute__((always_inline)) inline void qk_tile(
     }
 }
 
-// The 16 mask bits of this lane for one partial tile: keys 16st + 4g + i
-// of row r are bits 4(g&1)+i of byte r&7 of inner tile (r>>3, 2st+(g>>1));
-// bit 4st+i of the result.
-template <int D>
-__device__ __attribute__((always_inline)) inline uint32_t mask_bits(
-    const char *kb, int b_off, int nib) {
-    const uint8_t *wb = reinterpret_cast<const uint8_t *>(kb + Lds<D>::K_BYTES) + b_off;
-    uint32_t m = 0;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) m |= (((uint32_t)wb[16 * st] >> nib) & 0xFu) << (4 * st);
-    return m;
-}
-
 // Softmax of one tile's scores (masked if `partial`) and O^T += V^T P^T.
+// c = scale * log2(e) > 0.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void softmax_pv(
     RowState<D> &rs, f4_t (&sc)[4], bool partial, uint32_t mbits,
@@ -206,11 +186,18 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
         mx = fmaxf(fmaxf(mx, sc[st][2]), sc[st][3]);
     }
     mx = max_xor32(max_xor16(mx));
-    const float m_new = fmaxf(rs.m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((rs.m - m_use) * c);
-    const float mc = m_use * c;
-    rs.m = m_new;
+    {
+        const float m_new = fmaxf(rs.m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((rs.m - m_use) * c);
+        rs.m = m_new;
+        rs.l *= alpha;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
+        }
+    }
+    const float mc = (rs.m == -INFINITY ? 0.f : rs.m) * c;
 
     // P^T as B operand: keys 32u + 4g + j (j < 4), 32u + 16 + 4g + j - 4
     frag pf[2];
@@ -220,7 +207,7 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
         for (int i = 0; i < 4; ++i)
             pf[st >> 1][(st & 1) * 4 + i] =
                 (TIn)__builtin_amdgcn_exp2f(fmaf(sc[st][i], c, -mc));
-    float lsum = 0.f;
+    float lsum = rs.l;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         uint32_t pw[4];
@@ -228,23 +215,28 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
 #pragma unroll
         for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
     }
-    rs.l = rs.l * alpha + lsum;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
-    }
+    rs.l = lsum;
 
-    const TIn *vs = reinterpret_cast<const TIn *>(vb) + v_off;
+    // A operand V^T (rows = output columns 16dt + l%16, slots = keys of
+    // the P^T slots) read with ds_read_b64_tr_b16 from row-major V: within
+    // each 16-lane group, lane j = a + 4q points at V[key0 + q][d0 + 4a]
+    // and lane i receives V[key0 .. key0+3][d0 + i]; key0 = 32u + 4g for
+    // slots 0..3 and 32u + 16 + 4g for slots 4..7.  v_off is the lane's
+    // (q, a) offset in elements.
+    const char *vs = vb + 2 * v_off;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const TIn *vp = vs + 16 * dt * L::VLD + 32 * u;
-            const u2_t lo = *reinterpret_cast<const u2_t *>(vp);
-            const u2_t hi = *reinterpret_cast<const u2_t *>(vp + 16);
-            const u4_t packed = {lo[0], lo[1], hi[0], hi[1]};
+            const char *p0 = vs + 2 * (32 * u * L::KLD + 16 * dt);
+            const char *p1 = p0 + 2 * 16 * L::KLD;
+            const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4_t *)(p0));
+            const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4_t *)(p1));
             frag a;
-            __builtin_memcpy(&a, &packed, sizeof(a));
+            __builtin_memcpy(&a, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
             rs.acc[dt] = F::mfma(a, pf[u], rs.acc[dt]);
         }
     }
@@ -302,7 +294,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
 
     // per-lane LDS offsets (elements / bytes), the same in every buffer
     const int k_off = lq * L::KLD + 8 * g;
-    const int v_off = lq * L::VLD + 4 * g;
+    const int v_off = (4 * g + (lq >> 2)) * L::KLD + 4 * (lq & 3);
     const int b_off = ((r >> 3) * 8 + (g >> 1)) * 8 + (r & 7);
     const int nib = 4 * (g & 1);
 
@@ -310,47 +302,52 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     // V one tile ahead, so that iteration `it` can issue QK^T of tile it+1
     // before the softmax of tile it (matrix cores busy during the VALU
     // work).  Buffers: K(it) in kbuf(it&1), V(it) in vbuf(it&1).
+    // mask bits ride along in registers: m_cur for tile it, m_nxt for
+    // it+1, m_k2 for it+2 (taken from the K registers when they are staged)
     KRegs<D> kr, kr1;
     VRegs<D> vr;
-    kr.bw = 0;
-    kr1.bw = 0;
     f4_t s_cur[4], s_nxt[4];
     uint32_t m_cur = 0, m_nxt = 0;
     if (nT > 0) {
-        fetch_k<D, TIn>(kr, Kh, tl.col(0), tl.words(0), t);
+        fetch_k<D, TIn>(kr, Kh, tl.col(0), tl.words(0), b_off, t);
         fetch_v<D, TIn>(vr, Vh, tl.col(0), t);
-        if (nT > 1) fetch_k<D, TIn>(kr1, Kh, tl.col(1), tl.words(1), t);
-        stage_k<D, TIn>(kr, L::kbuf(smem, 0), nF == 0, t);
+        if (nT > 1) fetch_k<D, TIn>(kr1, Kh, tl.col(1), tl.words(1), b_off, t);
+        stage_k<D, TIn>(kr, L::kbuf(smem, 0), t);
+        if (nF == 0) m_cur = mask_bits<D>(kr, nib);
         stage_v<D>(vr, L::vbuf(smem, 0), t);
-        if (nT > 1) stage_k<D, TIn>(kr1, L::kbuf(smem, 1), 1 >= nF, t);
-        if (nT > 2) fetch_k<D, TIn>(kr, Kh, tl.col(2), tl.words(2), t);
+        if (nT > 1) {
+            stage_k<D, TIn>(kr1, L::kbuf(smem, 1), t);
+            if (1 >= nF) m_nxt = mask_bits<D>(kr1, nib);
+        }
+        if (nT > 2) fetch_k<D, TIn>(kr, Kh, tl.col(2), tl.words(2), b_off, t);
         if (nT > 1) fetch_v<D, TIn>(vr, Vh, tl.col(1), t);
     }
     __syncthreads();
-    if (nT > 0) {
-        qk_tile<D, TIn>(s_cur, qf, L::kbuf(smem, 0), k_off);
-        if (nF == 0) m_cur = mask_bits<D>(L::kbuf(smem, 0), b_off, nib);
-    }
+    if (nT > 0) qk_tile<D, TIn>(s_cur, qf, L::kbuf(smem, 0), k_off);
     // every wave has read K(0) before iteration 0 overwrites its buffer
     __syncthreads();
 
     for (int it = 0; it < nT; ++it) {
         const int cb = it & 1, nb = cb ^ 1;
-        if (it + 1 < nT) {
-            qk_tile<D, TIn>(s_nxt, qf, L::kbuf(smem, nb), k_off);
-            if (it + 1 >= nF) m_nxt = mask_bits<D>(L::kbuf(smem, nb), b_off, nib);
+        if (it + 1 < nT) qk_tile<D, TIn>(s_nxt, qf, L::kbuf(smem, nb), k_off);
+        softmax_pv<D, TIn>(rs, s_cur, it >= nF, m_cur, L::vbuf(smem, cb), a.c,
+                           v_off);
+        // K(it+2) replaces K(it) (read in the previous iteration); V(it+1)
+        // replaces V(it-1)
+        uint32_t m_k2 = 0;
+        if (it + 2 < nT) {
+            stage_k<D, TIn>(kr, L::kbuf(smem, cb), t);
+            if (it + 2 >= nF) m_k2 = mask_bits<D>(kr, nib);
         }
-        softmax_pv<D, TIn>(rs, s_cur, it >= nF, m_cur, L::vbuf(smem, cb), a.c, v_off);
-        // K(it+2) replaces K(it) (read in the previous iteration; its words
-        // are in registers already); V(it+1) replaces V(it-1)
-        if (it + 2 < nT) stage_k<D, TIn>(kr, L::kbuf(smem, cb), it + 2 >= nF, t);
         if (it + 1 < nT) stage_v<D>(vr, L::vbuf(smem, nb), t);
-        if (it + 3 < nT) fetch_k<D, TIn>(kr, Kh, tl.col(it + 3), tl.words(it + 3), t);
+        if (it + 3 < nT)
+            fetch_k<D, TIn>(kr, Kh, tl.col(it + 3), tl.words(it + 3), b_off, t);
         if (it + 2 < nT) fetch_v<D, TIn>(vr, Vh, tl.col(it + 2), t);
         __syncthreads();
 #pragma unroll
         for (int st = 0; st < 4; ++st) s_cur[st] = s_nxt[st];
         m_cur = m_nxt;
+        m_nxt = m_k2;
     }
 
     // epilogue: total l over the 4 lanes of this query
