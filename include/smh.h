@@ -52,7 +52,7 @@ typedef enum {
 } smh_kernel;
 
 /* Largest sequence length accepted (the encoding workspace grows as
- * (S/64)^2 * 528 bytes: 2.2 GB at this limit). */
+ * (S/64)^2 * 1040 bytes: 4.4 GB at this limit). */
 #define SMH_MAX_S 131072
 /* Outer tile edge and inner tile edge, in elements. */
 #define SMH_OT 64
@@ -109,7 +109,9 @@ size_t smh_encode_workspace_bytes(int32_t S);
 
 /* Encode a dense mask ([EXP] storage-format items: BSR outer tiles split
  * into full and partial pointer arrays, empty tiles skipped, one uint64 per
- * 8x8 inner tile of a partial tile).
+ * 8x8 inner tile of a partial tile).  Two or three kernel launches:
+ * a strip pass over segments of outer-tile rows, then the placement of
+ * their tiles (with the prefix scan inside it, or before it for long S).
  *   mask: device uint8 [S][S], row-major, 16-byte aligned, element (i, j)
  *         nonzero means query i attends to key j.  Read only.  NULL allowed
  *         only when S == 0.

@@ -6,29 +6,29 @@
 // tiles are listed by column only; partial tiles are listed and carry one
 // uint64 bitmap per 8x8 inner tile.  Exact layout: include/smh.h.
 //
-// Two launches, one workgroup per outer-tile row I in both:
-//   1. enc_rows    streams the 64 x S strip of mask rows of I, eight outer
-//                  tiles (512 contiguous bytes per mask row) per step with
-//                  the next step's loads in flight.  Builds the 64 inner-tile
-//                  words of each tile in LDS, counts its valid elements, and
-//                  appends the tile to the row's own full or partial list
-//                  (row-local positions, ascending J) in scratch, partial
-//                  tiles with their 64 words.  Also counts the row's valid
-//                  pairs and its query rows without a valid key.
-//   2. enc_finish  turns the per-row counts into the row's offsets in the
-//                  global lists (a sum over the rows before it), copies the
-//                  row's lists and words into place, writes the row
-//                  pointers, the row's rank in the heavy-first schedule and,
-//                  in the last row's workgroup, the statistics.
-// Every value is a pure function of the mask (no atomics, no order
-// dependence), so the result is deterministic and equals appending tiles
-// row by row, column by column.
+// Work unit: a segment of one outer-tile row (seg_plan), numbered row by
+// row, left to right, so the encoding is the concatenation of the
+// segments' tile lists in that order.
+//   strip pass (one workgroup per segment): stream the segment's 64-row
+//     strip, one window (64 rows x 512 bytes) at a time with the next
+//     window's loads in flight; build the inner-tile words of every tile in
+//     LDS and count its elements; classify the tiles (full / partial /
+//     empty) and write the segment's tile columns, partial-tile words,
+//     tile counts, valid-pair count and covered query rows to scratch;
+//   scan (one workgroup): exclusive prefix of the segments' tile counts,
+//     row pointers, statistics and the heavy-first row order;
+//   placement (one workgroup per segment): copy the segment's columns and
+//     words to their final places.
+// With at most kFusedMaxSegs segments the scan runs as one extra workgroup
+// of the placement launch and each placement workgroup adds up the counts
+// before it itself (cheap at that size, and one launch fewer).  No
+// workgroup ever waits for another.  Every output is a pure function of
+// the mask: the result is deterministic and equals appending tiles row by
+// row, column by column.
 #include "smh_internal.h"
 
 namespace smh {
 namespace {
-
-constexpr int kT = 8;  // outer tiles per step of enc_rows
 
 // High bit of each byte of w set iff that byte is nonzero.
 __device__ inline uint32_t nonzero_bytes(uint32_t w) {
@@ -47,171 +47,273 @@ __device__ inline uint32_t row_bits8(uint32_t lo, uint32_t hi) {
     return gather4(nonzero_bytes(lo)) | (gather4(nonzero_bytes(hi)) << 4);
 }
 
-struct Scratch {
-    int32_t *row_nf, *row_np, *row_empty;
-    int64_t *row_nnz;
-    int32_t *full_local, *part_local;  // [n][n], row-local lists of J
-    uint64_t *words;                   // [n][n][64], row-local order
-};
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-// 256 threads.  Thread t reads, for k = 0..7, mask row 8k + (t >> 5) of the
-// strip, bytes 16*(t & 31) .. +15 of the current 8-tile window: tile
-// jj = (t & 31) >> 2, columns 16*((t & 31) & 3) .. +15 of that tile.  Each
-// wavefront instruction thus reads two contiguous 512-byte row pieces.
-__global__ __launch_bounds__(256) void enc_rows(const uint8_t *__restrict__ mask,
-                                                int S, int n, Scratch sc) {
-    __shared__ uint64_t words[kT][64];
-    __shared__ int wsum[kT][4];
-    __shared__ uint32_t rows_any[8];
-    const int I = blockIdx.x;
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    const int r0 = t >> 5, c = t & 31, jj = c >> 2, quarter = c & 3;
-    const uint8_t *strip = mask + (size_t)64 * I * S;
-    uint8_t *wb = reinterpret_cast<uint8_t *>(&words[0][0]);
-
-    uint4 cur[8], nxt[8];
-    auto load = [&](uint4 (&v)[8], int J0) {
-        const bool ok = J0 + jj < n;
+// Loads of one window: thread t reads, for k = 0..7, mask row 8k + (t >> 5)
+// of the strip, bytes 16*(t & 31) .. +15 of the window (tile (t & 31) >> 2,
+// columns 16*(t & 3) .. +15 of it).  Each wavefront instruction reads two
+// contiguous 512-byte row pieces.  Tiles at or past n read as zero.
+__device__ __forceinline__ void load_window(u4v (&v)[8], const uint8_t *strip,
+                                            int S, int n, int J0, int t) {
+    const int r0 = t >> 5, c = t & 31;
+    const bool ok = J0 + (c >> 2) < n;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            v[k] = ok ? *reinterpret_cast<const uint4 *>(
-                            strip + (size_t)(8 * k + r0) * S + 64 * J0 + 16 * c)
-                      : make_uint4(0, 0, 0, 0);
-    };
-
-    uint32_t any_rows = 0;  // bit k: row 8k + r0 has a valid element so far
-    int run_f = 0, run_p = 0;
-    long long nnz = 0;
-    load(cur, 0);
-    for (int J0 = 0; J0 < n; J0 += kT) {
-        if (J0 + kT < n) load(nxt, J0 + kT);
-        int cnt = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            // inner tile (k, 2*quarter) and (k, 2*quarter+1), its row r0
-            const uint32_t b0 = row_bits8(cur[k].x, cur[k].y);
-            const uint32_t b1 = row_bits8(cur[k].z, cur[k].w);
-            wb[jj * 512 + (k * 8 + 2 * quarter) * 8 + r0] = (uint8_t)b0;
-            wb[jj * 512 + (k * 8 + 2 * quarter + 1) * 8 + r0] = (uint8_t)b1;
-            cnt += __popc(b0) + __popc(b1);
-            any_rows |= (uint32_t)((b0 | b1) != 0) << k;
-        }
-        // lanes of one tile within this wavefront: quarters (xor 1, 2) and
-        // the two row offsets (xor 32)
-        cnt += __shfl_xor(cnt, 1);
-        cnt += __shfl_xor(cnt, 2);
-        cnt += __shfl_xor(cnt, 32);
-        if (lane < 32 && quarter == 0) wsum[jj][w] = cnt;
-        __syncthreads();
-
-        // walk the window's tiles in column order (uniform in every thread)
-#pragma unroll
-        for (int j = 0; j < kT; ++j) {
-            const int J = J0 + j;
-            if (J >= n) break;
-            const int cj = wsum[j][0] + wsum[j][1] + wsum[j][2] + wsum[j][3];
-            if (cj == 0) continue;
-            nnz += cj;
-            if (cj == 64 * 64) {
-                if (t == 0) sc.full_local[(size_t)I * n + run_f] = J;
-                ++run_f;
-            } else {
-                if (t == 0) sc.part_local[(size_t)I * n + run_p] = J;
-                if (w == (j & 3))
-                    sc.words[((size_t)I * n + run_p) * 64 + lane] = words[j][lane];
-                ++run_p;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
-    }
-
-    // rows without a valid key: OR the masks of the 32 lanes that share r0
-    uint32_t a = any_rows;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) a |= __shfl_xor(a, off);
-    if (c == 0) rows_any[r0] = a;
-    __syncthreads();
-    if (t == 0) {
-        int empty = 0;
-        for (int r = 0; r < 8; ++r) empty += 8 - __popc(rows_any[r] & 0xFFu);
-        sc.row_nf[I] = run_f;
-        sc.row_np[I] = run_p;
-        sc.row_nnz[I] = nnz;
-        sc.row_empty[I] = empty;
-    }
+    for (int k = 0; k < 8; ++k)
+        v[k] = ok ? *reinterpret_cast<const u4v *>(
+                        strip + (size_t)(8 * k + r0) * S + 64 * J0 + 16 * c)
+                  : u4v{0, 0, 0, 0};
 }
 
 template <typename T> __device__ inline T block_sum(T x, T *sh) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
     __syncthreads();
-    return sh[0] + sh[1] + sh[2] + sh[3];
+    const T r = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();  // sh may be reused right away
+    return r;
 }
 
 __device__ inline int block_max(int x, int *sh) {
     for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
     __syncthreads();
-    return max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+    const int r = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+    __syncthreads();
+    return r;
 }
 
-__global__ __launch_bounds__(256) void enc_finish(int n, Scratch sc,
-                                                  smh_mask_enc enc) {
-    __shared__ int shi[4];
-    __shared__ long long shl[4];
-    const int I = blockIdx.x, t = threadIdx.x;
-    const int nf = sc.row_nf[I], np = sc.row_np[I], ci = nf + np;
-    int pf = 0, pp = 0, rank = 0;
+
+constexpr int kMaxSegTiles = kWin * kMaxSegWin;  // 64
+constexpr int kMaxRows = SMH_MAX_S / 64;          // outer-tile rows
+constexpr int kFusedMaxSegs = 2048;
+
+struct Seg {  // per-segment scratch (EncLayout)
+    uint64_t *cnt, *off, *nnz, *any;
+    int32_t *fcol, *pcol;
+    uint64_t *words;
+    int cap;  // tiles of room per segment
+};
+
+__global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mask,
+                                                 int S, int n, SegPlan plan, Seg sg) {
+    // inner-tile words of the segment's tiles (tile l = 8 * window + j)
+    __shared__ uint64_t lw[kMaxSegTiles][64];
+    __shared__ int wsum[kMaxSegTiles][4];  // tile counts per wavefront
+    __shared__ int tkind[kMaxSegTiles];    // rank | 1<<16 partial | 1<<17 full
+    __shared__ uint32_t rows_any[8];
+
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int s = blockIdx.x;
+    const int I = s / plan.per_row, seg_c = s % plan.per_row;
+    const int nw = (n + kWin - 1) / kWin;
+    const int w0 = seg_c * plan.win;
+    const int nwin = min(plan.win, nw - w0);  // windows in this segment
+
+    {
+        const uint8_t *strip = mask + (size_t)64 * I * S;
+        uint8_t *wb = reinterpret_cast<uint8_t *>(&lw[0][0]);
+        const int r0 = t >> 5, c = t & 31, jj = c >> 2, quarter = c & 3;
+        uint32_t any_rows = 0;  // bit k: row 8k + r0 has a valid element
+        u4v cur[8], nxt[8];
+        load_window(cur, strip, S, n, kWin * w0, t);
+        for (int wi = 0; wi < nwin; ++wi) {
+            if (wi + 1 < nwin) load_window(nxt, strip, S, n, kWin * (w0 + wi + 1), t);
+            uint8_t *tb = wb + (size_t)(kWin * wi + jj) * 512;
+            int cnt = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                // inner tiles (k, 2*quarter) and (k, 2*quarter+1), their row r0
+                const uint32_t b0 = row_bits8(cur[k][0], cur[k][1]);
+                const uint32_t b1 = row_bits8(cur[k][2], cur[k][3]);
+                tb[(k * 8 + 2 * quarter) * 8 + r0] = (uint8_t)b0;
+                tb[(k * 8 + 2 * quarter + 1) * 8 + r0] = (uint8_t)b1;
+                cnt += __popc(b0) + __popc(b1);
+                any_rows |= (uint32_t)((b0 | b1) != 0) << k;
+            }
+            // lanes of one tile within this wavefront: quarters (xor 1, 2)
+            // and the two row offsets (xor 32)
+            cnt += __shfl_xor(cnt, 1);
+            cnt += __shfl_xor(cnt, 2);
+            cnt += __shfl_xor(cnt, 32);
+            if (lane < 32 && quarter == 0) wsum[kWin * wi + jj][w] = cnt;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
+        }
+        // query rows covered in this segment: OR over the 32 lanes sharing r0
+        uint32_t a = any_rows;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) a |= __shfl_xor(a, off);
+        if (c == 0) rows_any[r0] = a;
+    }
+    __syncthreads();
+
+    // classify the tiles (wavefront 0, lane = tile), write columns and counts
+    if (w == 0) {
+        const int wi = lane >> 3, J = kWin * (w0 + wi) + (lane & 7);
+        const bool valid = wi < nwin && J < n;
+        const int cnt = valid ? wsum[lane][0] + wsum[lane][1] + wsum[lane][2] +
+                                    wsum[lane][3]
+                              : 0;
+        const bool full = cnt == 64 * 64, part = cnt > 0 && !full;
+        const uint64_t mf = __ballot(full), mp = __ballot(part);
+        const uint64_t below = (1ull << lane) - 1;
+        const int rf = __popcll(mf & below), rp = __popcll(mp & below);
+        tkind[lane] = full ? (1 << 17) | rf : part ? (1 << 16) | rp : 0;
+        if (full) sg.fcol[(size_t)s * sg.cap + rf] = J;
+        if (part) sg.pcol[(size_t)s * sg.cap + rp] = J;
+        long long nz = cnt;
+        for (int off = 32; off > 0; off >>= 1) nz += __shfl_xor(nz, off);
+        if (lane == 0) {
+            uint64_t any64 = 0;  // bit 8k + r: query row 8k + r of the strip
+            for (int r = 0; r < 8; ++r)
+                for (int k = 0; k < 8; ++k)
+                    any64 |= (uint64_t)((rows_any[r] >> k) & 1u) << (8 * k + r);
+            sg.cnt[s] = ((uint64_t)__popcll(mf) << 32) | (uint64_t)__popcll(mp);
+            sg.nnz[s] = (uint64_t)nz;
+            sg.any[s] = any64;
+        }
+    }
+    __syncthreads();
+    // partial-tile words, one wavefront per tile
+    for (int l = w; l < kWin * nwin; l += 4) {
+        const int k = tkind[l];
+        if (k & (1 << 16))
+            sg.words[((size_t)s * sg.cap + (k & 0xFFFF)) * 64 + lane] = lw[l][lane];
+    }
+}
+
+// Exclusive scan over the 256 threads of a workgroup.
+__device__ inline unsigned long long block_exclusive_scan(unsigned long long x,
+                                                          unsigned long long *sh) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    unsigned long long incl = x;
+    for (int d = 1; d < 64; d <<= 1) {
+        const unsigned long long y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    unsigned long long before = 0;
+    for (int q = 0; q < w; ++q) before += sh[q];
+    const unsigned long long r = before + incl - x;
+    __syncthreads();
+    return r;
+}
+
+// Exclusive scan of the segments' tile counts, row pointers, statistics and
+// the heavy-first schedule (one workgroup of 256 threads).  Writes each
+// segment's offsets when `offsets` is set.  Thread t owns a run of whole
+// rows; every load of the first pass is independent of the others, so the
+// pass costs one memory round trip.
+__device__ void scan_body(int n, SegPlan plan, Seg sg, smh_mask_enc enc,
+                          bool offsets) {
+    __shared__ int rowf[kMaxRows], rowp[kMaxRows];
+    __shared__ unsigned long long sh_u[4];
+    __shared__ long long sh_l[4];
+    __shared__ int sh_i[4];
+    const int t = threadIdx.x;
+    const int C = plan.per_row;
+    const int rows_per = (n + 255) / 256;
+    const int r_lo = min(n, t * rows_per), r_hi = min(n, r_lo + rows_per);
+    unsigned long long own = 0;
+    long long nnz = 0, empty = 0;
+    int mx = 0;
+    for (int I = r_lo; I < r_hi; ++I) {
+        unsigned long long rc = 0;
+        uint64_t an = 0;
+#pragma unroll 8
+        for (int c = 0; c < C; ++c) {
+            rc += sg.cnt[I * C + c];
+            nnz += (long long)sg.nnz[I * C + c];
+            an |= sg.any[I * C + c];
+        }
+        const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull);
+        rowf[I] = f;
+        rowp[I] = p;
+        mx = max(mx, f + p);
+        empty += 64 - __popcll(an);
+        own += rc;
+    }
+    unsigned long long run = block_exclusive_scan(own, sh_u);  // prefix of row r_lo
+    for (int I = r_lo; I < r_hi; ++I) {
+        enc.full_row_ptr[I] = (int32_t)(run >> 32);
+        enc.part_row_ptr[I] = (int32_t)(run & 0xFFFFFFFFull);
+        if (offsets) {
+            unsigned long long r2 = run;
+            for (int c = 0; c < C; ++c) {
+                sg.off[I * C + c] = r2;
+                r2 += sg.cnt[I * C + c];
+            }
+        }
+        run += ((unsigned long long)rowf[I] << 32) | (unsigned long long)rowp[I];
+    }
+    if (t == 255) {  // the last thread ends at the total
+        enc.full_row_ptr[n] = (int32_t)(run >> 32);
+        enc.part_row_ptr[n] = (int32_t)(run & 0xFFFFFFFFull);
+        enc.stats[1] = (int64_t)(run >> 32);
+        enc.stats[2] = (int64_t)(run & 0xFFFFFFFFull);
+    }
+    nnz = block_sum(nnz, sh_l);
+    empty = block_sum(empty, sh_l);
+    mx = block_max(mx, sh_i);
+    // heavy-first schedule: rank = number of rows that sort before row J
     for (int J = t; J < n; J += 256) {
-        const int f = sc.row_nf[J], p = sc.row_np[J];
-        if (J < I) {
-            pf += f;
-            pp += p;
+        const int cj = rowf[J] + rowp[J];
+        int rank = 0;
+        for (int J2 = 0; J2 < n; ++J2) {
+            const int c2 = rowf[J2] + rowp[J2];
+            rank += (c2 > cj) || (c2 == cj && J2 < J);
         }
-        rank += (f + p > ci) || (f + p == ci && J < I);
+        enc.row_order[rank] = J;
     }
-    pf = block_sum(pf, shi);
-    pp = block_sum(pp, shi);
-    rank = block_sum(rank, shi);
     if (t == 0) {
-        enc.full_row_ptr[I] = pf;
-        enc.part_row_ptr[I] = pp;
-        enc.row_order[rank] = I;
+        enc.stats[0] = nnz;
+        enc.stats[3] = empty;
+        enc.stats[4] = mx;
     }
-    if (I == n - 1) {
-        long long nnz = 0;
-        int empty = 0, mx = 0;
-        for (int J = t; J < n; J += 256) {
-            nnz += sc.row_nnz[J];
-            empty += sc.row_empty[J];
-            mx = max(mx, sc.row_nf[J] + sc.row_np[J]);
-        }
-        nnz = block_sum(nnz, shl);
-        empty = block_sum(empty, shi);
-        mx = block_max(mx, shi);
-        if (t == 0) {
-            enc.full_row_ptr[n] = pf + nf;
-            enc.part_row_ptr[n] = pp + np;
-            enc.stats[0] = nnz;
-            enc.stats[1] = pf + nf;
-            enc.stats[2] = pp + np;
-            enc.stats[3] = empty;
-            enc.stats[4] = mx;
-        }
+}
+
+__global__ __launch_bounds__(256) void enc_scan(int n, SegPlan plan, Seg sg,
+                                                smh_mask_enc enc) {
+    scan_body(n, plan, sg, enc, true);
+}
+
+// Placement of segment blockIdx.x.  kSelf: the workgroup adds up the tile
+// counts of the segments before it; the extra last workgroup runs the scan.
+// Otherwise the offsets come from enc_scan.  The segment's own columns and
+// first words are loaded together with its offsets (they do not depend on
+// them), so a small segment is placed after one memory round trip.
+template <bool kSelf>
+__global__ __launch_bounds__(256) void enc_place(int n, SegPlan plan, Seg sg,
+                                                 smh_mask_enc enc) {
+    __shared__ unsigned long long sh_u[4];
+    const int t = threadIdx.x, s = blockIdx.x;
+    if (kSelf && s == plan.total) {
+        scan_body(n, plan, sg, enc, false);
+        return;
     }
-    for (int i = t; i < nf; i += 256)
-        enc.full_col_idx[pf + i] = sc.full_local[(size_t)I * n + i];
-    for (int i = t; i < np; i += 256)
-        enc.part_col_idx[pp + i] = sc.part_local[(size_t)I * n + i];
-    // the row's partial-tile words are one contiguous block in both places
-    const uint4 *src = reinterpret_cast<const uint4 *>(sc.words + (size_t)I * n * 64);
-    uint4 *dst = reinterpret_cast<uint4 *>(enc.part_bitmaps + (size_t)pp * 64);
-    const int chunks = np * 32;
-    for (int e = t; e < chunks; e += 256) dst[e] = src[e];
+    const size_t base = (size_t)s * sg.cap;
+    const uint64_t cnt = sg.cnt[s];
+    // columns (t < cap) and the first 256 16-byte chunks of the words
+    const int colf = t < sg.cap ? sg.fcol[base + t] : 0;
+    const int colp = t < sg.cap ? sg.pcol[base + t] : 0;
+    const u4v *src = reinterpret_cast<const u4v *>(sg.words + base * 64);
+    const u4v w0 = t < sg.cap * 32 ? src[t] : u4v{0, 0, 0, 0};
+    unsigned long long off;
+    if (kSelf) {
+        unsigned long long x = 0;
+        for (int j = t; j < s; j += 256) x += sg.cnt[j];
+        off = block_sum(x, sh_u);
+    } else {
+        off = sg.off[s];
+    }
+    const int pf = (int)(off >> 32), pp = (int)(off & 0xFFFFFFFFull);
+    const int nf = (int)(cnt >> 32), np = (int)(cnt & 0xFFFFFFFFull);
+    if (t < nf) enc.full_col_idx[pf + t] = colf;
+    if (t < np) enc.part_col_idx[pp + t] = colp;
+    u4v *dst = reinterpret_cast<u4v *>(enc.part_bitmaps + (size_t)pp * 64);
+    if (t < np * 32) dst[t] = w0;
+    for (int e = t + 256; e < np * 32; e += 256) dst[e] = src[e];
 }
 
 // S == 0: an empty encoding.  Row pointers {0}, all statistics zero.
@@ -233,18 +335,29 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
         return hipGetLastError();
     }
     const int n = (int)L.n;
-    Scratch sc;
-    sc.row_nf = (int32_t *)(ws + L.row_nf);
-    sc.row_np = (int32_t *)(ws + L.row_np);
-    sc.row_empty = (int32_t *)(ws + L.row_empty);
-    sc.row_nnz = (int64_t *)(ws + L.row_nnz);
-    sc.full_local = (int32_t *)(ws + L.full_local);
-    sc.part_local = (int32_t *)(ws + L.part_local);
-    sc.words = (uint64_t *)(ws + L.tile_words);
-    hipLaunchKernelGGL(enc_rows, dim3(n), dim3(256), 0, stream, mask, S, n, sc);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(enc_finish, dim3(n), dim3(256), 0, stream, n, sc, enc);
+    const SegPlan plan = L.plan;
+    if (plan.total <= 0 || plan.win > kMaxSegWin || n > kMaxRows)
+        return hipErrorInvalidValue;
+    Seg sg;
+    sg.cnt = (uint64_t *)(ws + L.seg_cnt);
+    sg.off = (uint64_t *)(ws + L.seg_off);
+    sg.nnz = (uint64_t *)(ws + L.seg_nnz);
+    sg.any = (uint64_t *)(ws + L.seg_any);
+    sg.fcol = (int32_t *)(ws + L.seg_fcol);
+    sg.pcol = (int32_t *)(ws + L.seg_pcol);
+    sg.words = (uint64_t *)(ws + L.seg_words);
+    sg.cap = (int)L.seg_cap;
+    hipLaunchKernelGGL(enc_strip, dim3(plan.total), dim3(256), 0, stream, mask,
+                       S, n, plan, sg);
+    if (plan.total <= kFusedMaxSegs) {
+        hipLaunchKernelGGL(enc_place<true>, dim3(plan.total + 1), dim3(256), 0,
+                           stream, n, plan, sg, enc);
+    } else {
+        hipLaunchKernelGGL(enc_scan, dim3(1), dim3(256), 0, stream, n, plan, sg,
+                           enc);
+        hipLaunchKernelGGL(enc_place<false>, dim3(plan.total), dim3(256), 0,
+                           stream, n, plan, sg, enc);
+    }
     return hipGetLastError();
 }
 

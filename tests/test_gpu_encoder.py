@@ -52,6 +52,30 @@ def test_corner_and_random_masks(fam, S, kw):
     check(mask_family(fam, S, seed=S, **kw), dev)
 
 
+def band_and_points(S, w, npts, seed):
+    """Band |i - j| <= w, a full block of rows and scattered single points:
+    full, partial and empty tiles in every outer-tile row, cheap at any S."""
+    m = np.zeros((S, S), bool)
+    for d in range(-w, w + 1):
+        i = np.arange(max(0, -d), min(S, S - d))
+        m[i, i + d] = True
+    m[64:192, : S // 2] = True
+    rng = np.random.default_rng(seed)
+    m[rng.integers(0, S, npts), rng.integers(0, S, npts)] = True
+    return m
+
+
+@pytest.mark.parametrize("S", [576, 6400, 16448, 19200, 25600])
+def test_segment_cuts(S):
+    """Sizes whose rows are cut into several segments of one or more
+    windows, the last segment and its last window ragged (n = 9, 100, 257,
+    300, 400 outer tiles per side; n = 400 makes 2800 segments, past the
+    fused placement's limit, so the scan runs as a launch of its own)."""
+    dev = need_gpu()
+    print(f"encoder segment cuts S={S}", flush=True)
+    check(band_and_points(S, 70, 4 * S, seed=S), dev)
+
+
 def test_single_elements_and_diagonal():
     dev = need_gpu()
     S = 192
@@ -94,3 +118,15 @@ def test_deterministic_and_reusable_workspace():
     enc = smh.encode_mask(torch.from_numpy(~m).to(dev), workspace=ws)
     c = enc_to_host(enc, smh.mask_stats_get(enc))
     assert_same_encoding(c, encode_c(~m))
+
+
+def test_workspace_reused_across_sizes():
+    """One workspace serves encodes of different S in turn."""
+    dev = need_gpu()
+    ws = torch.full((smh.encode_workspace_bytes(1024),), 0xAB,
+                    dtype=torch.uint8, device=dev)
+    for S, p in [(1024, 0.2), (256, 0.5), (64, 0.9), (1024, 0.01), (512, 0.3)]:
+        m = mask_family("random", S, seed=S, p=p)
+        enc = smh.encode_mask(torch.from_numpy(m).to(dev), workspace=ws)
+        got = enc_to_host(enc, smh.mask_stats_get(enc))
+        assert_same_encoding(got, encode_c(m))
