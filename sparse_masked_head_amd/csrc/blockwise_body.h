@@ -23,12 +23,15 @@
 //     v_mfma_f32_16x16x32 (A = K rows from LDS, B = its Q rows held in
 //     registers for the whole row).  In this accumulator layout lane l holds
 //     query l%16's scores against keys 16st + 4(l/16) + i;
-//   * partial tiles reset masked scores to -inf: each lane loads from the
+//   * partial tiles get -inf for masked scores: each lane loads from the
 //     tile's 64 words the four bytes (one per 16-key sub-tile) that hold
-//     its query row's bits, together with the K tile, and carries its 16
-//     mask bits in a register until the tile's softmax;
-//   * online softmax in base 2 (running max and sum per query); only the
-//     4 lanes sharing a query exchange values (two gfx950 row swaps);
+//     its query row's bits, together with the K tile, carries them in a
+//     register, and starts the tile's QK^T accumulators at 0 / -inf from
+//     them, so the masking costs two VALU operations per score;
+//   * online softmax in base 2 (running max and sum per query) with lazy
+//     rescaling (the reference max moves only when passed by more than 8
+//     in exponent units); only the 4 lanes sharing a query exchange values
+//     (two gfx950 row swaps);
 //   * O^T += V^T P^T with the same MFMA: P^T is the B operand straight from
 //     the score registers rounded to the input type, V^T the A operand from
 //     LDS; the O rows a lane holds belong to the query whose softmax state
@@ -86,15 +89,21 @@ __device__ __attribute__((always_inline)) inline void fetch_k(
     }
 }
 
-// The lane's 16 mask bits of a fetched partial tile: bit 4st + i = key
-// 16st + 4g + i of its query row (nib = 4(g&1)).
+// The lane's mask bits of a fetched partial tile: bit 8st + i (i < 4) =
+// key 16st + 4g + i of its query row (nib = 4(g&1)); the other bits are
+// not used.
 template <int D>
 __device__ __attribute__((always_inline)) inline uint32_t mask_bits(
     const KRegs<D> &r, int nib) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) m |= ((r.mb[st] >> nib) & 0xFu) << (4 * st);
-    return m;
+    return (r.mb[0] | (r.mb[1] << 8) | (r.mb[2] << 16) | (r.mb[3] << 24)) >> nib;
+}
+
+// Bit `off` of x as 0 or -1 (v_bfe_i32; written out so that the compiler
+// keeps this one-instruction form instead of a compare and a select).
+template <int off> __device__ __attribute__((always_inline)) inline int bit_mask(int x) {
+    int r;
+    asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(r) : "v"(x), "i"(off));
+    return r;
 }
 
 // Global loads of V tile J, the same contiguous chunks as K.
@@ -143,19 +152,32 @@ template <int D> struct RowState {
     float m, l;
 };
 
-// S^T = K Q^T for one tile (four 16-key sub-tiles), raw scores.
-template <int D, typename TIn>
-__device__ __attribute__((always_inline)) inline void qk_tile(
+// S^T = K Q^T for one tile (four 16-key sub-tiles), raw scores.  For a
+// partial tile the accumulators start at 0 for a valid key and -inf for a
+// masked one (mbits: bit 8st + i = key 16st + 4g + i is valid), so masked
+// scores leave the matrix cores as -inf and the softmax needs no masking.
+// The two cases are separate code so that a full tile's first products
+// take the constant zero accumulator.
+template <int D, typename TIn, bool kPartial>
+__device__ __attribute__((always_inline)) inline void qk_tile_k(
     f4_t (&sc)[4], const typename Frag<TIn>::type (&qf)[D / 32],
-    const char *kb, int k_off) {
+    const char *kb, int k_off, uint32_t mbits) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     const TIn *ks = reinterpret_cast<const TIn *>(kb) + k_off;
+    const int inv = (int)~mbits;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        sc[st] = f4_t{0.f, 0.f, 0.f, 0.f};
+        f4_t c0 = f4_t{0.f, 0.f, 0.f, 0.f};
+        if (kPartial)  // all ones where masked -> the bits of -inf
+            c0 = f4_t{__int_as_float(bit_mask<0>(inv >> (8 * st)) & (int)0xFF800000u),
+                      __int_as_float(bit_mask<1>(inv >> (8 * st)) & (int)0xFF800000u),
+                      __int_as_float(bit_mask<2>(inv >> (8 * st)) & (int)0xFF800000u),
+                      __int_as_float(bit_mask<3>(inv >> (8 * st)) & (int)0xFF800000u)};
+        const frag a0 = *reinterpret_cast<const frag *>(ks + 16 * st * Lds<D>::KLD);
+        sc[st] = F::mfma(a0, qf[0], c0);
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
+        for (int s = 1; s < D / 32; ++s) {
             const frag a = *reinterpret_cast<const frag *>(
                 ks + 16 * st * Lds<D>::KLD + 32 * s);
             sc[st] = F::mfma(a, qf[s], sc[st]);
@@ -163,22 +185,24 @@ __device__ __attribute__((always_inline)) inline void qk_tile(
     }
 }
 
-// Softmax of one tile's scores (masked if `partial`) and O^T += V^T P^T.
-// c = scale * log2(e) > 0.
+template <int D, typename TIn>
+__device__ __attribute__((always_inline)) inline void qk_tile(
+    f4_t (&sc)[4], const typename Frag<TIn>::type (&qf)[D / 32],
+    const char *kb, int k_off, bool partial, uint32_t mbits) {
+    if (partial)
+        qk_tile_k<D, TIn, true>(sc, qf, kb, k_off, mbits);
+    else
+        qk_tile_k<D, TIn, false>(sc, qf, kb, k_off, mbits);
+}
+
+// Softmax of one tile's scores (masked ones already -inf) and
+// O^T += V^T P^T.  c = scale * log2(e) > 0.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void softmax_pv(
-    RowState<D> &rs, f4_t (&sc)[4], bool partial, uint32_t mbits,
-    const char *vb, float c, int v_off) {
+    RowState<D> &rs, f4_t (&sc)[4], const char *vb, float c, int v_off) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     using L = Lds<D>;
-    if (partial) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!((mbits >> (4 * st + i)) & 1u)) sc[st][i] = -INFINITY;
-    }
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -186,16 +210,19 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
         mx = fmaxf(fmaxf(mx, sc[st][2]), sc[st][3]);
     }
     mx = max_xor32(max_xor16(mx));
-    {
-        const float m_new = fmaxf(rs.m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((rs.m - m_use) * c);
+    // Lazy rescaling: the reference max rs.m moves only when a score passes
+    // it by more than 8 in base-2 exponent units, so most tiles skip the
+    // rescale; the probabilities then stay below 2^8 (well inside the input
+    // type's range) and the final division by l cancels the reference.
+    // (mx - m) * c is NaN (no move) when both are -inf, +inf when only m is.
+    const bool grow = (mx - rs.m) * c > 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : rs.m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((rs.m - m_new) * c) : 1.f;
         rs.m = m_new;
         rs.l *= alpha;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-            for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
-        }
+        for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
     }
     const float mc = (rs.m == -INFINITY ? 0.f : rs.m) * c;
 
@@ -243,12 +270,15 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
 }
 
 // The stored tiles of one outer-tile row: full tiles first, then partial.
+// Columns are clamped to [0, n): an encoding that is not this library's
+// then gives wrong numbers, never an access outside K and V.
 struct TileList {
     const int32_t *fci, *pci;
     const uint64_t *bm;
-    int f0, nF, p0, nT;
+    int f0, nF, p0, nT, nmax;
     __device__ int col(int idx) const {
-        return idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
+        const int J = idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
+        return (int)min((unsigned)J, (unsigned)nmax);
     }
     __device__ const uint64_t *words(int idx) const {
         return idx < nF ? nullptr : bm + (size_t)(p0 + idx - nF) * 64;
@@ -271,6 +301,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     tl.fci = a.fci;
     tl.pci = a.pci;
     tl.bm = a.bm;
+    tl.nmax = a.S / 64 - 1;
     tl.f0 = a.frp[I];
     tl.nF = a.frp[I + 1] - tl.f0;
     tl.p0 = a.prp[I];
@@ -299,55 +330,72 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     const int nib = 4 * (g & 1);
 
     // Pipeline: K (with its words) is staged two tiles ahead of its use and
-    // V one tile ahead, so that iteration `it` can issue QK^T of tile it+1
+    // V one tile ahead, so that tile step `it` can issue QK^T of tile it+1
     // before the softmax of tile it (matrix cores busy during the VALU
-    // work).  Buffers: K(it) in kbuf(it&1), V(it) in vbuf(it&1).
-    // mask bits ride along in registers: m_cur for tile it, m_nxt for
-    // it+1, m_k2 for it+2 (taken from the K registers when they are staged)
+    // work).  Buffers: K(it) in kbuf(it&1), V(it) in vbuf(it&1).  The mask
+    // bits ride along in registers, taken from the K registers when they
+    // are staged.  At d = 64 the loop is unrolled by two so that the two
+    // score buffers and mask slots swap roles instead of being copied.
     KRegs<D> kr, kr1;
     VRegs<D> vr;
-    f4_t s_cur[4], s_nxt[4];
-    uint32_t m_cur = 0, m_nxt = 0;
+    f4_t s_a[4], s_b[4];
+    uint32_t m_a = 0, m_b = 0;
     if (nT > 0) {
         fetch_k<D, TIn>(kr, Kh, tl.col(0), tl.words(0), b_off, t);
         fetch_v<D, TIn>(vr, Vh, tl.col(0), t);
         if (nT > 1) fetch_k<D, TIn>(kr1, Kh, tl.col(1), tl.words(1), b_off, t);
         stage_k<D, TIn>(kr, L::kbuf(smem, 0), t);
-        if (nF == 0) m_cur = mask_bits<D>(kr, nib);
+        if (nF == 0) m_a = mask_bits<D>(kr, nib);
         stage_v<D>(vr, L::vbuf(smem, 0), t);
         if (nT > 1) {
             stage_k<D, TIn>(kr1, L::kbuf(smem, 1), t);
-            if (1 >= nF) m_nxt = mask_bits<D>(kr1, nib);
+            if (1 >= nF) m_b = mask_bits<D>(kr1, nib);
         }
         if (nT > 2) fetch_k<D, TIn>(kr, Kh, tl.col(2), tl.words(2), b_off, t);
         if (nT > 1) fetch_v<D, TIn>(vr, Vh, tl.col(1), t);
     }
     __syncthreads();
-    if (nT > 0) qk_tile<D, TIn>(s_cur, qf, L::kbuf(smem, 0), k_off);
-    // every wave has read K(0) before iteration 0 overwrites its buffer
+    if (nT > 0) qk_tile<D, TIn>(s_a, qf, L::kbuf(smem, 0), k_off, nF == 0, m_a);
+    // every wave has read K(0) before tile step 0 overwrites its buffer
     __syncthreads();
 
-    for (int it = 0; it < nT; ++it) {
+    // One tile step: scores of tile it in `cur` (mask mc), of tile it+1 go
+    // to `nxt` (mask mn); mc is then reused for tile it+2's mask.
+    auto step = [&](int it, f4_t(&cur)[4], f4_t(&nxt)[4], uint32_t &mc,
+                    const uint32_t mn) __attribute__((always_inline)) {
         const int cb = it & 1, nb = cb ^ 1;
-        if (it + 1 < nT) qk_tile<D, TIn>(s_nxt, qf, L::kbuf(smem, nb), k_off);
-        softmax_pv<D, TIn>(rs, s_cur, it >= nF, m_cur, L::vbuf(smem, cb), a.c,
-                           v_off);
-        // K(it+2) replaces K(it) (read in the previous iteration); V(it+1)
+        if (it + 1 < nT)
+            qk_tile<D, TIn>(nxt, qf, L::kbuf(smem, nb), k_off, it + 1 >= nF, mn);
+        softmax_pv<D, TIn>(rs, cur, L::vbuf(smem, cb), a.c, v_off);
+        // K(it+2) replaces K(it) (read in the previous step); V(it+1)
         // replaces V(it-1)
-        uint32_t m_k2 = 0;
+        uint32_t m2 = 0;
         if (it + 2 < nT) {
             stage_k<D, TIn>(kr, L::kbuf(smem, cb), t);
-            if (it + 2 >= nF) m_k2 = mask_bits<D>(kr, nib);
+            if (it + 2 >= nF) m2 = mask_bits<D>(kr, nib);
         }
         if (it + 1 < nT) stage_v<D>(vr, L::vbuf(smem, nb), t);
         if (it + 3 < nT)
             fetch_k<D, TIn>(kr, Kh, tl.col(it + 3), tl.words(it + 3), b_off, t);
         if (it + 2 < nT) fetch_v<D, TIn>(vr, Vh, tl.col(it + 2), t);
         __syncthreads();
+        mc = m2;
+    };
+    if constexpr (D == 64) {
+        for (int it = 0; it < nT; it += 2) {
+            step(it, s_a, s_b, m_a, m_b);
+            if (it + 1 >= nT) break;
+            step(it + 1, s_b, s_a, m_b, m_a);
+        }
+    } else {  // measured: the unrolled body is slower at d = 128
+        for (int it = 0; it < nT; ++it) {
+            step(it, s_a, s_b, m_a, m_b);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) s_cur[st] = s_nxt[st];
-        m_cur = m_nxt;
-        m_nxt = m_k2;
+            for (int st = 0; st < 4; ++st) s_a[st] = s_b[st];
+            const uint32_t m2 = m_a;
+            m_a = m_b;
+            m_b = m2;
+        }
     }
 
     // epilogue: total l over the 4 lanes of this query
