@@ -81,8 +81,9 @@ def sweep(out_path, quick=False):
 
 def model(coef, p):
     """Python restatement of select_costs_us for fitting (same formula)."""
-    launch, bt, bp, bs, rv, rk, rs = coef
+    launch, bt, bp, bs, rg, rk, rsg, rsk = coef
     st = p["stats"]
+    n = p["S"] // 64
     tiles = st["n_full"] + st["n_partial"]
     w_blk = p["BH"] * (tiles * bt + st["n_partial"] * bp)
     t_blk = launch + max(w_blk, st["max_row_tiles"] * bs)
@@ -91,8 +92,11 @@ def model(coef, p):
         rho = (st["nnz"] - 4096.0 * st["n_full"]) / (4096.0 * st["n_partial"])
         rho = min(max(rho, 0.0), 1.0)
         live += st["n_partial"] * 64.0 * (1.0 - (1.0 - rho) ** 8)
-    w_row = p["BH"] * 8.0 * (tiles * rv + live * rk)
-    t_row = launch + max(w_row, st["max_row_tiles"] * rs)
+    chunks = live / 64.0 + n
+    w_row = p["BH"] * (tiles * rg + 8.0 * chunks * rk)
+    live_max = live / tiles * st["max_row_tiles"] if tiles else 0.0
+    s_row = st["max_row_tiles"] / 8.0 * rsg + (live_max / 64.0 + 1.0) * rsk
+    t_row = launch + max(w_row, s_row)
     return t_row, t_blk
 
 
@@ -110,15 +114,23 @@ def fit(points):
                 r.append(np.log(tr / p["t_row_us"]))
                 r.append(np.log(tb / p["t_blk_us"]))
             return np.array(r)
-        c0 = np.array([4.0, 1e-3, 2e-4, 0.3, 4e-4, 2e-5, 0.9])
+        c0 = np.array([4.0, 1e-3, 2e-4, 0.5, 1e-4, 1e-3, 1.0, 1.0])
         res = least_squares(resid, c0, x_scale=c0)
         c = np.abs(res.x)
-        agree = sum((model(c, p)[0] < model(c, p)[1]) ==
-                    (p["t_row_us"] < p["t_blk_us"]) for p in pts)
+        agree = regret = best_sum = 0
+        for p in pts:
+            tr, tb = model(c, p)
+            best = min(p["t_row_us"], p["t_blk_us"])
+            got = p["t_row_us"] if tr < tb else p["t_blk_us"]
+            agree += (tr < tb) == (p["t_row_us"] < p["t_blk_us"])
+            regret += got - best
+            best_sum += best
         out[d] = dict(coef=c.tolist(), rms_log=float(np.sqrt(np.mean(
-            res.fun ** 2))), agree=agree, n=len(pts))
+            res.fun ** 2))), agree=agree, n=len(pts),
+            regret=regret / best_sum)
         print(f"d={d}: coef {np.array2string(c, precision=4)}  rms log "
-              f"{out[d]['rms_log']:.3f}  choice agrees {agree}/{len(pts)}")
+              f"{out[d]['rms_log']:.3f}  choice agrees {agree}/{len(pts)}  "
+              f"time lost to wrong picks {100 * regret / best_sum:.2f}%")
     return out
 
 

@@ -221,7 +221,7 @@ inline long long resident_workgroups(Kernel kern, int lds) {
 // 2 block-wise (same function as smh_select_kernel on the host).
 template <int D, typename TIn, typename TOut>
 __device__ inline int device_choice(const FwdArgs<TIn, TOut> &a) {
-    return select_on_device(a.stats, a.BH, D, is_bf16<TIn>());
+    return select_on_device(a.stats, a.BH, a.S / 64, D, is_bf16<TIn>());
 }
 
 }  // namespace smh

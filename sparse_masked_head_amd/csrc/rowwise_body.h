@@ -10,18 +10,21 @@
 //
 // The 8 rows are one inner-tile row of an outer-tile row, so for a partial
 // outer tile the 8 inner-tile words (ir, 0..7) hold exactly their mask.  The
-// wavefront never executes s_barrier; it uses its own slice of LDS (query
-// rows and probabilities).  Per outer tile J (full tiles, then partial):
-//   * lane j owns key 64J + j and builds the 8-bit set of rows that see it
-//     (all rows for a full tile; a byte gather from the words otherwise); a
-//     lane whose set is empty loads nothing;
-//   * scores: lane j dots its K row with the 8 query rows (v_dot2, fp32
-//     accumulation); pairs outside the mask get -inf;
-//   * online softmax per row with 64-lane DPP max reductions; a row with
-//     no key in the tile is skipped;
-//   * P V with lane = output column: the probabilities pass through the LDS
-//     slice and the wavefront walks only the keys some row sees (the ballot
-//     of non-empty lanes), four keys per step so their V loads overlap.
+// wavefront never executes s_barrier; it uses its own slice of LDS.  Its
+// work follows the live keys, not the stored tiles:
+//   * gather: 8 stored tiles per step, lane = (tile, inner-tile column ic);
+//     the lane's 64-bit word transposed as an 8x8 bit matrix gives, in byte
+//     c, the set of rows that see key 8ic + c (all rows for a full tile);
+//     every key with a non-empty set is appended to a ring of pending
+//     entries (rows << 24 | key) in LDS (a wave prefix sum places them);
+//   * chunks of 64 entries, lane = entry: the lane's K row against the 8
+//     query rows (v_dot2, fp32 accumulation; pairs outside the mask -inf),
+//     online softmax per row with 64-lane DPP max reductions (a row with no
+//     key in the chunk is skipped), probabilities through LDS, then P V with
+//     lane = output column over the chunk's keys, 8 keys per batch with
+//     the next batch's V loads in flight.
+// A wavefront thus touches K and V only for keys some of its rows see, in
+// full 64-key chunks, however the keys are spread over the tiles.
 // Probabilities stay in fp32 here.
 #pragma once
 
@@ -31,139 +34,250 @@ namespace smh {
 
 constexpr int kRowsPerWave = 8;
 
-// LDS of one wavefront: probabilities [64 keys][8 rows] and 8 query rows.
+// LDS of one wavefront: the 8 query rows, the ring of pending entries and
+// the probabilities of one chunk [64 entries][8 rows].
 template <int D> struct RowLds {
-    static constexpr int P_BYTES = 64 * kRowsPerWave * 4;
+    static constexpr int CAP = 1024;  // > 63 pending + 8 full tiles (512)
     static constexpr int Q_BYTES = kRowsPerWave * D * 2;
-    static constexpr int BYTES = P_BYTES + Q_BYTES;
+    static constexpr int RING_BYTES = CAP * 4;
+    static constexpr int P_BYTES = 64 * kRowsPerWave * 4;
+    static constexpr int BYTES = Q_BYTES + RING_BYTES + P_BYTES;
 };
+
+// 8x8 bit-matrix transpose: bit 8r + c -> bit 8c + r (three delta swaps).
+__device__ inline uint64_t transpose8x8(uint64_t x) {
+    uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
+    x = x ^ t ^ (t << 7);
+    t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
+    x = x ^ t ^ (t << 14);
+    t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
+    return x ^ t ^ (t << 28);
+}
+
+// Bit b set iff byte b of x is nonzero (b < 8).
+__device__ inline uint32_t nonzero_byte_mask(uint64_t x) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) m |= (uint32_t)(((x >> (8 * b)) & 0xFFu) != 0) << b;
+    return m;
+}
+
+// Softmax state of the wavefront's 8 rows (lane-local partial sums; the
+// output columns of this lane).
+template <int D> struct RwState {
+    static constexpr int E = D / 64;  // output columns per lane
+    float m[kRowsPerWave], lp[kRowsPerWave], o[kRowsPerWave][E];
+};
+
+// One chunk: entries ring[head .. head+n) (n <= 64), lane = entry.
+template <int D, typename TIn>
+__device__ __attribute__((always_inline)) inline void rw_chunk(
+    RwState<D> &st, const uint32_t *ring, uint32_t head, int n,
+    const uint32_t *qbuf, float *pbuf, const TIn *__restrict__ Kh,
+    const TIn *__restrict__ Vh, float c) {
+    constexpr int R = kRowsPerWave;
+    constexpr int E = RwState<D>::E;
+    constexpr int CAP = RowLds<D>::CAP;
+    const int lane = threadIdx.x & 63;
+    const uint32_t ent = lane < n ? ring[(head + lane) & (CAP - 1)] : 0u;
+    const uint32_t rb = ent >> 24;
+    const int key = (int)(ent & 0xFFFFFFu);
+
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = 0.f;
+    if (rb) {
+        const u4_t *krow = reinterpret_cast<const u4_t *>(Kh + (size_t)key * D);
+        constexpr int H = D / 8 > 8 ? 8 : D / 8;  // 16-byte pieces per half row
+#pragma unroll
+        for (int h0 = 0; h0 < D / 8; h0 += H) {
+            u4_t kc[H];
+#pragma unroll
+            for (int cc = 0; cc < H; ++cc) kc[cc] = krow[h0 + cc];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                // one query row at a time: keeps its LDS reads from all
+                // being scheduled (and held in registers) at once
+                __builtin_amdgcn_sched_barrier(0);
+                float acc = s[r];
+#pragma unroll
+                for (int cc = 0; cc < H; ++cc) {
+                    const u4_t qc = *reinterpret_cast<const u4_t *>(
+                        qbuf + r * (D / 2) + 4 * (h0 + cc));
+                    acc = dot2<TIn>(qc[0], kc[cc][0], acc);
+                    acc = dot2<TIn>(qc[1], kc[cc][1], acc);
+                    acc = dot2<TIn>(qc[2], kc[cc][2], acc);
+                    acc = dot2<TIn>(qc[3], kc[cc][3], acc);
+                }
+                s[r] = acc;
+            }
+        }
+    }
+    float p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        p[r] = 0.f;
+        // a row with no key in this chunk keeps its state unchanged
+        if (!__builtin_amdgcn_ballot_w64((rb >> r) & 1)) continue;
+        const float sr = (rb >> r) & 1 ? s[r] : -INFINITY;
+        const float mx = wave_max(sr);
+        const float m_new = fmaxf(st.m[r], mx);
+        const float alpha = __builtin_amdgcn_exp2f((st.m[r] - m_new) * c);
+        st.m[r] = m_new;
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sr, c, -m_new * c));
+        st.lp[r] = st.lp[r] * alpha + p[r];
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.o[r][e] *= alpha;
+    }
+    wave_lds_sync();  // the previous chunk's readers of pbuf are done
+    {
+        f4_t *dst = reinterpret_cast<f4_t *>(pbuf + lane * R);
+        dst[0] = f4_t{p[0], p[1], p[2], p[3]};
+        dst[1] = f4_t{p[4], p[5], p[6], p[7]};
+    }
+    wave_lds_sync();
+
+    // P V: lane = output columns lane*E .. +E-1, 8 entries per batch, the
+    // next batch's V loads issued before this batch's products
+    constexpr int BATCH = 8;
+    const TIn *vcol = Vh + lane * E;
+    float vv[2][BATCH][E];
+    auto load = [&](int slot, int b0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int ei = b0 + u;
+            const int k = ei < n ? (int)(ring[(head + ei) & (CAP - 1)] & 0xFFFFFFu) : 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                vv[slot][u][e] = ei < n ? (float)vcol[(size_t)k * D + e] : 0.f;
+        }
+    };
+    load(0, 0);
+    for (int b0 = 0; b0 < n; b0 += 2 * BATCH) {
+        if (b0 + BATCH < n) load(1, b0 + BATCH);
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const f4_t pa = *reinterpret_cast<const f4_t *>(pbuf + (b0 + u) * R);
+            const f4_t pb = *reinterpret_cast<const f4_t *>(pbuf + (b0 + u) * R + 4);
+            const float pr[R] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < E; ++e) st.o[r][e] = fmaf(pr[r], vv[0][u][e], st.o[r][e]);
+        }
+        if (b0 + BATCH >= n) break;
+        if (b0 + 2 * BATCH < n) load(0, b0 + 2 * BATCH);
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int ei = b0 + BATCH + u;
+            const f4_t pa = *reinterpret_cast<const f4_t *>(pbuf + ei * R);
+            const f4_t pb = *reinterpret_cast<const f4_t *>(pbuf + ei * R + 4);
+            const float pr[R] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < E; ++e) st.o[r][e] = fmaf(pr[r], vv[1][u][e], st.o[r][e]);
+        }
+    }
+}
 
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void rowwise_group(
     const FwdArgs<TIn, TOut> &a, char *slice, int I, int ir, int bh) {
     constexpr int R = kRowsPerWave;
-    constexpr int E = D / 64;  // output columns per lane
-    float *pbuf = reinterpret_cast<float *>(slice);              // [64][R]
-    uint32_t *qbuf = reinterpret_cast<uint32_t *>(slice + RowLds<D>::P_BYTES);  // [R][D/2]
+    constexpr int E = RwState<D>::E;
+    constexpr int CAP = RowLds<D>::CAP;
+    uint32_t *qbuf = reinterpret_cast<uint32_t *>(slice);  // [R][D/2]
+    uint32_t *ring = reinterpret_cast<uint32_t *>(slice + RowLds<D>::Q_BYTES);
+    float *pbuf = reinterpret_cast<float *>(slice + RowLds<D>::Q_BYTES + RowLds<D>::RING_BYTES);
     const int lane = threadIdx.x & 63;
     const int row0 = 64 * I + 8 * ir;
-    const size_t head = (size_t)bh * a.S * D;
-    const TIn *Kh = a.K + head, *Vh = a.V + head;
+    const size_t head_off = (size_t)bh * a.S * D;
+    const TIn *Kh = a.K + head_off, *Vh = a.V + head_off;
+    const int nmax = a.S / 64 - 1;
 
     {  // stage the 8 query rows (contiguous) into the slice
-        const u4_t *src = reinterpret_cast<const u4_t *>(a.Q + head + (size_t)row0 * D);
+        const u4_t *src = reinterpret_cast<const u4_t *>(a.Q + head_off + (size_t)row0 * D);
         u4_t *dst = reinterpret_cast<u4_t *>(qbuf);
         for (int e = lane; e < R * D / 8; e += 64) dst[e] = src[e];
     }
-    wave_lds_sync();
 
     const int f0 = a.frp[I], nF = a.frp[I + 1] - f0;
     const int p0 = a.prp[I], nP = a.prp[I + 1] - p0;
     const int nT = nF + nP;
 
-    float m[R], lp[R], o[R][E];
+    RwState<D> st;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        m[r] = -INFINITY;
-        lp[r] = 0.f;
+        st.m[r] = -INFINITY;
+        st.lp[r] = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[r][e] = 0.f;
+        for (int e = 0; e < E; ++e) st.o[r][e] = 0.f;
     }
+    wave_lds_sync();
 
-    for (int it = 0; it < nT; ++it) {
-        const bool partial = it >= nF;
-        const int J = partial ? a.pci[p0 + it - nF] : a.fci[f0 + it];
-        uint32_t rb = 0xFFu;  // rows that see key 64J + lane
-        if (partial) {
-            const uint64_t wd = a.bm[(size_t)(p0 + it - nF) * 64 + ir * 8 + (lane >> 3)];
-            // bit 8r + (lane&7) of the word -> bit r: keep the chosen bit of
-            // each byte, then one multiply gathers the 8 byte-LSBs into the
-            // top byte (no two partial products meet in bits 56..63)
-            const uint64_t x = (wd >> (lane & 7)) & 0x0101010101010101ull;
-            rb = (uint32_t)((x * 0x0102040810204080ull) >> 56);
-        }
-
-        float s[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) s[r] = 0.f;
-        if (rb) {
-            const u4_t *krow = reinterpret_cast<const u4_t *>(Kh + (size_t)(64 * J + lane) * D);
-#pragma unroll 4
-            for (int cc = 0; cc < D / 8; ++cc) {
-                const u4_t kc = krow[cc];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const u4_t qc = *reinterpret_cast<const u4_t *>(qbuf + r * (D / 2) + 4 * cc);
-                    float acc = s[r];
-                    acc = dot2<TIn>(qc[0], kc[0], acc);
-                    acc = dot2<TIn>(qc[1], kc[1], acc);
-                    acc = dot2<TIn>(qc[2], kc[2], acc);
-                    acc = dot2<TIn>(qc[3], kc[3], acc);
-                    s[r] = acc;
-                }
+    // gather step: tile t0 + lane/8, inner-tile column lane%8; the loads of
+    // the next step are issued before this step's work
+    const int ic = lane & 7;
+    auto fetch = [&](int t0, int &J, uint64_t &w) __attribute__((always_inline)) {
+        const int tile = t0 + (lane >> 3);
+        J = 0;
+        w = 0;
+        if (tile < nT) {
+            if (tile < nF) {
+                J = a.fci[f0 + tile];
+                w = ~0ull;
+            } else {
+                const int p = p0 + tile - nF;
+                J = a.pci[p];
+                w = a.bm[(size_t)p * 64 + ir * 8 + ic];
             }
         }
-        float p[R];
+        J = (int)min((unsigned)J, (unsigned)nmax);  // never outside K / V
+    };
+    uint32_t head = 0, tail = 0;  // ring positions (uniform)
+    int J_cur, J_nxt = 0;
+    uint64_t w_cur, w_nxt = 0;
+    fetch(0, J_cur, w_cur);
+    for (int t0 = 0; t0 < nT; t0 += 8) {
+        if (t0 + 8 < nT) fetch(t0 + 8, J_nxt, w_nxt);
+        const uint64_t x = transpose8x8(w_cur);  // byte c: rows seeing key 8ic+c
+        const uint32_t nzb = nonzero_byte_mask(x);
+        const int cnt = __popc(nzb);
+        int incl = cnt;  // inclusive prefix over lanes
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            p[r] = 0.f;
-            // a row with no key in this tile keeps its state unchanged
-            if (!__builtin_amdgcn_ballot_w64((rb >> r) & 1)) continue;
-            const float sr = (rb >> r) & 1 ? s[r] : -INFINITY;
-            const float mx = wave_max(sr);
-            const float m_new = fmaxf(m[r], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m[r] - m_use) * a.c);
-            m[r] = m_new;
-            p[r] = __builtin_amdgcn_exp2f(fmaf(sr, a.c, -m_use * a.c));
-            lp[r] = lp[r] * alpha + p[r];
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[r][e] *= alpha;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
         }
-        wave_lds_sync();  // the previous tile's readers of pbuf are done
-        {
-            f4_t *dst = reinterpret_cast<f4_t *>(pbuf + lane * R);
-            dst[0] = f4_t{p[0], p[1], p[2], p[3]};
-            dst[1] = f4_t{p[4], p[5], p[6], p[7]};
+        const int total = __shfl(incl, 63);
+        uint32_t pos = tail + (uint32_t)(incl - cnt);
+        uint32_t m = nzb;
+        while (m) {
+            const int cb = __builtin_ctz(m);
+            m &= m - 1;
+            const uint32_t rbits = (uint32_t)(x >> (8 * cb)) & 0xFFu;
+            ring[pos & (CAP - 1)] = (rbits << 24) | (uint32_t)(64 * J_cur + 8 * ic + cb);
+            ++pos;
         }
+        tail += (uint32_t)total;
         wave_lds_sync();
-
-        uint64_t live = __ballot(rb != 0);
-        const TIn *vt = Vh + (size_t)64 * J * D + lane * E;
-        while (live) {
-            int js[4];
-            float vv[4][E];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                js[u] = live ? __builtin_ctzll(live) : -1;
-                if (live) live &= live - 1;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    vv[u][e] = js[u] >= 0 ? (float)vt[(size_t)js[u] * D + e] : 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (js[u] < 0) break;
-                const f4_t pa = *reinterpret_cast<const f4_t *>(pbuf + js[u] * R);
-                const f4_t pb = *reinterpret_cast<const f4_t *>(pbuf + js[u] * R + 4);
-                const float pr[R] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) o[r][e] = fmaf(pr[r], vv[u][e], o[r][e]);
-            }
+        while (tail - head >= 64) {
+            rw_chunk<D, TIn>(st, ring, head, 64, qbuf, pbuf, Kh, Vh, a.c);
+            head += 64;
         }
+        J_cur = J_nxt;
+        w_cur = w_nxt;
     }
+    if (tail != head) rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qbuf, pbuf, Kh, Vh, a.c);
 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const float lt = wave_sum(lp[r]);
+        const float lt = wave_sum(st.lp[r]);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        TOut *orow = a.O + head + (size_t)(row0 + r) * D + lane * E;
+        TOut *orow = a.O + head_off + (size_t)(row0 + r) * D + lane * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) store1<TOut>(orow + e, o[r][e] * inv);
+        for (int e = 0; e < E; ++e) store1<TOut>(orow + e, st.o[r][e] * inv);
     }
     wave_lds_sync();  // the slice may be reused by the next group
 }

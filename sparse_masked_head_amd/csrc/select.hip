@@ -12,6 +12,7 @@ smh_kernel select_kernel(const smh_mask_stats &st, int64_t BH, int d,
     in.n_partial = st.n_partial;
     in.max_row_tiles = st.max_row_tiles;
     in.BH = BH;
+    in.n_ot = st.S / 64;
     in.d = d;
     in.bf16 = dtype == SMH_BF16;
     double tr, tb;

@@ -13,15 +13,20 @@
 //     masking cost.  When the launch fits in one wave of workgroups it runs
 //     for the length of its heaviest row instead:
 //       T_blk = c0 + max(W_blk, max_row_tiles * t_tile_serial).
-//   row-wise: one wavefront per (head, 8 query rows); each stored tile
-//     costs a fixed score pass plus a probability-times-V pass over the
-//     keys any of the 8 rows can see:
-//       T_row = c0 + max(visits * t_visit + live_keys * t_key,
-//                        max_row_tiles * t_visit_serial).
+//   row-wise: one wavefront per (head, 8 query rows); it gathers the keys
+//     its rows see from its row's stored tiles, 8 tiles per step, and
+//     processes them in chunks of 64:
+//       T_row = c0 + max(heads * (tiles * t_gather + 8 * chunks * t_chunk),
+//                        max_row_tiles / 8 * t_gather_serial
+//                        + (live_max / 64 + 1) * t_chunk_serial),
+//     chunks = live / 64 + n_ot summed over the groups of one inner-tile
+//     row index (each group pays at least one chunk).
 // Sparsity enters through the tile counts and the expected number of live
-// keys of a partial tile (from the partial tiles' mean density); sequence
-// length through the tile counts and the serial term.  The coefficients are
-// microseconds measured on MI355X.
+// keys per (tile, 8-row group) of a partial tile (from the partial tiles'
+// mean density, rho: 64 (1 - (1 - rho)^8)); sequence length through the
+// tile counts, n_ot and the serial terms.  The coefficients are
+// microseconds, fitted (sparse_masked_head_amd/calibrate.py) to a sweep of
+// both kernels on MI355X over mask families, S, heads and d.
 //
 // The same function runs on the host (smh_select_kernel) and inside both
 // kernels (SMH_AUTO without host statistics), so it is written without
@@ -38,26 +43,29 @@ namespace smh {
 
 struct SelectInput {
     int64_t nnz, n_full, n_partial, max_row_tiles;
-    int64_t BH;
+    int64_t BH, n_ot;
     int d, bf16;
 };
 
 struct SelectCoef {
-    double launch_us;      // fixed cost of a launch
-    double blk_tile_us;    // block-wise: one 64x64 tile, whole chip busy
-    double blk_part_us;    // block-wise: extra per partial tile
-    double blk_serial_us;  // block-wise: one tile on one workgroup
-    double row_visit_us;   // row-wise: one (8 rows, tile) visit, chip busy
-    double row_key_us;     // row-wise: one live key of a visit
-    double row_serial_us;  // row-wise: one visit on one wavefront
+    double launch_us;          // fixed cost of a launch
+    double blk_tile_us;        // block-wise: one 64x64 tile, whole chip busy
+    double blk_part_us;        // block-wise: extra per partial tile
+    double blk_serial_us;      // block-wise: one tile on one workgroup
+    double row_gather_us;      // row-wise: one (tile, head) gathered, chip busy
+    double row_chunk_us;       // row-wise: one 64-key chunk, chip busy
+    double row_gather_ser_us;  // row-wise: one 8-tile gather step, one wavefront
+    double row_chunk_ser_us;   // row-wise: one chunk on one wavefront
 };
 
 #pragma clang fp contract(off)
 SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                                    double *t_blk) {
-    // [d == 128]; fp16 and bf16 share coefficients
-    const SelectCoef k64 = {4.0, 1.2e-3, 0.2e-3, 0.35, 4.0e-4, 2.0e-5, 0.9};
-    const SelectCoef k128 = {4.0, 2.2e-3, 0.2e-3, 0.6, 7.0e-4, 3.0e-5, 1.6};
+    // fitted on MI355X; fp16 and bf16 share coefficients
+    const SelectCoef k64 = {5.4605, 1.8829e-3, 3.1919e-4, 0.87456,
+                            2.2136e-4, 2.6365e-3, 0.66979, 4.8045};
+    const SelectCoef k128 = {4.1144, 4.1525e-3, 1.6700e-4, 1.3979,
+                             4.0450e-4, 5.4630e-3, 0.48558, 7.7900};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
     const double heads = (double)in.BH;
@@ -76,9 +84,13 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
         miss = miss * miss;
         live += (double)in.n_partial * 64.0 * (1.0 - miss);
     }
+    const double chunks = live / 64.0 + (double)in.n_ot;
     const double w_row =
-        heads * 8.0 * (tiles * k.row_visit_us + live * k.row_key_us);
-    const double crit_row = (double)in.max_row_tiles * k.row_serial_us;
+        heads * (tiles * k.row_gather_us + 8.0 * chunks * k.row_chunk_us);
+    const double live_max =
+        tiles > 0.0 ? live / tiles * (double)in.max_row_tiles : 0.0;
+    const double crit_row = (double)in.max_row_tiles / 8.0 * k.row_gather_ser_us +
+                            (live_max / 64.0 + 1.0) * k.row_chunk_ser_us;
     *t_row = k.launch_us + (w_row > crit_row ? w_row : crit_row);
 }
 
@@ -92,13 +104,14 @@ SMH_HD inline int select_model(const SelectInput &in) {
 
 // Device side: read the statistics the encoder wrote and decide.
 __device__ inline int select_on_device(const int64_t *stats, int64_t BH,
-                                       int d, int bf16) {
+                                       int64_t n_ot, int d, int bf16) {
     SelectInput in;
     in.nnz = stats[0];
     in.n_full = stats[1];
     in.n_partial = stats[2];
     in.max_row_tiles = stats[4];
     in.BH = BH;
+    in.n_ot = n_ot;
     in.d = d;
     in.bf16 = bf16;
     return select_model(in);

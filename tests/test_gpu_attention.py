@@ -209,7 +209,7 @@ def test_fused_kernel_both_branches(d, dt):
     feed only the decision) to steer it into each branch; each branch's
     output is bitwise the forced kernel's."""
     dev = need_gpu()
-    S, B, H = 256, 1, 3
+    S, B, H = 512, 1, 3   # long enough rows for the model to pick each kernel
     mask = mask_family("random", S, seed=31, p=0.08)
     q, k, v = make_qkv(B, H, S, d, dt, seed=31)
     qd, kd, vd = (x.to(dev) for x in (q, k, v))

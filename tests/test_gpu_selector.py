@@ -53,3 +53,30 @@ def test_selector_picks_faster_kernel(cid, config_mask):
     print(f"  rowwise {t['rowwise']:.1f} us  blockwise {t['blockwise']:.1f} us"
           f"  choice {choice}", flush=True)
     assert t[choice] <= t[other] * (1 + TIE), (choice, t)
+
+
+@pytest.mark.parametrize("S,p,B,H,d", [(4096, 0.001, 1, 1, 64),
+                                       (2048, 0.001, 1, 8, 128),
+                                       (1024, 0.05, 1, 8, 64),
+                                       (512, 0.3, 2, 8, 64)])
+def test_selector_on_random_masks(S, p, B, H, d):
+    """Random (unstructured) masks from very sparse, where the row-wise
+    kernel is the faster one on this chip, to dense-ish, where the
+    block-wise kernel is: the choice is the faster kernel, or within 10%
+    of it (these shapes are small, so launch noise is a larger share)."""
+    from workloads import mask_family
+    dev = need_gpu()
+    print(f"selector random S={S} p={p} B={B} H={H} d={d}", flush=True)
+    q, k, v = (x.to(dev) for x in make_qkv(B, H, S, d, "f16", seed=S))
+    enc = smh.encode_mask(torch.from_numpy(
+        mask_family("random", S, seed=S, p=p)).to(dev))
+    st = smh.mask_stats_get(enc)
+    out = torch.empty_like(q)
+    t = {kern: _time_us(lambda: smh.sparse_mha_fwd(
+        q, k, v, enc, kernel=kern, out=out), 10)
+        for kern in ("rowwise", "blockwise")}
+    choice = smh.select_kernel(st, B, H, d, q.dtype)
+    other = "rowwise" if choice == "blockwise" else "blockwise"
+    print(f"  rowwise {t['rowwise']:.1f} us  blockwise {t['blockwise']:.1f} us"
+          f"  choice {choice}", flush=True)
+    assert t[choice] <= t[other] * 1.10, (choice, t)
