@@ -17,7 +17,9 @@ explainer, Technical summary > Methodology > 1. Unified MHA module,
 storage-format items): 64x64 outer tiles; empty ones skipped; all-valid ones
 listed as full; the rest listed as partial with one uint64 per 8x8 inner
 tile, inner tile (ir, ic) stored at position 8*ir+ic, element (r, c) of an
-inner tile at bit 8*r+c.
+inner tile at bit 8*r+c.  For S not a multiple of 64 the tiles cover
+ceil(S/64)*64 rows and columns and elements outside the S x S mask are not
+valid.
 """
 import ctypes
 import os
@@ -51,9 +53,9 @@ def encode_c(mask):
     m = np.ascontiguousarray(np.asarray(mask).astype(np.uint8, copy=False))
     S = m.shape[0]
     assert m.shape == (S, S)
-    if S <= 0 or S % OT:
-        raise ValueError("S must be a positive multiple of 64")
-    n = S // OT
+    if S <= 0:
+        raise ValueError("S must be positive")
+    n = (S + OT - 1) // OT
     frp = np.zeros(n + 1, np.int32)
     prp = np.zeros(n + 1, np.int32)
     fci = np.zeros(n * n, np.int32)
@@ -76,14 +78,17 @@ def encode_py(mask):
     """Pure-Python twin, element by element (small masks only)."""
     m = np.asarray(mask).astype(bool)
     S = m.shape[0]
-    if S <= 0 or S % OT:
-        raise ValueError("S must be a positive multiple of 64")
-    n = S // OT
+    if S <= 0:
+        raise ValueError("S must be positive")
+    n = -(-S // OT)
+
+    def at(i, j):  # elements outside the S x S mask are not valid
+        return i < S and j < S and bool(m[i, j])
     frp, fci, prp, pci, bms = [0], [], [0], [], []
     nnz = 0
     for I in range(n):
         for J in range(n):
-            tile = [[bool(m[OT * I + r, OT * J + c]) for c in range(OT)]
+            tile = [[at(OT * I + r, OT * J + c) for c in range(OT)]
                     for r in range(OT)]
             cnt = sum(sum(row) for row in tile)
             nnz += cnt

@@ -21,21 +21,31 @@
  *
  * The loops below visit the outer tiles row by row in ascending column
  * order and append, which is the definition of the lists.
+ *
+ * S need not be a multiple of 64: the tiles cover ceil(S/64) * 64 rows and
+ * columns, and an element outside the S x S mask is not valid (reading of
+ * the pages' "arbitrary mask" for ragged lengths).
  */
 #include <stdint.h>
 #include <string.h>
 
-/* Returns 0 on success, -1 if S is not a positive multiple of 64.
+/* Element (row, col) of the mask, 0 outside the S x S matrix. */
+static int valid(const uint8_t *mask, int64_t S, int64_t row, int64_t col)
+{
+    return row < S && col < S && mask[row * S + col] != 0;
+}
+
+/* Returns 0 on success, -1 if S is not positive.  n_ot = ceil(S / 64).
  * Output capacities: row_ptr arrays n_ot+1, col_idx arrays n_ot*n_ot,
  * bitmaps n_ot*n_ot*64.  stats[0]=nnz, [1]=n_full, [2]=n_partial,
- * [3]=number of query rows with no valid key. */
+ * [3]=number of query rows (of the S) with no valid key. */
 int ref_encode(const uint8_t *mask, int64_t S,
                int32_t *full_row_ptr, int32_t *full_col_idx,
                int32_t *part_row_ptr, int32_t *part_col_idx,
                uint64_t *part_bitmaps, int64_t *stats)
 {
-    if (S <= 0 || (S % 64) != 0) return -1;
-    const int64_t n_ot = S / 64;
+    if (S <= 0) return -1;
+    const int64_t n_ot = (S + 63) / 64;
     int64_t nnz = 0;
     int32_t n_full = 0, n_part = 0;
 
@@ -47,7 +57,7 @@ int ref_encode(const uint8_t *mask, int64_t S,
             int64_t cnt = 0;
             for (int64_t r = 0; r < 64; ++r)
                 for (int64_t c = 0; c < 64; ++c)
-                    cnt += mask[(64 * I + r) * S + (64 * J + c)] != 0;
+                    cnt += valid(mask, S, 64 * I + r, 64 * J + c);
             nnz += cnt;
             if (cnt == 0) continue;                 /* skipped tile */
             if (cnt == 64 * 64) {                   /* full tile */
@@ -64,7 +74,7 @@ int ref_encode(const uint8_t *mask, int64_t S,
                         for (int c = 0; c < 8; ++c) {
                             int64_t row = 64 * I + 8 * ir + r;
                             int64_t col = 64 * J + 8 * ic + c;
-                            if (mask[row * S + col])
+                            if (valid(mask, S, row, col))
                                 word |= (uint64_t)1 << (r * 8 + c);
                         }
                     bm[ir * 8 + ic] = word;

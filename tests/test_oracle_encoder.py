@@ -9,7 +9,10 @@
 * counting identity nnz = 4096 * n_full + popcount of all partial bitmaps;
 * structure: row pointers monotone, column indices strictly ascending and
   disjoint between the lists, partial tiles neither empty nor full;
-* the C loop and the Python twin agree on small masks.
+* the C loop and the Python twin agree on small masks;
+* ragged S (not a multiple of 64): closed forms of the full and causal
+  masks, and the padding identity (a ragged mask encodes like the same mask
+  padded with invalid elements to 64 * ceil(S/64)).
 """
 import json
 import os
@@ -27,9 +30,10 @@ ONES = (1 << 64) - 1
 
 
 def decode(enc, S):
-    """Independent inverse of the format: rebuild the dense mask."""
-    n = S // 64
-    m = np.zeros((S, S), bool)
+    """Independent inverse of the format: rebuild the dense mask (the
+    padding beyond S of a ragged mask must decode as invalid)."""
+    n = -(-S // 64)
+    m = np.zeros((64 * n, 64 * n), bool)
     for I in range(n):
         for t in range(enc["full_row_ptr"][I], enc["full_row_ptr"][I + 1]):
             J = int(enc["full_col_idx"][t])
@@ -44,11 +48,12 @@ def decode(enc, S):
                     if (w >> bit) & 1:
                         r, c = divmod(bit, 8)
                         m[64 * I + 8 * ir + r, 64 * J + 8 * ic + c] = True
-    return m
+    assert not m[S:].any() and not m[:, S:].any()
+    return m[:S, :S]
 
 
 def check_structure(enc, S):
-    n = S // 64
+    n = -(-S // 64)
     frp, prp = enc["full_row_ptr"], enc["part_row_ptr"]
     assert frp[0] == 0 and prp[0] == 0
     assert (np.diff(frp) >= 0).all() and (np.diff(prp) >= 0).all()
@@ -103,11 +108,74 @@ def test_full_and_empty():
     assert enc["n_empty_rows"] == 192
 
 
-def test_rejects_ragged():
+def test_ragged_full_closed_form():
+    """All-valid mask of S = 100: tiles (0,0) full; (0,1), (1,0), (1,1)
+    partial with 64x36, 36x64 and 36x36 valid elements.  Inner-tile column
+    4 of a tile holds mask columns 96..103, of which 96..99 exist: byte
+    0x0F in every row; inner-tile row 4 holds mask rows 96..103: bytes 0..3
+    all ones."""
+    S = 100
+    for enc in (encode_c(np.ones((S, S), bool)), encode_py(np.ones((S, S), bool))):
+        assert enc["full_row_ptr"].tolist() == [0, 1, 1]
+        assert enc["full_col_idx"].tolist() == [0]
+        assert enc["part_row_ptr"].tolist() == [0, 1, 3]
+        assert enc["part_col_idx"].tolist() == [1, 0, 1]
+        assert enc["nnz"] == S * S and enc["n_empty_rows"] == 0
+        col4 = 0x0F0F0F0F0F0F0F0F        # columns c < 4 in all 8 rows
+        row4 = 0x00000000FFFFFFFF        # rows r < 4, all 8 columns
+        t01 = [ONES if ic < 4 else (col4 if ic == 4 else 0)
+               for ir in range(8) for ic in range(8)]
+        t10 = [ONES if ir < 4 else (row4 if ir == 4 else 0)
+               for ir in range(8) for ic in range(8)]
+        t11 = [(ONES if ir < 4 else row4 if ir == 4 else 0) &
+               (ONES if ic < 4 else col4 if ic == 4 else 0)
+               for ir in range(8) for ic in range(8)]
+        assert enc["part_bitmaps"].tolist() == [t01, t10, t11]
+
+
+@pytest.mark.parametrize("S", [1, 65, 100, 191])
+def test_ragged_causal_closed_form(S):
+    """Causal mask of ragged S: nnz = S(S+1)/2; row I of n = ceil(S/64)
+    tiles stores tiles 0..I, tiles J < I full unless cut by S."""
+    m = np.tril(np.ones((S, S), bool))
+    n = -(-S // 64)
+    for enc in (encode_c(m), encode_py(m)):
+        assert enc["nnz"] == S * (S + 1) // 2 and enc["n_empty_rows"] == 0
+        full = [(I, J) for I in range(n) for J in range(I)
+                if 64 * (I + 1) <= S]       # below the diagonal, row not cut
+        assert enc["n_full"] == len(full)
+        assert enc["n_full"] + enc["n_partial"] == n * (n + 1) // 2
+        check_structure(enc, S)
+        assert np.array_equal(decode(enc, S), m)
+
+
+@pytest.mark.parametrize("S,p,seed", [(70, 0.3, 1), (130, 0.05, 2),
+                                      (200, 0.9, 3), (257, 0.5, 4)])
+def test_ragged_equals_padded(S, p, seed):
+    """A ragged mask encodes exactly like the same mask padded with invalid
+    elements to 64 * ceil(S/64), except that the padding's rows are not
+    counted as empty rows; the C loop and the Python twin agree."""
+    rng = np.random.default_rng(seed)
+    m = rng.random((S, S)) < p
+    Sp = 64 * -(-S // 64)
+    mp = np.zeros((Sp, Sp), bool)
+    mp[:S, :S] = m
+    a, b = encode_c(m), encode_c(mp)
+    for key in ("full_row_ptr", "full_col_idx", "part_row_ptr",
+                "part_col_idx", "part_bitmaps"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["nnz"] == b["nnz"] == int(m.sum())
+    assert a["n_empty_rows"] == b["n_empty_rows"] - (Sp - S)
+    assert a["n_empty_rows"] == int((~m.any(axis=1)).sum())
+    same(a, encode_py(m))
+    assert np.array_equal(decode(a, S), m)
+
+
+def test_rejects_nonpositive():
     with pytest.raises(ValueError):
-        encode_c(np.ones((100, 100), bool))
+        encode_c(np.ones((0, 0), bool))
     with pytest.raises(ValueError):
-        encode_py(np.ones((65, 65), bool))
+        encode_py(np.ones((0, 0), bool))
 
 
 @pytest.mark.parametrize("S", [64, 256, 1024])
