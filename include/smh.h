@@ -38,7 +38,7 @@ extern "C" {
 typedef enum {
     SMH_OK = 0,
     SMH_EINVAL = 1,        /* bad argument (null pointer, size mismatch, ...) */
-    SMH_EUNSUPPORTED = 2,  /* valid request outside what is built (d, dtype, S % 64) */
+    SMH_EUNSUPPORTED = 2,  /* valid request outside what is built (d, dtype) */
     SMH_ENOSPACE = 3,      /* workspace smaller than smh_encode_workspace_bytes */
     SMH_EHIP = 4           /* a HIP runtime call or kernel launch failed */
 } smh_status;
@@ -51,38 +51,52 @@ typedef enum {
     SMH_BLOCKWISE = 2   /* block-wise kernel ([EXP] block-wise kernel item) */
 } smh_kernel;
 
-/* Largest sequence length accepted (the encoding workspace grows as
- * (S/64)^2 * 1040 bytes: 4.4 GB at this limit). */
+/* Largest sequence length accepted (the encoding workspace of one mask
+ * grows as ceil(S/64)^2 * 1040 bytes: 4.4 GB at this limit). */
 #define SMH_MAX_S 131072
+/* Largest number of outer-tile rows of one encoding: masks in the stack
+ * times ceil(S/64). */
+#define SMH_MAX_ENC_ROWS 8192
 /* Outer tile edge and inner tile edge, in elements. */
 #define SMH_OT 64
 #define SMH_IT 8
 
-/* The two-level encoding of one S x S mask ([EXP] storage-format items).
- * A host struct of device pointers into the caller's workspace; it stays
- * valid while the workspace lives and may be reused by any number of
+/* The two-level encoding of a stack of S x S masks ([EXP] storage-format
+ * items).  A host struct of device pointers into the caller's workspace; it
+ * stays valid while the workspace lives and may be reused by any number of
  * smh_sparse_mha_fwd calls (every batch, head and layer that shares the
- * mask).  n_ot = S / 64 outer tiles per side.  Outer tile (I, J) covers
- * rows 64I..64I+63 and columns 64J..64J+63.
- *   full_row_ptr[n_ot+1], full_col_idx[n_full]: CSR lists of the outer
+ * masks).
+ *   The stack holds G = mask_b * mask_h masks, mask g = gb * mask_h + gh
+ *   (gb < mask_b, gh < mask_h); one mask is the stack 1 x 1.  Batch b and
+ *   head h of an attention call use mask (mask_b > 1 ? b : 0, mask_h > 1 ?
+ *   h : 0), so mask_b is 1 or B and mask_h is 1 or H (broadcasting).
+ *   n_ot = ceil(S / 64) outer tiles per side.  Outer tile (I, J) covers rows
+ *   64I..64I+63 and columns 64J..64J+63; when S is not a multiple of 64 the
+ *   last row and column of tiles are cut by S, and elements outside the
+ *   S x S mask count as not valid (so a cut tile is never full).
+ *   The encoding has R = G * n_ot rows: row g * n_ot + I is outer-tile row
+ *   I of mask g.  Column indices J are in [0, n_ot).
+ *   full_row_ptr[R+1], full_col_idx[n_full]: CSR lists of the outer
  *       tiles whose 4096 elements are all valid, J ascending in each row.
- *   part_row_ptr[n_ot+1], part_col_idx[n_partial]: CSR lists of the outer
+ *   part_row_ptr[R+1], part_col_idx[n_partial]: CSR lists of the outer
  *       tiles with some but not all elements valid, J ascending.
  *   part_bitmaps[n_partial * 64]: the p-th partial tile (global order, i.e.
  *       position p in part_col_idx) owns words 64p..64p+63; word 8*ir+ic is
  *       inner tile (ir, ic), covering tile rows 8ir..8ir+7 and columns
  *       8ic..8ic+7; bit 8*r+c of it is element (8ir+r, 8ic+c).
  *   Outer tiles with no valid element appear in neither list.
- *   stats[5] (device int64): nnz, n_full, n_partial, n_empty_rows (query
- *       rows with no valid key), max_row_tiles (stored tiles in the fullest
- *       outer-tile row).
- *   row_order[n_ot] (device int32): outer-tile rows sorted by their number
+ *   stats[5] (device int64), summed over the stack: nnz, n_full,
+ *       n_partial, n_empty_rows (query rows with no valid key), and
+ *       max_row_tiles (stored tiles in the fullest outer-tile row).
+ *   row_order[R] (device int32): the encoding's rows sorted by their number
  *       of stored tiles, most first, ties by ascending row (a schedule).
- * Capacities reserved in the workspace: col_idx arrays n_ot^2, bitmaps
- * n_ot^2 * 64 words. */
+ * Capacities reserved in the workspace: col_idx arrays R * n_ot, bitmaps
+ * R * n_ot * 64 words. */
 typedef struct {
     int32_t S;
     int32_t n_ot;
+    int32_t mask_b;
+    int32_t mask_h;
     int32_t *full_row_ptr;
     int32_t *full_col_idx;
     int32_t *part_row_ptr;
@@ -92,20 +106,29 @@ typedef struct {
     int32_t *row_order;
 } smh_mask_enc;
 
-/* Host copy of the encoding statistics. */
+/* Host copy of the encoding statistics (totals over the masks of the
+ * stack). */
 typedef struct {
-    int64_t nnz;          /* valid (query, key) pairs of the mask */
+    int64_t nnz;          /* valid (query, key) pairs of the masks */
     int32_t S;
     int32_t n_full;       /* full outer tiles */
     int32_t n_partial;    /* partial outer tiles */
     int32_t n_empty_rows; /* query rows with no valid key (their output is 0) */
     int32_t max_row_tiles; /* stored tiles in the fullest outer-tile row */
+    int32_t mask_b;       /* the stack's shape, as in smh_mask_enc */
+    int32_t mask_h;
 } smh_mask_stats;
 
 /* Bytes of device workspace smh_encode_mask needs for sequence length S
  * (encoding arrays plus internal scratch).  Returns 0 when S is not
- * accepted (S < 0, S % 64 != 0 or S > SMH_MAX_S); S == 0 is accepted. */
+ * accepted (S < 0 or S > SMH_MAX_S); S == 0 is accepted. */
 size_t smh_encode_workspace_bytes(int32_t S);
+
+/* The same for a stack of mask_b x mask_h masks (smh_encode_masks).
+ * Returns 0 when the arguments are not accepted (mask_b or mask_h < 1,
+ * S out of range, or mask_b * mask_h * ceil(S/64) > SMH_MAX_ENC_ROWS). */
+size_t smh_encode_masks_workspace_bytes(int32_t mask_b, int32_t mask_h,
+                                        int32_t S);
 
 /* Encode a dense mask ([EXP] storage-format items: BSR outer tiles split
  * into full and partial pointer arrays, empty tiles skipped, one uint64 per
@@ -115,17 +138,35 @@ size_t smh_encode_workspace_bytes(int32_t S);
  *   mask: device uint8 [S][S], row-major, 16-byte aligned, element (i, j)
  *         nonzero means query i attends to key j.  Read only.  NULL allowed
  *         only when S == 0.
- *   S: sequence length, 0 <= S <= SMH_MAX_S and S % 64 == 0 (else
- *      SMH_EUNSUPPORTED for S % 64 != 0, SMH_EINVAL for the rest).
+ *   S: sequence length, 0 <= S <= SMH_MAX_S (else SMH_EINVAL); any S,
+ *      the last outer tiles are cut when S % 64 != 0.
  *   workspace: device memory, 256-byte aligned, at least
  *      smh_encode_workspace_bytes(S) bytes (else SMH_ENOSPACE); it holds the
  *      encoding afterwards and must outlive every use of *enc_out.
- *   enc_out: host struct filled with pointers into workspace.
+ *   enc_out: host struct filled with pointers into workspace (mask_b =
+ *      mask_h = 1).
  * The result is deterministic and independent of the launch configuration.
  * Asynchronous on `stream`. */
 smh_status smh_encode_mask(const uint8_t *mask, int32_t S, void *workspace,
                            size_t ws_bytes, smh_mask_enc *enc_out,
                            void *stream);
+
+/* Encode a stack of masks, one per batch and/or head ([EXP] problem
+ * statement: the mask decides which pairs take part, and it may differ
+ * from sequence to sequence).  One encoding holds them all (layout in
+ * smh_mask_enc); the launches are those of smh_encode_mask, over every
+ * mask at once.
+ *   masks: device uint8 [mask_b][mask_h][S][S] contiguous, 16-byte
+ *          aligned, nonzero = valid.  Read only.
+ *   mask_b, mask_h >= 1, mask_b * mask_h * ceil(S/64) <= SMH_MAX_ENC_ROWS
+ *          (else SMH_EINVAL).
+ *   S, workspace (smh_encode_masks_workspace_bytes bytes), enc_out: as for
+ *          smh_encode_mask.
+ * Encoding a 1 x 1 stack is smh_encode_mask. */
+smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
+                            int32_t mask_h, int32_t S, void *workspace,
+                            size_t ws_bytes, smh_mask_enc *enc_out,
+                            void *stream);
 
 /* Copy the encoding statistics to the host.  Synchronises `stream`. */
 smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
@@ -135,8 +176,9 @@ smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
  * the row-wise and the block-wise kernel follows from mask sparsity and
  * sequence length; [ABS]: "analytical modeling").  Pure host arithmetic on
  * the statistics and the problem shape; touches no device.
- *   st: statistics of the mask (smh_mask_stats_get).
- *   B, H >= 0; d in {64, 128}; dt in {SMH_F16, SMH_BF16}.
+ *   st: statistics of the mask stack (smh_mask_stats_get).
+ *   B, H >= 0, st->mask_b in {1, B}, st->mask_h in {1, H} (else
+ *   SMH_EINVAL); d in {64, 128}; dt in {SMH_F16, SMH_BF16}.
  *   *out receives SMH_ROWWISE or SMH_BLOCKWISE. */
 smh_status smh_select_kernel(const smh_mask_stats *st, int32_t B, int32_t H,
                              int32_t d, smh_dtype dt, smh_kernel *out);
@@ -149,16 +191,20 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
                             double *t_blockwise_us);
 
 /* Masked attention forward: for every b < B, h < H and query row i,
- *   O[b,h,i,:] = sum_j w_j V[b,h,j,:] / sum_j w_j over valid keys j of row i,
+ *   O[b,h,i,:] = sum_j w_j V[b,h,j,:] / sum_j w_j over valid keys j of row i
+ *   in the mask of (b, h),
  *   w_j = exp(scale * <Q[b,h,i,:], K[b,h,j,:]> - max), and O = 0 for a row
  * with no valid key.  Outer tiles absent from the encoding are never read.
  *   q, k, v: device [B][H][S][d] contiguous, element type in_dt (SMH_F16 or
  *            SMH_BF16), 16-byte aligned.  Read only.
  *   o: device [B][H][S][d] contiguous, element type out_dt (in_dt or
  *      SMH_F32), 16-byte aligned, not overlapping q, k or v.
- *   B, H >= 0 (0 is a no-op); S == enc->S; d in {64, 128}.
+ *   B, H >= 0 (0 is a no-op); S == enc->S (any S up to SMH_MAX_S);
+ *   d in {64, 128}.
  *   scale: score multiplier, finite and >= 0; 0 means 1/sqrt(d).
- *   enc: encoding of the [S][S] mask shared by every (b, h).
+ *   enc: encoding of the mask stack: enc->mask_b in {1, B} and enc->mask_h
+ *        in {1, H} (else SMH_EINVAL); (b, h) uses the mask smh_mask_enc
+ *        describes.
  *   which: SMH_ROWWISE, SMH_BLOCKWISE, or SMH_AUTO.  With SMH_AUTO and st
  *          non-NULL the host decides (smh_select_kernel).  With SMH_AUTO and
  *          st NULL the same model is evaluated on the device from the
@@ -167,7 +213,9 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
  * Arithmetic: fp32 scores, softmax statistics and accumulators.  The
  * block-wise kernel rounds the probabilities to in_dt for its matrix-core
  * probability-times-V product (the row sums use the rounded values); the
- * row-wise kernel keeps them in fp32.  Asynchronous on `stream`. */
+ * row-wise kernel keeps them in fp32.  Q, K and V must be finite: a
+ * masked key's V row is multiplied by a zero probability.  Asynchronous on
+ * `stream`. */
 smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
                               void *o, int32_t B, int32_t H, int32_t S,
                               int32_t d, smh_dtype in_dt, smh_dtype out_dt,

@@ -12,8 +12,11 @@ module: the masking is exact), for every batch b, head h and query row i:
     O_i   = sum_j exp(s_j - m) V[b,h,j,:] / sum_j exp(s_j - m),  m = max s_j
     O_i   = 0                                            if J_i is empty
 
-tau = 1/sqrt(d) unless given.  Subtracting m changes no value; it only keeps
-exp from overflowing.  The empty-row convention (O = 0, never NaN) is a
+tau = 1/sqrt(d) unless given.  The mask may be one [S, S] matrix for every
+(b, h) or a stack [Bm, Hm, S, S] with Bm in {1, B} and Hm in {1, H}: (b, h)
+then uses mask[b if Bm > 1 else 0, h if Hm > 1 else 0] (a mask per sequence
+and/or per head; the pages' masks decide per pair, for any mask).
+Subtracting m changes no value; it only keeps exp from overflowing.  The empty-row convention (O = 0, never NaN) is a
 reading: the pages are silent on rows with no valid key.
 
 The dense score matrix is computed and masked afterwards, i.e. the
@@ -52,11 +55,28 @@ def _rows(q, k, v, mask_rows, tau):
     return out
 
 
+def mask_of(mask, b, h):
+    """The [S, S] mask that batch b, head h uses (broadcast rule above)."""
+    mask = np.asarray(mask)
+    if mask.ndim == 2:
+        return mask
+    return mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]
+
+
+def _check_mask(mask, B, H, S):
+    if mask.ndim == 2:
+        assert mask.shape == (S, S)
+    else:
+        assert mask.ndim == 4 and mask.shape[2:] == (S, S)
+        assert mask.shape[0] in (1, B) and mask.shape[1] in (1, H)
+
+
 def attention(q, k, v, mask, scale=None, row_block=1024):
     """Dense fp64 masked attention.
 
     q, k, v: [B, H, S, d] (numpy or CPU torch; upcast exactly to fp64).
-    mask: [S, S] bool, shared by every (b, h), True = pair takes part.
+    mask: bool, True = pair takes part: [S, S] shared by every (b, h), or
+    a stack [Bm, Hm, S, S] (mask_of).
     scale: tau, default 1/sqrt(d).
     Returns a float64 numpy array [B, H, S, d].
 
@@ -67,15 +87,16 @@ def attention(q, k, v, mask, scale=None, row_block=1024):
     mask = np.asarray(mask, dtype=bool)
     B, H, S, d = q.shape
     assert k.shape == (B, H, S, d) and v.shape == (B, H, S, d)
-    assert mask.shape == (S, S)
+    _check_mask(mask, B, H, S)
     tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
     out = np.empty((B, H, S, d), dtype=np.float64)
     for b in range(B):
         for h in range(H):
+            m = mask_of(mask, b, h)
             for r0 in range(0, S, row_block):
                 r1 = min(S, r0 + row_block)
                 out[b, h, r0:r1] = _rows(q[b, h, r0:r1], k[b, h], v[b, h],
-                                         mask[r0:r1], tau)
+                                         m[r0:r1], tau)
     return out
 
 
@@ -95,4 +116,5 @@ def attention_rows(q, k, v, mask, b, h, rows, scale=None):
     vb = _as_f64(v[b, h])
     d = qb.shape[1]
     tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
-    return _rows(qb, kb, vb, np.asarray(mask, dtype=bool)[rows], tau)
+    m = np.asarray(mask_of(mask, b, h), dtype=bool)
+    return _rows(qb, kb, vb, m[rows], tau)

@@ -4,8 +4,10 @@ TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
 ``encode_c`` runs the scalar C loop in ``encode_ref.c`` (built by
 ``oracle.build``); ``encode_py`` is a pure-Python twin of the same
-definition for small masks, written independently of the C loop.  Both
-return a dict:
+definition for small masks, written independently of the C loop;
+``encode_stack`` encodes a stack of masks [Bm, Hm, S, S] (one per sequence
+and/or head) as the masks' encodings one after another.  All return a
+dict:
 
     full_row_ptr  int32 [n_ot+1]     full_col_idx  int32 [n_full]
     part_row_ptr  int32 [n_ot+1]     part_col_idx  int32 [n_partial]
@@ -118,3 +120,30 @@ def encode_py(mask):
                 part_bitmaps=np.array(bms, np.uint64).reshape(-1, 64),
                 nnz=nnz, n_full=len(fci), n_partial=len(pci),
                 n_empty_rows=empty)
+
+
+def encode_stack(masks, encode=None):
+    """Encoding of a stack of masks [Bm, Hm, S, S]: the rows of mask
+    g = gb * Hm + gh follow those of mask g - 1, so the row pointers of
+    mask g are its own offset by the tiles of the masks before it, and the
+    lists and bitmaps are concatenated in that order.  Counts are totals.
+    Row g * n_ot + I of the result is outer-tile row I of mask g."""
+    encode = encode_c if encode is None else encode
+    m = np.asarray(masks)
+    assert m.ndim == 4 and m.shape[2] == m.shape[3]
+    parts = [encode(m[gb, gh]) for gb in range(m.shape[0])
+             for gh in range(m.shape[1])]
+    out = {}
+    for key in ("full", "part"):
+        ptrs, cols, base = [np.zeros(1, np.int32)], [], 0
+        for e in parts:
+            ptrs.append(e[key + "_row_ptr"][1:] + base)
+            cols.append(e[key + "_col_idx"])
+            base += int(e[key + "_row_ptr"][-1])
+        out[key + "_row_ptr"] = np.concatenate(ptrs).astype(np.int32)
+        out[key + "_col_idx"] = np.concatenate(cols).astype(np.int32)
+    out["part_bitmaps"] = np.concatenate(
+        [e["part_bitmaps"].reshape(-1, 64) for e in parts]).astype(np.uint64)
+    for key in ("nnz", "n_full", "n_partial", "n_empty_rows"):
+        out[key] = sum(int(e[key]) for e in parts)
+    return out

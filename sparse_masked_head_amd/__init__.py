@@ -6,6 +6,9 @@ and the current stream.  Function names are the C names without the
 ``smh_`` prefix.
 
     enc = encode_mask(mask)                 # mask: cuda bool/uint8 [S, S]
+                                            # or [Bm, Hm, S, S], Bm in {1, B},
+                                            # Hm in {1, H}: one mask per
+                                            # batch and/or head
     st = mask_stats_get(enc)                # host statistics (syncs)
     which = select_kernel(st, B, H, d, torch.float16)
     o = sparse_mha_fwd(q, k, v, enc, kernel="auto", stats=st)
@@ -43,25 +46,34 @@ def version():
     return lib().smh_version().decode()
 
 
-def encode_workspace_bytes(S):
-    return int(lib().smh_encode_workspace_bytes(int(S)))
+def encode_workspace_bytes(S, mask_b=1, mask_h=1):
+    return int(lib().smh_encode_masks_workspace_bytes(int(mask_b),
+                                                      int(mask_h), int(S)))
 
 
 class MaskEncoding:
-    """A mask's encoding: the device workspace that holds it and the C
-    struct of pointers into that workspace."""
+    """The encoding of a stack of masks [mask_b, mask_h, S, S]: the device
+    workspace that holds it and the C struct of pointers into that
+    workspace."""
 
-    def __init__(self, workspace, enc, S):
+    def __init__(self, workspace, enc, S, mask_b=1, mask_h=1):
         self.workspace = workspace
         self.enc = enc
         self.S = S
+        self.mask_b = mask_b
+        self.mask_h = mask_h
         self.device = workspace.device
+
+    @property
+    def rows(self):
+        """Outer-tile rows of the encoding (masks * ceil(S / 64))."""
+        return self.mask_b * self.mask_h * (-(-self.S // 64))
 
     def arrays(self, stats=None):
         """Views of the encoding arrays (device tensors), trimmed to their
         used length (needs the host statistics)."""
         st = stats if stats is not None else mask_stats_get(self)
-        n = self.S // 64
+        n = self.rows
         base = self.workspace.data_ptr()
 
         def view(ptr, count, dtype, width):
@@ -79,28 +91,35 @@ class MaskEncoding:
 
 
 def encode_mask(mask, workspace=None):
-    """Encode a [S, S] device mask (bool or uint8, nonzero = attend)."""
+    """Encode a device mask (bool or uint8, nonzero = attend): one [S, S]
+    mask, or a stack [mask_b, mask_h, S, S] whose mask (b', h') serves
+    batch b and head h with b' = b if mask_b > 1 else 0 and h' likewise."""
     if mask.dtype not in (torch.bool, torch.uint8):
         raise TypeError("mask must be bool or uint8")
     if not mask.is_cuda:
         raise ValueError("mask must be a device tensor")
-    if mask.dim() != 2 or mask.shape[0] != mask.shape[1]:
-        raise ValueError("mask must be square [S, S]")
+    if mask.dim() not in (2, 4) or mask.shape[-1] != mask.shape[-2]:
+        raise ValueError("mask must be [S, S] or [mask_b, mask_h, S, S]")
     mask = mask.contiguous()
-    S = int(mask.shape[0])
-    nbytes = encode_workspace_bytes(S)
+    if mask.data_ptr() % 16:
+        mask = mask.clone()
+    S = int(mask.shape[-1])
+    mb, mh = (1, 1) if mask.dim() == 2 else (int(mask.shape[0]),
+                                              int(mask.shape[1]))
+    nbytes = encode_workspace_bytes(S, mb, mh)
     if nbytes == 0:
-        check(lib().smh_encode_mask(None, S, None, 0, ctypes.byref(MaskEnc()),
-                                    None), "smh_encode_mask")
+        check(lib().smh_encode_masks(None, mb, mh, S, None, 0,
+                                     ctypes.byref(MaskEnc()), None),
+              "smh_encode_masks")
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=mask.device)
     enc = MaskEnc()
-    st = lib().smh_encode_mask(
-        ctypes.c_void_p(mask.data_ptr()), S,
+    st = lib().smh_encode_masks(
+        ctypes.c_void_p(mask.data_ptr()), mb, mh, S,
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
         ctypes.byref(enc), _stream(mask.device))
-    check(st, "smh_encode_mask")
-    return MaskEncoding(workspace, enc, S)
+    check(st, "smh_encode_masks")
+    return MaskEncoding(workspace, enc, S, mb, mh)
 
 
 def mask_stats_get(enc):
@@ -114,7 +133,8 @@ def mask_stats_get(enc):
 def _stats_struct(st):
     s = MaskStats()
     for k, _ in MaskStats._fields_:
-        setattr(s, k, int(st[k]))
+        # a dict without the stack shape describes one mask
+        setattr(s, k, int(st.get(k, 1) if k in ("mask_b", "mask_h") else st[k]))
     return s
 
 

@@ -9,15 +9,18 @@ SMH_OK, SMH_EINVAL, SMH_EUNSUPPORTED, SMH_ENOSPACE, SMH_EHIP = range(5)
 SMH_F16, SMH_BF16, SMH_F32 = range(3)
 SMH_AUTO, SMH_ROWWISE, SMH_BLOCKWISE = range(3)
 SMH_MAX_S = 131072
+SMH_MAX_ENC_ROWS = 8192
 
 # every exported name of include/smh.h
-EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_mask",
-           "smh_mask_stats_get", "smh_select_kernel", "smh_select_costs",
-           "smh_sparse_mha_fwd", "smh_status_string", "smh_version")
+EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_masks_workspace_bytes",
+           "smh_encode_mask", "smh_encode_masks", "smh_mask_stats_get",
+           "smh_select_kernel", "smh_select_costs", "smh_sparse_mha_fwd",
+           "smh_status_string", "smh_version")
 
 
 class MaskEnc(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int32), ("n_ot", ctypes.c_int32),
+                ("mask_b", ctypes.c_int32), ("mask_h", ctypes.c_int32),
                 ("full_row_ptr", ctypes.c_void_p),
                 ("full_col_idx", ctypes.c_void_p),
                 ("part_row_ptr", ctypes.c_void_p),
@@ -31,7 +34,8 @@ class MaskStats(ctypes.Structure):
     _fields_ = [("nnz", ctypes.c_int64), ("S", ctypes.c_int32),
                 ("n_full", ctypes.c_int32), ("n_partial", ctypes.c_int32),
                 ("n_empty_rows", ctypes.c_int32),
-                ("max_row_tiles", ctypes.c_int32)]
+                ("max_row_tiles", ctypes.c_int32),
+                ("mask_b", ctypes.c_int32), ("mask_h", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -58,9 +62,14 @@ def lib():
         p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         L.smh_encode_workspace_bytes.argtypes = [i32]
         L.smh_encode_workspace_bytes.restype = sz
+        L.smh_encode_masks_workspace_bytes.argtypes = [i32, i32, i32]
+        L.smh_encode_masks_workspace_bytes.restype = sz
         L.smh_encode_mask.argtypes = [p, i32, p, sz, ctypes.POINTER(MaskEnc),
                                       p]
         L.smh_encode_mask.restype = ctypes.c_int
+        L.smh_encode_masks.argtypes = [p, i32, i32, i32, p, sz,
+                                       ctypes.POINTER(MaskEnc), p]
+        L.smh_encode_masks.restype = ctypes.c_int
         L.smh_mask_stats_get.argtypes = [ctypes.POINTER(MaskEnc),
                                          ctypes.POINTER(MaskStats), p]
         L.smh_mask_stats_get.restype = ctypes.c_int

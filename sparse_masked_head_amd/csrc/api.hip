@@ -16,16 +16,31 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Outer-tile rows of a stack of mask_b x mask_h masks of S x S, or -1 when
+// the stack is not accepted.
+int64_t stack_rows(int32_t mask_b, int32_t mask_h, int32_t S) {
+    if (S < 0 || S > SMH_MAX_S || mask_b < 1 || mask_h < 1) return -1;
+    const int64_t rows = (int64_t)mask_b * mask_h * (((int64_t)S + SMH_OT - 1) / SMH_OT);
+    return rows > SMH_MAX_ENC_ROWS ? -1 : rows;
+}
+
+// A mask stack [mask_b][mask_h] serves B x H (batch, head) pairs when each
+// side is 1 (broadcast) or equal.
+bool broadcasts(int32_t mask_b, int32_t mask_h, int32_t B, int32_t H) {
+    return (mask_b == 1 || mask_b == B) && (mask_h == 1 || mask_h == H);
+}
+
 smh_status check_stats(const smh_mask_stats *st) {
     if (!st) return SMH_EINVAL;
-    if (st->S < 0 || st->S > SMH_MAX_S) return SMH_EINVAL;
-    if (st->S % SMH_OT) return SMH_EUNSUPPORTED;
-    const int64_t n = st->S / SMH_OT;
+    const int64_t rows = stack_rows(st->mask_b, st->mask_h, st->S);
+    if (rows < 0) return SMH_EINVAL;
+    const int64_t n = ((int64_t)st->S + SMH_OT - 1) / SMH_OT;
+    const int64_t G = (int64_t)st->mask_b * st->mask_h;
     if (st->n_full < 0 || st->n_partial < 0 || st->nnz < 0 ||
         st->max_row_tiles < 0 || st->n_empty_rows < 0)
         return SMH_EINVAL;
-    if ((int64_t)st->n_full + st->n_partial > n * n ||
-        st->nnz > (int64_t)st->S * st->S || st->max_row_tiles > n)
+    if ((int64_t)st->n_full + st->n_partial > rows * n ||
+        st->nnz > G * st->S * st->S || st->max_row_tiles > n)
         return SMH_EINVAL;
     return SMH_OK;
 }
@@ -35,16 +50,23 @@ smh_status check_select(const smh_mask_stats *st, int32_t B, int32_t H,
     smh_status s = check_stats(st);
     if (s != SMH_OK) return s;
     if (B < 0 || H < 0) return SMH_EINVAL;
+    if (B > 0 && H > 0 && !broadcasts(st->mask_b, st->mask_h, B, H))
+        return SMH_EINVAL;
     if (d != 64 && d != 128) return SMH_EUNSUPPORTED;
     if (dt != SMH_F16 && dt != SMH_BF16) return SMH_EUNSUPPORTED;
     return SMH_OK;
+}
+
+// (batch, head) pairs that share each mask of the stack.
+int64_t heads_per_mask(const smh_mask_stats *st, int32_t B, int32_t H) {
+    return (int64_t)(st->mask_b > 1 ? 1 : B) * (st->mask_h > 1 ? 1 : H);
 }
 
 }  // namespace
 
 extern "C" {
 
-const char *smh_version(void) { return "smh 0.1 (gfx950)"; }
+const char *smh_version(void) { return "smh 0.2 (gfx950)"; }
 
 const char *smh_status_string(smh_status s) {
     switch (s) {
@@ -57,28 +79,36 @@ const char *smh_status_string(smh_status s) {
     return "unknown status";
 }
 
-size_t smh_encode_workspace_bytes(int32_t S) {
-    if (S < 0 || S > SMH_MAX_S || S % SMH_OT) return 0;
-    return enc_layout(S).total;
+size_t smh_encode_masks_workspace_bytes(int32_t mask_b, int32_t mask_h,
+                                        int32_t S) {
+    if (stack_rows(mask_b, mask_h, S) < 0) return 0;
+    return enc_layout(S, (int64_t)mask_b * mask_h).total;
 }
 
-smh_status smh_encode_mask(const uint8_t *mask, int32_t S, void *workspace,
-                           size_t ws_bytes, smh_mask_enc *enc_out,
-                           void *stream) {
+size_t smh_encode_workspace_bytes(int32_t S) {
+    return smh_encode_masks_workspace_bytes(1, 1, S);
+}
+
+smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
+                            int32_t mask_h, int32_t S, void *workspace,
+                            size_t ws_bytes, smh_mask_enc *enc_out,
+                            void *stream) {
     try {
-        if (S < 0 || S > SMH_MAX_S) return SMH_EINVAL;
-        if (S % SMH_OT) return SMH_EUNSUPPORTED;
+        if (stack_rows(mask_b, mask_h, S) < 0) return SMH_EINVAL;
         if (!enc_out || !workspace) return SMH_EINVAL;
-        if (S > 0 && (!mask || !aligned(mask, 16))) return SMH_EINVAL;
+        if (S > 0 && (!masks || !aligned(masks, 16))) return SMH_EINVAL;
         if (!aligned(workspace, 256)) return SMH_EINVAL;
-        const EncLayout L = enc_layout(S);
+        const int64_t G = (int64_t)mask_b * mask_h;
+        const EncLayout L = enc_layout(S, G);
         if (ws_bytes < L.total) return SMH_ENOSPACE;
-        if (S > 0 && overlaps(mask, (size_t)S * S, workspace, L.total))
+        if (S > 0 && overlaps(masks, (size_t)G * S * S, workspace, L.total))
             return SMH_EINVAL;
         char *ws = (char *)workspace;
         smh_mask_enc e;
         e.S = S;
         e.n_ot = (int32_t)L.n;
+        e.mask_b = mask_b;
+        e.mask_h = mask_h;
         e.full_row_ptr = (int32_t *)(ws + L.full_row_ptr);
         e.full_col_idx = (int32_t *)(ws + L.full_col_idx);
         e.part_row_ptr = (int32_t *)(ws + L.part_row_ptr);
@@ -86,7 +116,7 @@ smh_status smh_encode_mask(const uint8_t *mask, int32_t S, void *workspace,
         e.part_bitmaps = (uint64_t *)(ws + L.part_bitmaps);
         e.stats = (int64_t *)(ws + L.stats);
         e.row_order = (int32_t *)(ws + L.row_order);
-        if (launch_encode(mask, S, ws, L, e, (hipStream_t)stream) !=
+        if (launch_encode(masks, S, ws, L, e, (hipStream_t)stream) !=
             hipSuccess)
             return SMH_EHIP;
         *enc_out = e;
@@ -96,10 +126,18 @@ smh_status smh_encode_mask(const uint8_t *mask, int32_t S, void *workspace,
     }
 }
 
+smh_status smh_encode_mask(const uint8_t *mask, int32_t S, void *workspace,
+                           size_t ws_bytes, smh_mask_enc *enc_out,
+                           void *stream) {
+    return smh_encode_masks(mask, 1, 1, S, workspace, ws_bytes, enc_out,
+                            stream);
+}
+
 smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
                               void *stream) {
     try {
         if (!enc || !out || !enc->stats) return SMH_EINVAL;
+        if (stack_rows(enc->mask_b, enc->mask_h, enc->S) < 0) return SMH_EINVAL;
         int64_t h[5];
         hipStream_t s = (hipStream_t)stream;
         if (hipMemcpyAsync(h, enc->stats, sizeof(h), hipMemcpyDeviceToHost,
@@ -112,6 +150,8 @@ smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
         out->n_partial = (int32_t)h[2];
         out->n_empty_rows = (int32_t)h[3];
         out->max_row_tiles = (int32_t)h[4];
+        out->mask_b = enc->mask_b;
+        out->mask_h = enc->mask_h;
         return SMH_OK;
     } catch (...) {
         return SMH_EHIP;
@@ -123,7 +163,8 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
                             double *t_blockwise_us) {
     smh_status s = check_select(st, B, H, d, dt);
     if (s != SMH_OK) return s;
-    select_kernel(*st, (int64_t)B * H, d, dt, t_rowwise_us, t_blockwise_us);
+    select_kernel(*st, heads_per_mask(st, B, H), d, dt, t_rowwise_us,
+                  t_blockwise_us);
     return SMH_OK;
 }
 
@@ -132,7 +173,7 @@ smh_status smh_select_kernel(const smh_mask_stats *st, int32_t B, int32_t H,
     if (!out) return SMH_EINVAL;
     smh_status s = check_select(st, B, H, d, dt);
     if (s != SMH_OK) return s;
-    *out = select_kernel(*st, (int64_t)B * H, d, dt, nullptr, nullptr);
+    *out = select_kernel(*st, heads_per_mask(st, B, H), d, dt, nullptr, nullptr);
     return SMH_OK;
 }
 
@@ -145,8 +186,8 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
     try {
         if (!enc) return SMH_EINVAL;
         if (B < 0 || H < 0 || S < 0 || S > SMH_MAX_S) return SMH_EINVAL;
-        if (S % SMH_OT) return SMH_EUNSUPPORTED;
-        if (enc->S != S || enc->n_ot != S / SMH_OT) return SMH_EINVAL;
+        if (enc->S != S || enc->n_ot != (S + SMH_OT - 1) / SMH_OT) return SMH_EINVAL;
+        if (stack_rows(enc->mask_b, enc->mask_h, S) < 0) return SMH_EINVAL;
         if (d != 64 && d != 128) return SMH_EUNSUPPORTED;
         if (in_dt != SMH_F16 && in_dt != SMH_BF16) return SMH_EUNSUPPORTED;
         if (out_dt != in_dt && out_dt != SMH_F32) return SMH_EUNSUPPORTED;
@@ -154,14 +195,17 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
         if (which != SMH_AUTO && which != SMH_ROWWISE && which != SMH_BLOCKWISE)
             return SMH_EINVAL;
         const int64_t BH = (int64_t)B * H;
+        if (BH > 0 && !broadcasts(enc->mask_b, enc->mask_h, B, H)) return SMH_EINVAL;
         // grid sizes: one workgroup per (head, outer-tile row) for the
         // block-wise kernel, one wavefront per (head, 8 query rows) for the
         // row-wise kernel
-        if (BH * (S / 8) > (int64_t)INT32_MAX) return SMH_EINVAL;
+        if (BH * 8 * enc->n_ot > (int64_t)INT32_MAX) return SMH_EINVAL;
         if (which == SMH_AUTO && st) {
             smh_status s2 = check_select(st, B, H, d, in_dt);
             if (s2 != SMH_OK) return s2;
-            if (st->S != S) return SMH_EINVAL;
+            if (st->S != S || st->mask_b != enc->mask_b ||
+                st->mask_h != enc->mask_h)
+                return SMH_EINVAL;
         }
         const size_t n_el = (size_t)BH * S * d;
         if (n_el == 0) return SMH_OK;  // nothing to compute
@@ -184,7 +228,8 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
             e = launch_auto(q, k, v, o, B, H, S, d, in_dt, out_dt, sc, *enc, hs);
         else {
             if (which == SMH_AUTO)
-                which = select_kernel(*st, BH, d, in_dt, nullptr, nullptr);
+                which = select_kernel(*st, heads_per_mask(st, B, H), d, in_dt,
+                                      nullptr, nullptr);
             if (which == SMH_ROWWISE)
                 e = launch_rowwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
                                    *enc, hs);

@@ -2,9 +2,9 @@
 // workgroups first evaluate the kernel-choice cost model on the statistics
 // the encoder wrote (the same function as smh_select_kernel) and then run
 // either algorithm.  Grid and workgroup shape are the block-wise kernel's
-// (one workgroup per (head, outer-tile row), 256 threads); under the
-// row-wise choice each of the 4 wavefronts takes inner-tile rows w and w+4
-// of that outer-tile row, independently and without barriers.
+// (one workgroup per (head, outer-tile row): slot_of), 256 threads; under
+// the row-wise choice each of the 4 wavefronts takes inner-tile rows w and
+// w+4 of that outer-tile row, independently and without barriers.
 #include "blockwise_body.h"
 #include "rowwise_body.h"
 
@@ -14,32 +14,31 @@ namespace {
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TOut> a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int oi = blockIdx.x / a.BH;
-    const int bh = blockIdx.x - oi * a.BH;
-    const int I = a.use_order ? a.row_order[oi] : oi;
+    const int oi = blockIdx.x / a.U;
+    const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
     if (device_choice<D>(a) == 2) {
-        blockwise_row<D, TIn, TOut>(a, smem, I, bh);
+        blockwise_row<D, TIn, TOut>(a, smem, sl.row, sl.I, sl.bh);
     } else {
         const int w = threadIdx.x >> 6;
         char *slice = smem + w * RowLds<D>::BYTES;
-        rowwise_group<D, TIn, TOut>(a, slice, I, w, bh);
-        rowwise_group<D, TIn, TOut>(a, slice, I, w + 4, bh);
+        rowwise_group<D, TIn, TOut>(a, slice, sl.row, sl.I, w, sl.bh);
+        rowwise_group<D, TIn, TOut>(a, slice, sl.row, sl.I, w + 4, sl.bh);
     }
 }
 
 template <int D, typename TIn, typename TOut>
 hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
-                    int BH, int S, float scale, const smh_mask_enc &enc,
+                    int B, int H, int S, float scale, const smh_mask_enc &enc,
                     hipStream_t stream) {
     static_assert(4 * RowLds<D>::BYTES <= Lds<D>::BYTES, "LDS slices");
     const int smem = Lds<D>::BYTES;
     auto kern = auto_fwd<D, TIn, TOut>;
     hipError_t e = ensure_lds_limit(kern, smem);
     if (e != hipSuccess) return e;
-    FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, BH, S, scale, enc);
-    a.use_order = (long long)enc.n_ot * BH > resident_workgroups(kern, smem);
-    hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)enc.n_ot * BH)), dim3(256),
-                       smem, stream, a);
+    FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, B, H, S, scale, enc);
+    const long long slots = (long long)a.R * a.U;  // = n * B * H
+    a.use_order = slots > resident_workgroups(kern, smem);
+    hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(256), smem, stream, a);
     return hipGetLastError();
 }
 
@@ -49,9 +48,8 @@ hipError_t launch_auto(const void *q, const void *k, const void *v, void *o,
                        int B, int H, int S, int d, int in_dt, int out_dt,
                        float scale, const smh_mask_enc &enc,
                        hipStream_t stream) {
-    const int BH = B * H;
 #define SMH_CASE(D_, TI, TO)                                                  \
-    return launch_d<D_, TI, TO>(q, k, v, o, BH, S, scale, enc, stream)
+    return launch_d<D_, TI, TO>(q, k, v, o, B, H, S, scale, enc, stream)
     if (d == 64) {
         if (in_dt == SMH_F16) {
             if (out_dt == SMH_F32) SMH_CASE(64, _Float16, float);

@@ -8,31 +8,25 @@ namespace {
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TIn, TOut> a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    // heavy rows first across all heads; one head's workgroups are BH apart
-    // in launch order, so with BH % 8 == 0 they all land on one XCD
-    const int oi = blockIdx.x / a.BH;
-    const int bh = blockIdx.x - oi * a.BH;
-    blockwise_row<D, TIn, TOut>(a, smem, a.use_order ? a.row_order[oi] : oi, bh);
-}
-
-template <int D, typename TIn, typename TOut>
-hipError_t launch_t(FwdArgs<TIn, TOut> a, int n, hipStream_t stream) {
-    const int smem = Lds<D>::BYTES;
-    auto kern = blockwise_fwd<D, TIn, TOut>;
-    hipError_t e = ensure_lds_limit(kern, smem);
-    if (e != hipSuccess) return e;
-    a.use_order = (long long)n * a.BH > resident_workgroups(kern, smem);
-    hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)n * a.BH)), dim3(256),
-                       smem, stream, a);
-    return hipGetLastError();
+    // heavy rows first across all heads (slot_of)
+    const int oi = blockIdx.x / a.U;
+    const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
+    blockwise_row<D, TIn, TOut>(a, smem, sl.row, sl.I, sl.bh);
 }
 
 template <int D, typename TIn, typename TOut>
 hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
-                    int BH, int S, float scale, const smh_mask_enc &enc,
+                    int B, int H, int S, float scale, const smh_mask_enc &enc,
                     hipStream_t stream) {
-    return launch_t<D, TIn, TOut>(
-        make_args<TIn, TOut>(q, k, v, o, BH, S, scale, enc), enc.n_ot, stream);
+    const int smem = Lds<D>::BYTES;
+    auto kern = blockwise_fwd<D, TIn, TOut>;
+    hipError_t e = ensure_lds_limit(kern, smem);
+    if (e != hipSuccess) return e;
+    FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, B, H, S, scale, enc);
+    const long long slots = (long long)a.R * a.U;  // = n * B * H
+    a.use_order = slots > resident_workgroups(kern, smem);
+    hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(256), smem, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -41,9 +35,8 @@ hipError_t launch_blockwise(const void *q, const void *k, const void *v,
                             void *o, int B, int H, int S, int d, int in_dt,
                             int out_dt, float scale, const smh_mask_enc &enc,
                             hipStream_t stream) {
-    const int BH = B * H;
 #define SMH_CASE(D_, TI, TO)                                                  \
-    return launch_d<D_, TI, TO>(q, k, v, o, BH, S, scale, enc, stream)
+    return launch_d<D_, TI, TO>(q, k, v, o, B, H, S, scale, enc, stream)
     if (d == 64) {
         if (in_dt == SMH_F16) {
             if (out_dt == SMH_F32) SMH_CASE(64, _Float16, float);

@@ -70,18 +70,21 @@ template <int D> struct VRegs {
 };
 
 // Global loads of K tile J (one contiguous block: thread t takes 16-byte
-// chunks t, t+256, ...) and, for a partial tile, this lane's mask bytes:
+// chunks t, t+256, ...; a chunk at element offset above `lim` is read from
+// `lim` instead, so that the rows of a tile cut by S come from inside K:
+// they are masked, and any finite value serves) and, for a partial tile,
+// this lane's mask bytes:
 // keys 16st + 4g + i of query row r are bits 4(g&1)+i of byte r&7 of inner
 // tile (r>>3, 2st + (g>>1)); b_off is that byte's offset for st = 0, each
 // further st is two words (16 bytes) on.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void fetch_k(
-    KRegs<D> &r, const TIn *__restrict__ Kh, int J,
+    KRegs<D> &r, const TIn *__restrict__ Kh, int J, int lim,
     const uint64_t *__restrict__ words, int b_off, int t) {
     const TIn *kt = Kh + (size_t)J * 64 * D;
 #pragma unroll
     for (int i = 0; i < KRegs<D>::N; ++i)
-        r.kr[i] = *reinterpret_cast<const u4_t *>(kt + (t + 256 * i) * 8);
+        r.kr[i] = *reinterpret_cast<const u4_t *>(kt + min((t + 256 * i) * 8, lim));
     if (words) {
         const uint8_t *wb = reinterpret_cast<const uint8_t *>(words) + b_off;
 #pragma unroll
@@ -106,14 +109,15 @@ template <int off> __device__ __attribute__((always_inline)) inline int bit_mask
     return r;
 }
 
-// Global loads of V tile J, the same contiguous chunks as K.
+// Global loads of V tile J, the same contiguous chunks and limit as K (a
+// masked key's V row is multiplied by a zero probability).
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void fetch_v(
-    VRegs<D> &r, const TIn *__restrict__ Vh, int J, int t) {
+    VRegs<D> &r, const TIn *__restrict__ Vh, int J, int lim, int t) {
     const TIn *vt = Vh + (size_t)J * 64 * D;
 #pragma unroll
     for (int i = 0; i < VRegs<D>::N; ++i)
-        r.vr[i] = *reinterpret_cast<const u4_t *>(vt + (t + 256 * i) * 8);
+        r.vr[i] = *reinterpret_cast<const u4_t *>(vt + min((t + 256 * i) * 8, lim));
 }
 
 // K tile row-major into a K buffer (padded rows).
@@ -271,23 +275,29 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
 
 // The stored tiles of one outer-tile row: full tiles first, then partial.
 // Columns are clamped to [0, n): an encoding that is not this library's
-// then gives wrong numbers, never an access outside K and V.
+// then gives wrong numbers, never an access outside K and V.  lim(J) is the
+// last in-bounds 8-element chunk offset of tile J (S cuts the last tile).
 struct TileList {
     const int32_t *fci, *pci;
     const uint64_t *bm;
-    int f0, nF, p0, nT, nmax;
+    int f0, nF, p0, nT, nmax, S;
     __device__ int col(int idx) const {
         const int J = idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
         return (int)min((unsigned)J, (unsigned)nmax);
+    }
+    template <int D> __device__ int lim(int J) const {
+        return min(64, S - 64 * J) * D - 8;
     }
     __device__ const uint64_t *words(int idx) const {
         return idx < nF ? nullptr : bm + (size_t)(p0 + idx - nF) * 64;
     }
 };
 
+// Workgroup work: encoding row `row` (outer-tile row I of its mask) of
+// head bh.
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void blockwise_row(
-    const FwdArgs<TIn, TOut> &a, char *smem, int I, int bh) {
+    const FwdArgs<TIn, TOut> &a, char *smem, int row, int I, int bh) {
     using frag = typename Frag<TIn>::type;
     using L = Lds<D>;
     const size_t head = (size_t)bh * a.S * D;
@@ -301,17 +311,20 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     tl.fci = a.fci;
     tl.pci = a.pci;
     tl.bm = a.bm;
-    tl.nmax = a.S / 64 - 1;
-    tl.f0 = a.frp[I];
-    tl.nF = a.frp[I + 1] - tl.f0;
-    tl.p0 = a.prp[I];
-    tl.nT = tl.nF + a.prp[I + 1] - tl.p0;
+    tl.nmax = a.n - 1;
+    tl.S = a.S;
+    tl.f0 = a.frp[row];
+    tl.nF = a.frp[row + 1] - tl.f0;
+    tl.p0 = a.prp[row];
+    tl.nT = tl.nF + a.prp[row + 1] - tl.p0;
     const int nT = tl.nT, nF = tl.nF;
 
     // this lane's Q rows as the B operand: query r, d = 32s + 8g + 0..7
+    // (a query past S, in a tile cut by S, reads query S-1 and is not stored)
+    const int qi = 64 * I + r;
     frag qf[D / 32];
     {
-        const TIn *qrow = Qh + (size_t)(64 * I + r) * D;
+        const TIn *qrow = Qh + (size_t)min(qi, a.S - 1) * D;
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
             qf[s] = *reinterpret_cast<const frag *>(qrow + 32 * s + 8 * g);
@@ -340,10 +353,19 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     VRegs<D> vr;
     f4_t s_a[4], s_b[4];
     uint32_t m_a = 0, m_b = 0;
+    // loads of stored tile idx: K (with its mask bytes) or V
+    auto load_k = [&](KRegs<D> &dst, int idx) __attribute__((always_inline)) {
+        const int J = tl.col(idx);
+        fetch_k<D, TIn>(dst, Kh, J, tl.lim<D>(J), tl.words(idx), b_off, t);
+    };
+    auto load_v = [&](int idx) __attribute__((always_inline)) {
+        const int J = tl.col(idx);
+        fetch_v<D, TIn>(vr, Vh, J, tl.lim<D>(J), t);
+    };
     if (nT > 0) {
-        fetch_k<D, TIn>(kr, Kh, tl.col(0), tl.words(0), b_off, t);
-        fetch_v<D, TIn>(vr, Vh, tl.col(0), t);
-        if (nT > 1) fetch_k<D, TIn>(kr1, Kh, tl.col(1), tl.words(1), b_off, t);
+        load_k(kr, 0);
+        load_v(0);
+        if (nT > 1) load_k(kr1, 1);
         stage_k<D, TIn>(kr, L::kbuf(smem, 0), t);
         if (nF == 0) m_a = mask_bits<D>(kr, nib);
         stage_v<D>(vr, L::vbuf(smem, 0), t);
@@ -351,8 +373,8 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
             stage_k<D, TIn>(kr1, L::kbuf(smem, 1), t);
             if (1 >= nF) m_b = mask_bits<D>(kr1, nib);
         }
-        if (nT > 2) fetch_k<D, TIn>(kr, Kh, tl.col(2), tl.words(2), b_off, t);
-        if (nT > 1) fetch_v<D, TIn>(vr, Vh, tl.col(1), t);
+        if (nT > 2) load_k(kr, 2);
+        if (nT > 1) load_v(1);
     }
     __syncthreads();
     if (nT > 0) qk_tile<D, TIn>(s_a, qf, L::kbuf(smem, 0), k_off, nF == 0, m_a);
@@ -375,9 +397,8 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
             if (it + 2 >= nF) m2 = mask_bits<D>(kr, nib);
         }
         if (it + 1 < nT) stage_v<D>(vr, L::vbuf(smem, nb), t);
-        if (it + 3 < nT)
-            fetch_k<D, TIn>(kr, Kh, tl.col(it + 3), tl.words(it + 3), b_off, t);
-        if (it + 2 < nT) fetch_v<D, TIn>(vr, Vh, tl.col(it + 2), t);
+        if (it + 3 < nT) load_k(kr, it + 3);
+        if (it + 2 < nT) load_v(it + 2);
         __syncthreads();
         mc = m2;
     };
@@ -401,10 +422,12 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     // epilogue: total l over the 4 lanes of this query
     const float lt = sum_xor32(sum_xor16(rs.l));
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    TOut *orow = a.O + head + (size_t)(64 * I + r) * D;
+    if (qi < a.S) {
+        TOut *orow = a.O + head + (size_t)qi * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-        store4<TOut>(orow + 16 * dt + 4 * g, rs.acc[dt] * inv);
+        for (int dt = 0; dt < D / 16; ++dt)
+            store4<TOut>(orow + 16 * dt + 4 * g, rs.acc[dt] * inv);
+    }
 }
 
 }  // namespace smh

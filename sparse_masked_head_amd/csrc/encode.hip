@@ -6,9 +6,10 @@
 // tiles are listed by column only; partial tiles are listed and carry one
 // uint64 bitmap per 8x8 inner tile.  Exact layout: include/smh.h.
 //
-// Work unit: a segment of one outer-tile row (seg_plan), numbered row by
-// row, left to right, so the encoding is the concatenation of the
-// segments' tile lists in that order.
+// Input: a stack of G masks [G][S][S]; the encoding has G * n outer-tile
+// rows (mask after mask).  Work unit: a segment of one outer-tile row
+// (seg_plan), numbered row by row, left to right, so the encoding is the
+// concatenation of the segments' tile lists in that order.
 //   strip pass (one workgroup per segment): stream the segment's 64-row
 //     strip, one window (64 rows x 512 bytes) at a time with the next
 //     window's loads in flight; build the inner-tile words of every tile in
@@ -19,8 +20,8 @@
 //     row pointers, statistics and the heavy-first row order;
 //   placement (one workgroup per segment): copy the segment's columns and
 //     words to their final places.
-// With at most kFusedMaxSegs segments the scan runs as one extra workgroup
-// of the placement launch and each placement workgroup adds up the counts
+// With at most kFusedMaxSegs segments and kFusedRows rows the scan runs as
+// one extra workgroup of the placement launch and each placement workgroup adds up the counts
 // before it itself (cheap at that size, and one launch fewer).  No
 // workgroup ever waits for another.  Every output is a pure function of
 // the mask: the result is deterministic and equals appending tiles row by
@@ -49,19 +50,42 @@ __device__ inline uint32_t row_bits8(uint32_t lo, uint32_t hi) {
 
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
+// How the strip pass reads a mask row: kAligned64 (S % 64 == 0: whole
+// 16-byte pieces, no bounds beyond the tile count), kAligned16 (S % 16 == 0:
+// whole pieces, rows and pieces past S read as zero), kBytes (rows are not
+// 16-byte aligned: byte loads, elements past S read as zero).
+enum LoadMode { kAligned64 = 0, kAligned16 = 1, kBytes = 2 };
+
 // Loads of one window: thread t reads, for k = 0..7, mask row 8k + (t >> 5)
-// of the strip, bytes 16*(t & 31) .. +15 of the window (tile (t & 31) >> 2,
-// columns 16*(t & 3) .. +15 of it).  Each wavefront instruction reads two
-// contiguous 512-byte row pieces.  Tiles at or past n read as zero.
+// of the strip (strip row 0 = mask row row0), bytes 16*(t & 31) .. +15 of
+// the window (tile (t & 31) >> 2, columns 16*(t & 3) .. +15 of it).  Each
+// wavefront instruction reads two contiguous 512-byte row pieces.  Tiles
+// at or past n, and elements outside the S x S mask, read as zero.
+template <int kMode>
 __device__ __forceinline__ void load_window(u4v (&v)[8], const uint8_t *strip,
-                                            int S, int n, int J0, int t) {
+                                            int S, int n, int row0, int J0, int t) {
     const int r0 = t >> 5, c = t & 31;
     const bool ok = J0 + (c >> 2) < n;
+    const int col = 64 * J0 + 16 * c;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-        v[k] = ok ? *reinterpret_cast<const u4v *>(
-                        strip + (size_t)(8 * k + r0) * S + 64 * J0 + 16 * c)
-                  : u4v{0, 0, 0, 0};
+    for (int k = 0; k < 8; ++k) {
+        const uint8_t *p = strip + (size_t)(8 * k + r0) * S + col;
+        const bool row_ok = row0 + 8 * k + r0 < S;
+        if (kMode == kAligned64) {
+            v[k] = ok ? *reinterpret_cast<const u4v *>(p) : u4v{0, 0, 0, 0};
+        } else if (kMode == kAligned16) {
+            v[k] = ok && row_ok && col < S ? *reinterpret_cast<const u4v *>(p)
+                                           : u4v{0, 0, 0, 0};
+        } else {
+            uint32_t wd[4] = {0, 0, 0, 0};
+            if (ok && row_ok) {
+#pragma unroll
+                for (int b = 0; b < 16; ++b)
+                    if (col + b < S) wd[b >> 2] |= (uint32_t)p[b] << (8 * (b & 3));
+            }
+            v[k] = u4v{wd[0], wd[1], wd[2], wd[3]};
+        }
+    }
 }
 
 template <typename T> __device__ inline T block_sum(T x, T *sh) {
@@ -84,7 +108,13 @@ __device__ inline int block_max(int x, int *sh) {
 
 
 constexpr int kMaxSegTiles = kWin * kMaxSegWin;  // 64
-constexpr int kMaxRows = SMH_MAX_S / 64;          // outer-tile rows
+constexpr int kMaxN = SMH_MAX_S / 64;              // outer tiles per side
+// Scan sizes: rows of the encoding it holds in LDS, and bins of its
+// stored-tile-count histogram (counts 0..n).  The fused form (scan as one
+// workgroup of the placement launch) is kept small because every placement
+// workgroup reserves its LDS.
+constexpr int kScanRows = SMH_MAX_ENC_ROWS, kScanBins = kMaxN + 1;
+constexpr int kFusedRows = 1024, kFusedBins = kFusedRows + 1;
 constexpr int kFusedMaxSegs = 2048;
 
 struct Seg {  // per-segment scratch (EncLayout)
@@ -94,8 +124,10 @@ struct Seg {  // per-segment scratch (EncLayout)
     int cap;  // tiles of room per segment
 };
 
+template <int kMode>
 __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mask,
                                                  int S, int n, SegPlan plan, Seg sg) {
+    // segment s: row s / per_row of the encoding = outer-tile row I of mask g
     // inner-tile words of the segment's tiles (tile l = 8 * window + j)
     __shared__ uint64_t lw[kMaxSegTiles][64];
     __shared__ int wsum[kMaxSegTiles][4];  // tile counts per wavefront
@@ -104,20 +136,22 @@ __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mas
 
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int s = blockIdx.x;
-    const int I = s / plan.per_row, seg_c = s % plan.per_row;
+    const int row = s / plan.per_row, seg_c = s - row * plan.per_row;
+    const int g = row / n, I = row - g * n;
     const int nw = (n + kWin - 1) / kWin;
     const int w0 = seg_c * plan.win;
     const int nwin = min(plan.win, nw - w0);  // windows in this segment
 
     {
-        const uint8_t *strip = mask + (size_t)64 * I * S;
+        const uint8_t *strip = mask + (size_t)g * S * S + (size_t)64 * I * S;
         uint8_t *wb = reinterpret_cast<uint8_t *>(&lw[0][0]);
         const int r0 = t >> 5, c = t & 31, jj = c >> 2, quarter = c & 3;
         uint32_t any_rows = 0;  // bit k: row 8k + r0 has a valid element
         u4v cur[8], nxt[8];
-        load_window(cur, strip, S, n, kWin * w0, t);
+        load_window<kMode>(cur, strip, S, n, 64 * I, kWin * w0, t);
         for (int wi = 0; wi < nwin; ++wi) {
-            if (wi + 1 < nwin) load_window(nxt, strip, S, n, kWin * (w0 + wi + 1), t);
+            if (wi + 1 < nwin)
+                load_window<kMode>(nxt, strip, S, n, 64 * I, kWin * (w0 + wi + 1), t);
             uint8_t *tb = wb + (size_t)(kWin * wi + jj) * 512;
             int cnt = 0;
 #pragma unroll
@@ -201,20 +235,31 @@ __device__ inline unsigned long long block_exclusive_scan(unsigned long long x,
 }
 
 // Exclusive scan of the segments' tile counts, row pointers, statistics and
-// the heavy-first schedule (one workgroup of 256 threads).  Writes each
-// segment's offsets when `offsets` is set.  Thread t owns a run of whole
-// rows; every load of the first pass is independent of the others, so the
-// pass costs one memory round trip.
-__device__ void scan_body(int n, SegPlan plan, Seg sg, smh_mask_enc enc,
-                          bool offsets) {
-    __shared__ int rowf[kMaxRows], rowp[kMaxRows];
+// the heavy-first schedule (one workgroup of 256 threads) over the R = G * n
+// rows of the encoding.  Writes each segment's offsets when `offsets` is
+// set.  Thread t owns a run of whole rows; every load of the first pass is
+// independent of the others, so the pass costs one memory round trip.
+// Schedule: row J's rank = rows with more stored tiles + rows before J with
+// as many; the first term from a histogram of the counts, the second from
+// a running histogram over blocks of 256 rows plus a count inside J's block.
+template <int kRows, int kBins>
+__device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
+                          smh_mask_enc enc, bool offsets) {
+    __shared__ uint32_t rowc[kRows];  // full << 16 | partial (each <= n <= 2048)
+    __shared__ int above[kBins];      // histogram, then rows with a larger count
+    __shared__ int seen[kBins];       // rows of earlier blocks per count
     __shared__ unsigned long long sh_u[4];
     __shared__ long long sh_l[4];
     __shared__ int sh_i[4];
     const int t = threadIdx.x;
     const int C = plan.per_row;
-    const int rows_per = (n + 255) / 256;
-    const int r_lo = min(n, t * rows_per), r_hi = min(n, r_lo + rows_per);
+    for (int c = t; c <= n; c += 256) {
+        above[c] = 0;
+        seen[c] = 0;
+    }
+    __syncthreads();
+    const int rows_per = (R + 255) / 256;
+    const int r_lo = min(R, t * rows_per), r_hi = min(R, r_lo + rows_per);
     unsigned long long own = 0;
     long long nnz = 0, empty = 0;
     int mx = 0;
@@ -228,8 +273,8 @@ __device__ void scan_body(int n, SegPlan plan, Seg sg, smh_mask_enc enc,
             an |= sg.any[I * C + c];
         }
         const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull);
-        rowf[I] = f;
-        rowp[I] = p;
+        rowc[I] = ((uint32_t)f << 16) | (uint32_t)p;
+        atomicAdd(&above[f + p], 1);
         mx = max(mx, f + p);
         empty += 64 - __popcll(an);
         own += rc;
@@ -245,37 +290,55 @@ __device__ void scan_body(int n, SegPlan plan, Seg sg, smh_mask_enc enc,
                 r2 += sg.cnt[I * C + c];
             }
         }
-        run += ((unsigned long long)rowf[I] << 32) | (unsigned long long)rowp[I];
+        run += ((unsigned long long)(rowc[I] >> 16) << 32) |
+               (unsigned long long)(rowc[I] & 0xFFFFu);
     }
     if (t == 255) {  // the last thread ends at the total
-        enc.full_row_ptr[n] = (int32_t)(run >> 32);
-        enc.part_row_ptr[n] = (int32_t)(run & 0xFFFFFFFFull);
+        enc.full_row_ptr[R] = (int32_t)(run >> 32);
+        enc.part_row_ptr[R] = (int32_t)(run & 0xFFFFFFFFull);
         enc.stats[1] = (int64_t)(run >> 32);
         enc.stats[2] = (int64_t)(run & 0xFFFFFFFFull);
     }
     nnz = block_sum(nnz, sh_l);
     empty = block_sum(empty, sh_l);
     mx = block_max(mx, sh_i);
-    // heavy-first schedule: rank = number of rows that sort before row J
-    for (int J = t; J < n; J += 256) {
-        const int cj = rowf[J] + rowp[J];
-        int rank = 0;
-        for (int J2 = 0; J2 < n; ++J2) {
-            const int c2 = rowf[J2] + rowp[J2];
-            rank += (c2 > cj) || (c2 == cj && J2 < J);
+    {   // histogram -> rows with a larger count: R - (rows with count <= c)
+        const int per = (n + 1 + 255) / 256;
+        const int c_lo = min(n + 1, t * per), c_hi = min(n + 1, c_lo + per);
+        unsigned long long h = 0;
+        for (int c = c_lo; c < c_hi; ++c) h += (unsigned long long)above[c];
+        unsigned long long below = block_exclusive_scan(h, sh_u);
+        for (int c = c_lo; c < c_hi; ++c) {
+            below += (unsigned long long)above[c];
+            above[c] = R - (int)below;
         }
-        enc.row_order[rank] = J;
+    }
+    __syncthreads();
+    for (int k0 = 0; k0 < R; k0 += 256) {
+        const int J = k0 + t;
+        const int cj = J < R ? (int)((rowc[J] >> 16) + (rowc[J] & 0xFFFFu)) : 0;
+        if (J < R) {
+            int ties = 0;
+            for (int J2 = k0; J2 < J; ++J2)
+                ties += (int)((rowc[J2] >> 16) + (rowc[J2] & 0xFFFFu)) == cj;
+            enc.row_order[above[cj] + seen[cj] + ties] = J;
+        }
+        __syncthreads();  // every rank of this block read seen[]
+        if (J < R) atomicAdd(&seen[cj], 1);
+        __syncthreads();
     }
     if (t == 0) {
         enc.stats[0] = nnz;
-        enc.stats[3] = empty;
+        // rows past S do not exist
+        enc.stats[3] = empty - (long long)G * (64LL * n - S);
         enc.stats[4] = mx;
     }
 }
 
-__global__ __launch_bounds__(256) void enc_scan(int n, SegPlan plan, Seg sg,
+__global__ __launch_bounds__(256) void enc_scan(int S, int n, int R, int G,
+                                                SegPlan plan, Seg sg,
                                                 smh_mask_enc enc) {
-    scan_body(n, plan, sg, enc, true);
+    scan_body<kScanRows, kScanBins>(S, n, R, G, plan, sg, enc, true);
 }
 
 // Placement of segment blockIdx.x.  kSelf: the workgroup adds up the tile
@@ -284,13 +347,16 @@ __global__ __launch_bounds__(256) void enc_scan(int n, SegPlan plan, Seg sg,
 // first words are loaded together with its offsets (they do not depend on
 // them), so a small segment is placed after one memory round trip.
 template <bool kSelf>
-__global__ __launch_bounds__(256) void enc_place(int n, SegPlan plan, Seg sg,
+__global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
+                                                 SegPlan plan, Seg sg,
                                                  smh_mask_enc enc) {
     __shared__ unsigned long long sh_u[4];
     const int t = threadIdx.x, s = blockIdx.x;
-    if (kSelf && s == plan.total) {
-        scan_body(n, plan, sg, enc, false);
-        return;
+    if constexpr (kSelf) {
+        if (s == plan.total) {
+            scan_body<kFusedRows, kFusedBins>(S, n, R, G, plan, sg, enc, false);
+            return;
+        }
     }
     const size_t base = (size_t)s * sg.cap;
     const uint64_t cnt = sg.cnt[s];
@@ -334,9 +400,11 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
         hipLaunchKernelGGL(enc_empty, dim3(1), dim3(64), 0, stream, enc);
         return hipGetLastError();
     }
-    const int n = (int)L.n;
+    const int n = (int)L.n, R = (int)L.rows;
+    const int G = enc.mask_b * enc.mask_h;
     const SegPlan plan = L.plan;
-    if (plan.total <= 0 || plan.win > kMaxSegWin || n > kMaxRows)
+    if (plan.total <= 0 || plan.win > kMaxSegWin || n > kMaxN || R > kScanRows ||
+        (int64_t)G * n != L.rows)
         return hipErrorInvalidValue;
     Seg sg;
     sg.cnt = (uint64_t *)(ws + L.seg_cnt);
@@ -347,16 +415,23 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
     sg.pcol = (int32_t *)(ws + L.seg_pcol);
     sg.words = (uint64_t *)(ws + L.seg_words);
     sg.cap = (int)L.seg_cap;
-    hipLaunchKernelGGL(enc_strip, dim3(plan.total), dim3(256), 0, stream, mask,
-                       S, n, plan, sg);
-    if (plan.total <= kFusedMaxSegs) {
+    if (S % 64 == 0)
+        hipLaunchKernelGGL(enc_strip<kAligned64>, dim3(plan.total), dim3(256), 0,
+                           stream, mask, S, n, plan, sg);
+    else if (S % 16 == 0)
+        hipLaunchKernelGGL(enc_strip<kAligned16>, dim3(plan.total), dim3(256), 0,
+                           stream, mask, S, n, plan, sg);
+    else
+        hipLaunchKernelGGL(enc_strip<kBytes>, dim3(plan.total), dim3(256), 0,
+                           stream, mask, S, n, plan, sg);
+    if (plan.total <= kFusedMaxSegs && R <= kFusedRows) {
         hipLaunchKernelGGL(enc_place<true>, dim3(plan.total + 1), dim3(256), 0,
-                           stream, n, plan, sg, enc);
+                           stream, S, n, R, G, plan, sg, enc);
     } else {
-        hipLaunchKernelGGL(enc_scan, dim3(1), dim3(256), 0, stream, n, plan, sg,
-                           enc);
+        hipLaunchKernelGGL(enc_scan, dim3(1), dim3(256), 0, stream, S, n, R, G,
+                           plan, sg, enc);
         hipLaunchKernelGGL(enc_place<false>, dim3(plan.total), dim3(256), 0,
-                           stream, n, plan, sg, enc);
+                           stream, S, n, R, G, plan, sg, enc);
     }
     return hipGetLastError();
 }

@@ -19,14 +19,18 @@ typedef __attribute__((address_space(3))) s4_t lds_s4_t;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Everything an attention kernel reads: the tensors of one call and the
-// encoding of its mask.  c = scale * log2(e) (scores are exponentiated in
-// base 2).
+// encoding of its mask stack.  c = scale * log2(e) (scores are
+// exponentiated in base 2).
 template <typename TIn, typename TOut> struct FwdArgs {
     const TIn *Q, *K, *V;
     TOut *O;
-    int S, BH;
+    int S, BH, H;
+    int n;       // outer tiles per side, ceil(S / 64)
+    int R;       // rows of the encoding: masks * n
+    int U;       // (batch, head) pairs per mask: BH / masks
+    int mask_b, mask_h;
     float c;
-    // 1: visit outer-tile rows in row_order (heavy first); 0: in index
+    // 1: visit the encoding's rows in row_order (heavy first); 0: in index
     // order, used when every workgroup of the launch is resident at once
     // and the order cannot matter (saves a dependent load per workgroup)
     int use_order;
@@ -38,15 +42,22 @@ template <typename TIn, typename TOut> struct FwdArgs {
 
 template <typename TIn, typename TOut>
 inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
-                                    const void *v, void *o, int BH, int S,
-                                    float scale, const smh_mask_enc &enc) {
+                                    const void *v, void *o, int B, int H,
+                                    int S, float scale,
+                                    const smh_mask_enc &enc) {
     FwdArgs<TIn, TOut> a;
     a.Q = (const TIn *)q;
     a.K = (const TIn *)k;
     a.V = (const TIn *)v;
     a.O = (TOut *)o;
     a.S = S;
-    a.BH = BH;
+    a.BH = B * H;
+    a.H = H;
+    a.n = enc.n_ot;
+    a.mask_b = enc.mask_b;
+    a.mask_h = enc.mask_h;
+    a.R = enc.mask_b * enc.mask_h * enc.n_ot;
+    a.U = (enc.mask_b > 1 ? 1 : B) * (enc.mask_h > 1 ? 1 : H);
     a.c = scale * kLog2e;
     a.use_order = 1;
     a.frp = enc.full_row_ptr;
@@ -57,6 +68,31 @@ inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
     a.row_order = enc.row_order;
     a.stats = enc.stats;
     return a;
+}
+
+// What one launch slot works on.  Slots are (encoding row, user) pairs,
+// slot = oi * U + user: oi walks the encoding's rows (heavy first when
+// use_order), user walks the U (batch, head) pairs that share the row's
+// mask.  A head's slots are U apart, so with U % 8 == 0 they all land on
+// one XCD (slots go round-robin over the 8 XCDs).
+struct Slot {
+    int row;  // row of the encoding: mask g, outer-tile row I
+    int I;    // outer-tile row inside the mask
+    int bh;   // b * H + h
+};
+template <typename TIn, typename TOut>
+__device__ inline Slot slot_of(const FwdArgs<TIn, TOut> &a, int oi, int user) {
+    Slot sl;
+    sl.row = a.use_order ? a.row_order[oi] : oi;
+    const int g = sl.row / a.n;
+    sl.I = sl.row - g * a.n;
+    // mask g = gb * mask_h + gh; users of g: b in {gb} or all B, h in {gh}
+    // or all H (a broadcast side of size 1 spans every index)
+    const int Hu = a.mask_h > 1 ? 1 : a.H;
+    const int b = a.mask_b > 1 ? g / a.mask_h : user / Hu;
+    const int h = a.mask_h > 1 ? g - (g / a.mask_h) * a.mask_h : user - (user / Hu) * Hu;
+    sl.bh = b * a.H + h;
+    return sl;
 }
 
 template <typename T> constexpr int is_bf16() { return __is_same(T, __bf16) ? 1 : 0; }
@@ -221,7 +257,7 @@ inline long long resident_workgroups(Kernel kern, int lds) {
 // 2 block-wise (same function as smh_select_kernel on the host).
 template <int D, typename TIn, typename TOut>
 __device__ inline int device_choice(const FwdArgs<TIn, TOut> &a) {
-    return select_on_device(a.stats, a.BH, a.S / 64, D, is_bf16<TIn>());
+    return select_on_device(a.stats, a.U, a.R, D, is_bf16<TIn>());
 }
 
 }  // namespace smh

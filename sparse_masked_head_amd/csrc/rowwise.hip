@@ -13,23 +13,25 @@ __global__ __launch_bounds__(256) void rowwise_fwd(FwdArgs<TIn, TOut> a,
     const int w = threadIdx.x >> 6;
     const long long gw = (long long)blockIdx.x * 4 + w;
     if (gw >= n_groups) return;  // the whole wavefront leaves; no barriers
-    // heavy outer-tile rows first, then head, then inner-tile row
-    const long long per_oi = (long long)a.BH * 8;
+    // heavy encoding rows first, then the row's heads (slot_of), then
+    // inner-tile row
+    const long long per_oi = (long long)a.U * 8;
     const int oi = (int)(gw / per_oi);
     const int rem = (int)(gw - (long long)oi * per_oi);
-    rowwise_group<D, TIn, TOut>(a, lds + w * RowLds<D>::BYTES,
-                                a.row_order[oi], rem & 7, rem >> 3);
+    const Slot sl = slot_of(a, oi, rem >> 3);
+    rowwise_group<D, TIn, TOut>(a, lds + w * RowLds<D>::BYTES, sl.row, sl.I,
+                                rem & 7, sl.bh);
 }
 
 template <int D, typename TIn, typename TOut>
 hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
-                    int BH, int S, float scale, const smh_mask_enc &enc,
+                    int B, int H, int S, float scale, const smh_mask_enc &enc,
                     hipStream_t stream) {
-    const long long n_groups = (long long)BH * (S / 8);
+    FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, B, H, S, scale, enc);
+    const long long n_groups = (long long)a.R * a.U * 8;  // = 8 n B H
     hipLaunchKernelGGL((rowwise_fwd<D, TIn, TOut>),
                        dim3((unsigned)((n_groups + 3) / 4)), dim3(256), 0,
-                       stream, make_args<TIn, TOut>(q, k, v, o, BH, S, scale, enc),
-                       n_groups);
+                       stream, a, n_groups);
     return hipGetLastError();
 }
 
@@ -39,9 +41,8 @@ hipError_t launch_rowwise(const void *q, const void *k, const void *v,
                           void *o, int B, int H, int S, int d, int in_dt,
                           int out_dt, float scale, const smh_mask_enc &enc,
                           hipStream_t stream) {
-    const int BH = B * H;
 #define SMH_CASE(D_, TI, TO)                                                  \
-    return launch_d<D_, TI, TO>(q, k, v, o, BH, S, scale, enc, stream)
+    return launch_d<D_, TI, TO>(q, k, v, o, B, H, S, scale, enc, stream)
     if (d == 64) {
         if (in_dt == SMH_F16) {
             if (out_dt == SMH_F32) SMH_CASE(64, _Float16, float);

@@ -181,9 +181,12 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
     }
 }
 
+// Wavefront work: inner-tile row ir of encoding row `row` (outer-tile row I
+// of its mask) of head bh.  Query rows past S (S cuts the last outer tile)
+// see no key, read zeros for Q and are not stored.
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void rowwise_group(
-    const FwdArgs<TIn, TOut> &a, char *slice, int I, int ir, int bh) {
+    const FwdArgs<TIn, TOut> &a, char *slice, int row, int I, int ir, int bh) {
     constexpr int R = kRowsPerWave;
     constexpr int E = RwState<D>::E;
     constexpr int CAP = RowLds<D>::CAP;
@@ -194,16 +197,17 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
     const int row0 = 64 * I + 8 * ir;
     const size_t head_off = (size_t)bh * a.S * D;
     const TIn *Kh = a.K + head_off, *Vh = a.V + head_off;
-    const int nmax = a.S / 64 - 1;
+    const int nmax = a.n - 1;
 
     {  // stage the 8 query rows (contiguous) into the slice
         const u4_t *src = reinterpret_cast<const u4_t *>(a.Q + head_off + (size_t)row0 * D);
         u4_t *dst = reinterpret_cast<u4_t *>(qbuf);
-        for (int e = lane; e < R * D / 8; e += 64) dst[e] = src[e];
+        for (int e = lane; e < R * D / 8; e += 64)
+            dst[e] = row0 + e / (D / 8) < a.S ? src[e] : u4_t{0, 0, 0, 0};
     }
 
-    const int f0 = a.frp[I], nF = a.frp[I + 1] - f0;
-    const int p0 = a.prp[I], nP = a.prp[I + 1] - p0;
+    const int f0 = a.frp[row], nF = a.frp[row + 1] - f0;
+    const int p0 = a.prp[row], nP = a.prp[row + 1] - p0;
     const int nT = nF + nP;
 
     RwState<D> st;
@@ -276,8 +280,10 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
         const float lt = wave_sum(st.lp[r]);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         TOut *orow = a.O + head_off + (size_t)(row0 + r) * D + lane * E;
+        if (row0 + r < a.S) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) store1<TOut>(orow + e, st.o[r][e] * inv);
+            for (int e = 0; e < E; ++e) store1<TOut>(orow + e, st.o[r][e] * inv);
+        }
     }
     wave_lds_sync();  // the slice may be reused by the next group
 }

@@ -4,15 +4,15 @@
 
 namespace smh {
 
-smh_kernel select_kernel(const smh_mask_stats &st, int64_t BH, int d,
+smh_kernel select_kernel(const smh_mask_stats &st, int64_t heads, int d,
                          int dtype, double *t_row_us, double *t_blk_us) {
     SelectInput in;
     in.nnz = st.nnz;
     in.n_full = st.n_full;
     in.n_partial = st.n_partial;
     in.max_row_tiles = st.max_row_tiles;
-    in.BH = BH;
-    in.n_ot = st.S / 64;
+    in.heads = heads;
+    in.rows = (int64_t)st.mask_b * st.mask_h * ((st.S + 63) / 64);
     in.d = d;
     in.bf16 = dtype == SMH_BF16;
     double tr, tb;

@@ -19,12 +19,12 @@
 //       T_row = c0 + max(heads * (tiles * t_gather + 8 * chunks * t_chunk),
 //                        max_row_tiles / 8 * t_gather_serial
 //                        + (live_max / 64 + 1) * t_chunk_serial),
-//     chunks = live / 64 + n_ot summed over the groups of one inner-tile
+//     chunks = live / 64 + rows summed over the groups of one inner-tile
 //     row index (each group pays at least one chunk).
 // Sparsity enters through the tile counts and the expected number of live
 // keys per (tile, 8-row group) of a partial tile (from the partial tiles'
 // mean density, rho: 64 (1 - (1 - rho)^8)); sequence length through the
-// tile counts, n_ot and the serial terms.  The coefficients are
+// tile counts, the row count and the serial terms.  The coefficients are
 // microseconds, fitted (sparse_masked_head_amd/calibrate.py) to a sweep of
 // both kernels on MI355X over mask families, S, heads and d.
 //
@@ -41,9 +41,11 @@
 
 namespace smh {
 
+// Statistics are totals over the masks of the stack; heads = (batch, head)
+// pairs per mask; rows = outer-tile rows of the encoding (masks * n_ot).
 struct SelectInput {
     int64_t nnz, n_full, n_partial, max_row_tiles;
-    int64_t BH, n_ot;
+    int64_t heads, rows;
     int d, bf16;
 };
 
@@ -68,7 +70,7 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                              4.0450e-4, 5.4630e-3, 0.48558, 7.7900};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
-    const double heads = (double)in.BH;
+    const double heads = (double)in.heads;
     const double w_blk =
         heads * (tiles * k.blk_tile_us + (double)in.n_partial * k.blk_part_us);
     const double crit_blk = (double)in.max_row_tiles * k.blk_serial_us;
@@ -84,7 +86,7 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
         miss = miss * miss;
         live += (double)in.n_partial * 64.0 * (1.0 - miss);
     }
-    const double chunks = live / 64.0 + (double)in.n_ot;
+    const double chunks = live / 64.0 + (double)in.rows;
     const double w_row =
         heads * (tiles * k.row_gather_us + 8.0 * chunks * k.row_chunk_us);
     const double live_max =
@@ -103,15 +105,15 @@ SMH_HD inline int select_model(const SelectInput &in) {
 #pragma clang fp contract(on)
 
 // Device side: read the statistics the encoder wrote and decide.
-__device__ inline int select_on_device(const int64_t *stats, int64_t BH,
-                                       int64_t n_ot, int d, int bf16) {
+__device__ inline int select_on_device(const int64_t *stats, int64_t heads,
+                                       int64_t rows, int d, int bf16) {
     SelectInput in;
     in.nnz = stats[0];
     in.n_full = stats[1];
     in.n_partial = stats[2];
     in.max_row_tiles = stats[4];
-    in.BH = BH;
-    in.n_ot = n_ot;
+    in.heads = heads;
+    in.rows = rows;
     in.d = d;
     in.bf16 = bf16;
     return select_model(in);

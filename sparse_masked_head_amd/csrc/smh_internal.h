@@ -11,34 +11,37 @@
 namespace smh {
 
 // The encoder's unit of work: a segment = up to kMaxSegWin windows of kWin
-// outer tiles of one outer-tile row.  Each row is cut into `per_row`
-// segments of `win` windows (the last one possibly shorter), enough
-// segments in all to keep the chip busy; `total` = n * per_row.  Segments
-// are numbered row by row, left to right.
+// outer tiles of one outer-tile row.  Each of the `rows` rows (G masks of
+// n outer-tile rows each, mask after mask) is cut into `per_row` segments
+// of `win` windows (the last one possibly shorter), enough segments in all
+// to keep the chip busy; `total` = rows * per_row.  Segments are numbered
+// row by row, left to right.
 constexpr int kWin = 8;         // outer tiles per window (512 mask columns)
 constexpr int kMaxSegWin = 8;   // windows per segment
 struct SegPlan {
     int per_row, win, total;
 };
-inline SegPlan seg_plan(int n) {
+inline SegPlan seg_plan(int rows, int n) {
     SegPlan p{0, 0, 0};
-    if (n <= 0) return p;
+    if (rows <= 0 || n <= 0) return p;
     const int nw = (n + kWin - 1) / kWin;  // windows per row
-    int c = (1024 + n - 1) / n;           // aim at >= 1024 segments
+    int c = (1024 + rows - 1) / rows;      // aim at >= 1024 segments
     c = c < nw ? c : nw;
     const int cmin = (nw + kMaxSegWin - 1) / kMaxSegWin;
     c = c > cmin ? c : cmin;
     p.win = (nw + c - 1) / c;
     p.per_row = (nw + p.win - 1) / p.win;
-    p.total = n * p.per_row;
+    p.total = rows * p.per_row;
     return p;
 }
 
-// Byte offsets of every array inside the encode workspace.  Each array
-// starts on a 256-byte boundary: the encoding proper, then per-segment
-// scratch written by the strip pass and read by the placement pass.
+// Byte offsets of every array inside the encode workspace of G masks of
+// S x S.  Each array starts on a 256-byte boundary: the encoding proper
+// (rows = G * n outer-tile rows), then per-segment scratch written by the
+// strip pass and read by the placement pass.
 struct EncLayout {
-    int64_t n;  // outer tiles per side
+    int64_t n;     // outer tiles per side of one mask
+    int64_t rows;  // outer-tile rows of the stack (G * n)
     SegPlan plan;
     size_t full_row_ptr, part_row_ptr, full_col_idx, part_col_idx,
         part_bitmaps, stats, row_order;
@@ -53,10 +56,12 @@ struct EncLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline EncLayout enc_layout(int32_t S) {
+// Caller guarantees 0 <= S <= SMH_MAX_S, G >= 1 and G * n <= SMH_MAX_ENC_ROWS.
+inline EncLayout enc_layout(int32_t S, int64_t G) {
     EncLayout L{};
-    const int64_t n = S / 64;
-    const size_t n2 = size_t(n) * size_t(n);
+    const int64_t n = ((int64_t)S + 63) / 64;  // ragged S: the last tiles are cut
+    const int64_t rows = G * n;
+    const size_t cap = size_t(rows) * size_t(n);  // tiles of the stack
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -64,14 +69,15 @@ inline EncLayout enc_layout(int32_t S) {
         return at;
     };
     L.n = n;
-    L.plan = seg_plan((int)n);
-    L.full_row_ptr = take(sizeof(int32_t) * (n + 1));
-    L.part_row_ptr = take(sizeof(int32_t) * (n + 1));
-    L.full_col_idx = take(sizeof(int32_t) * n2);
-    L.part_col_idx = take(sizeof(int32_t) * n2);
-    L.part_bitmaps = take(sizeof(uint64_t) * 64 * n2);
+    L.rows = rows;
+    L.plan = seg_plan((int)rows, (int)n);
+    L.full_row_ptr = take(sizeof(int32_t) * (rows + 1));
+    L.part_row_ptr = take(sizeof(int32_t) * (rows + 1));
+    L.full_col_idx = take(sizeof(int32_t) * cap);
+    L.part_col_idx = take(sizeof(int32_t) * cap);
+    L.part_bitmaps = take(sizeof(uint64_t) * 64 * cap);
     L.stats = take(sizeof(int64_t) * 8);  // nnz, n_full, n_partial, empty rows, max row tiles
-    L.row_order = take(sizeof(int32_t) * n);
+    L.row_order = take(sizeof(int32_t) * rows);
     const size_t T = (size_t)L.plan.total;
     L.seg_cap = (size_t)L.plan.win * kWin;
     L.seg_cnt = take(sizeof(uint64_t) * T);
@@ -85,8 +91,8 @@ inline EncLayout enc_layout(int32_t S) {
     return L;
 }
 
-// Encoder: two or three launches on `stream` (strip pass, [scan,]
-// placement).
+// Encoder of a stack of G = enc.mask_b * enc.mask_h masks [G][S][S]: two or
+// three launches on `stream` (strip pass, [scan,] placement).
 hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
                          const EncLayout &L, const smh_mask_enc &enc,
                          hipStream_t stream);
@@ -110,8 +116,9 @@ hipError_t launch_auto(const void *q, const void *k, const void *v, void *o,
                        float scale, const smh_mask_enc &enc,
                        hipStream_t stream);
 
-// Cost model of the selector (host only).
-smh_kernel select_kernel(const smh_mask_stats &st, int64_t BH, int d,
+// Cost model of the selector (host only).  heads = (batch, head) pairs per
+// mask of the stack.
+smh_kernel select_kernel(const smh_mask_stats &st, int64_t heads, int d,
                          int dtype, double *t_row_us, double *t_blk_us);
 
 }  // namespace smh

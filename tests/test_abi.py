@@ -36,13 +36,18 @@ def test_status_strings_and_version():
 
 def test_workspace_bytes():
     f = L.lib().smh_encode_workspace_bytes
-    assert f(-64) == 0 and f(65) == 0 and f(L.SMH_MAX_S + 64) == 0
-    assert f(0) > 0
+    assert f(-64) == 0 and f(L.SMH_MAX_S + 64) == 0
+    assert f(0) > 0 and f(65) >= f(128) > f(64)    # ragged S rounds up
     small, big = f(64), f(16384)
     assert 0 < small < big
     n = 16384 // 64
     # encoding + scratch: at least two bitmap areas of n^2 * 512 bytes
     assert big >= 2 * n * n * 512
+    g = L.lib().smh_encode_masks_workspace_bytes
+    assert g(1, 1, 512) == f(512)
+    assert g(2, 3, 512) >= 6 * 8 * 8 * 512 * 2 > f(512)
+    assert g(0, 1, 64) == 0 and g(1, -1, 64) == 0
+    assert g(32, 32, 512) > 0 and g(32, 33, 512) == 0   # 8192 rows at most
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # never dereferenced: validation fails first
@@ -54,9 +59,15 @@ def encode(mask, S, ws, nbytes, enc=True):
                                    ctypes.byref(e) if enc else None, None)
 
 
+def encode_stack(masks, mb, mh, S, ws, nbytes):
+    e = L.MaskEnc()
+    return L.lib().smh_encode_masks(masks, mb, mh, S, ws, nbytes,
+                                    ctypes.byref(e), None)
+
+
 def test_encode_validation():
     f = L.lib().smh_encode_workspace_bytes
-    assert encode(FAKE, 100, FAKE, 1 << 30) == L.SMH_EUNSUPPORTED
+    g = L.lib().smh_encode_masks_workspace_bytes
     assert encode(FAKE, -64, FAKE, 1 << 30) == L.SMH_EINVAL
     assert encode(FAKE, L.SMH_MAX_S + 64, FAKE, 1 << 40) == L.SMH_EINVAL
     assert encode(FAKE, 128, FAKE, f(128), enc=False) == L.SMH_EINVAL
@@ -71,12 +82,21 @@ def test_encode_validation():
     ws = 1 << 24
     assert encode(ctypes.c_void_p(ws + 4096), 128, ctypes.c_void_p(ws),
                   f(128)) == L.SMH_EINVAL
+    # stacks
+    assert encode_stack(FAKE, 0, 1, 128, FAKE, 1 << 30) == L.SMH_EINVAL
+    assert encode_stack(FAKE, 1, 8193, 64, FAKE, 1 << 40) == L.SMH_EINVAL
+    assert encode_stack(FAKE, 2, 3, 128, FAKE, g(2, 3, 128) - 1) \
+        == L.SMH_ENOSPACE
+    assert encode_stack(FAKE, 2, 3, 128, FAKE, f(128)) == L.SMH_ENOSPACE
+    # the last mask of the stack reaches into the workspace
+    assert encode_stack(ctypes.c_void_p(ws - 6 * 128 * 128 + 16), 2, 3, 128,
+                        ctypes.c_void_p(ws), g(2, 3, 128)) == L.SMH_EINVAL
 
 
 def stats(**kw):
     s = L.MaskStats()
     base = dict(nnz=61888, S=512, n_full=8, n_partial=14, n_empty_rows=0,
-                max_row_tiles=3)
+                max_row_tiles=3, mask_b=1, mask_h=1)
     base.update(kw)
     for k, v in base.items():
         setattr(s, k, v)
@@ -97,8 +117,14 @@ def test_select_validation_and_choice():
     assert select(stats(), d=96)[0] == L.SMH_EUNSUPPORTED
     assert select(stats(), dt=L.SMH_F32)[0] == L.SMH_EUNSUPPORTED
     assert select(stats(), B=-1)[0] == L.SMH_EINVAL
-    assert select(stats(S=500))[0] == L.SMH_EUNSUPPORTED
+    assert select(stats(S=500))[0] == L.SMH_OK                # ragged S
     assert select(stats(n_full=100))[0] == L.SMH_EINVAL       # > n_ot^2
+    assert select(stats(mask_b=0))[0] == L.SMH_EINVAL
+    assert select(stats(mask_b=8))[0] == L.SMH_OK             # B = 8
+    assert select(stats(mask_b=8, n_full=100))[0] == L.SMH_OK
+    assert select(stats(mask_b=4))[0] == L.SMH_EINVAL         # B = 8
+    assert select(stats(mask_h=12, mask_b=8))[0] == L.SMH_OK
+    assert select(stats(mask_h=5))[0] == L.SMH_EINVAL
     assert select(stats(nnz=512 * 512 + 1))[0] == L.SMH_EINVAL
     assert select(stats(max_row_tiles=9))[0] == L.SMH_EINVAL
     a, b = ctypes.c_double(), ctypes.c_double()
@@ -121,13 +147,19 @@ def test_select_cost_model_monotone():
     assert r2 >= r1 and b2 >= b1
     r3, b3 = costs(stats(), d=128)
     assert r3 >= r1 and b3 >= b1
+    # 12 per-head copies of the mask (totals x 12) cost what one shared
+    # mask costs: the same work
+    r4, b4 = costs(stats(mask_h=12, nnz=12 * 61888, n_full=96,
+                         n_partial=168))
+    assert r4 == pytest.approx(r1, rel=1e-12)
+    assert b4 == pytest.approx(b1, rel=1e-12)
 
 
 def fwd(q=FAKE, k=FAKE, v=FAKE, o=ctypes.c_void_p(1 << 30), B=1, H=1, S=128,
         d=64, in_dt=L.SMH_F16, out_dt=L.SMH_F16, scale=0.0, enc="ok",
-        which=L.SMH_BLOCKWISE, st=None):
+        which=L.SMH_BLOCKWISE, st=None, mb=1, mh=1, enc_S=128):
     e = L.MaskEnc()
-    e.S, e.n_ot = 128, 2
+    e.S, e.n_ot, e.mask_b, e.mask_h = enc_S, -(-enc_S // 64), mb, mh
     for name in ("full_row_ptr", "full_col_idx", "part_row_ptr",
                  "part_col_idx", "part_bitmaps", "stats", "row_order"):
         setattr(e, name, 1 << 28)
@@ -140,7 +172,12 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, o=ctypes.c_void_p(1 << 30), B=1, H=1, S=128,
 def test_fwd_validation():
     assert fwd(enc=None) == L.SMH_EINVAL
     assert fwd(S=256) == L.SMH_EINVAL                 # enc->S mismatch
-    assert fwd(S=100) == L.SMH_EUNSUPPORTED
+    assert fwd(S=100) == L.SMH_EINVAL                 # enc->S mismatch
+    assert fwd(S=100, enc_S=100, B=0) == L.SMH_OK     # ragged S accepted
+    assert fwd(mb=2) == L.SMH_EINVAL                  # B = 1
+    assert fwd(mh=2, H=3) == L.SMH_EINVAL
+    assert fwd(mh=3, H=3, B=0) == L.SMH_OK
+    assert fwd(mb=0) == L.SMH_EINVAL
     assert fwd(d=96) == L.SMH_EUNSUPPORTED
     assert fwd(in_dt=L.SMH_F32, out_dt=L.SMH_F32) == L.SMH_EUNSUPPORTED
     assert fwd(out_dt=L.SMH_BF16) == L.SMH_EUNSUPPORTED

@@ -279,3 +279,132 @@ def test_graph_replay_matches_eager():
         assert torch.isfinite(eager).all()
     err = maxerr(out, attention(q, k, v, mask))
     assert err <= TOL["f16"]
+
+
+def run_stack(q, k, v, masks, kernel, out_dtype, dev, guard=0):
+    """Forward through an encoding of `masks` ([S, S] or a stack); the
+    output lives at the front of a larger buffer whose tail (`guard`
+    elements of NaN) must come back untouched."""
+    mt = torch.from_numpy(np.ascontiguousarray(masks)).to(dev)
+    enc = smh.encode_mask(mt)
+    st = smh.mask_stats_get(enc)
+    odt = out_dtype or q.dtype
+    buf = torch.full((q.numel() + guard,), float("nan"), dtype=odt,
+                     device=dev)
+    out = buf[:q.numel()].view(q.shape)
+    o = smh.sparse_mha_fwd(q.to(dev), k.to(dev), v.to(dev), enc,
+                           kernel=kernel, out_dtype=out_dtype,
+                           stats=None if kernel == "auto" else st, out=out)
+    torch.cuda.synchronize()
+    if guard:
+        assert torch.isnan(buf[q.numel():]).all(), "write past the output"
+    return o
+
+
+RAGGED = [  # (B, H, S, d, dtype, family, kw)
+    (1, 2, 1, 64, "f16", "full", {}),
+    (2, 1, 8, 64, "f16", "causal", {}),
+    (1, 2, 65, 64, "f16", "random", {"p": 0.3}),
+    (1, 1, 100, 128, "bf16", "full", {}),
+    (2, 2, 200, 64, "f16", "causal", {}),
+    (1, 3, 333, 128, "f16", "random", {"p": 0.02}),
+    (1, 2, 520, 64, "bf16", "window", {"w": 30}),
+]
+
+
+@pytest.mark.parametrize("kernel", ["blockwise", "rowwise", "auto"])
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"{c[5]}-S{c[2]}-d{c[3]}-{c[4]}")
+def test_ragged_sequence(case, kernel):
+    """S not a multiple of 64, whole output against the oracle; nothing is
+    written past the output (rows past S are never stored)."""
+    dev = need_gpu()
+    B, H, S, d, dt, fam, kw = case
+    print(f"ragged {kernel} {case}", flush=True)
+    mask = mask_family(fam, S, seed=S + d, **kw)
+    q, k, v = make_qkv(B, H, S, d, dt, seed=S + 1)
+    out_dt = torch.float32 if dt == "bf16" else None
+    o = run_stack(q, k, v, mask, kernel, out_dt, dev, guard=4096)
+    err = maxerr(o, attention(q, k, v, mask))
+    assert err <= TOL[dt], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("kernel", ["blockwise", "rowwise", "auto"])
+@pytest.mark.parametrize("mb,mh,S,d,dt", [
+    (2, 1, 192, 64, "f16"), (1, 3, 100, 128, "bf16"), (2, 3, 256, 64, "f16"),
+    (1, 1, 130, 64, "f16")])
+def test_mask_stack(kernel, mb, mh, S, d, dt):
+    """A mask per sequence and/or head (B = 2, H = 3), whole output."""
+    dev = need_gpu()
+    print(f"stack {kernel} {mb}x{mh} S={S} d={d} {dt}", flush=True)
+    rng = np.random.default_rng(mb * 100 + mh * 10 + S)
+    dens = rng.uniform(0.01, 0.8, (mb, mh, 1, 1))
+    masks = rng.random((mb, mh, S, S)) < dens
+    masks[0, 0, 5] = False                        # an empty row
+    masks[-1, -1] = np.tril(np.ones((S, S), bool))
+    q, k, v = make_qkv(2, 3, S, d, dt, seed=S + mb)
+    out_dt = torch.float32 if dt == "bf16" else None
+    o = run_stack(q, k, v, masks, kernel, out_dt, dev, guard=1024)
+    err = maxerr(o, attention(q, k, v, masks))
+    assert err <= TOL[dt], f"max abs err {err}"
+    if (mb, mh) != (1, 1):      # mask (0, 0) serves (b, h) = (0, 0)
+        assert (o[0, 0, 5] == 0).all()
+
+
+@pytest.mark.parametrize("kernel", ["blockwise", "rowwise", "auto"])
+def test_mask_stack_heavy_order(kernel):
+    """Per-head masks of different weight on a grid larger than one wave of
+    workgroups, so the rows are visited in the encoding's heavy-first order
+    across masks; sampled rows against the oracle."""
+    dev = need_gpu()
+    B, H, S, d = 4, 16, 2048, 64
+    print(f"stack heavy order {kernel}", flush=True)
+    rng = np.random.default_rng(8)
+    i = np.arange(S)
+    masks = np.zeros((1, H, S, S), bool)
+    for h in range(H):
+        w = 32 * (h + 1)
+        band = np.abs(i[:, None] - i[None, :]) <= w
+        masks[0, h] = band & (rng.random((S, S)) < (0.3 + 0.04 * h))
+    masks[0, 3] |= np.tril(np.ones((S, S), bool))   # one heavy causal head
+    q, k, v = make_qkv(B, H, S, d, "f16", seed=9)
+    o = run_stack(q, k, v, masks, kernel, torch.float32, dev)
+    worst = 0.0
+    for b, h in [(0, 0), (1, 3), (2, 9), (3, 15)]:
+        rows = sample_rows(S, None, rng, n=24)
+        ref = attention_rows(q, k, v, masks, b, h, rows)
+        got = o[b, h, torch.as_tensor(rows, device=dev)].double().cpu().numpy()
+        worst = max(worst, float(np.abs(got - ref).max()))
+    assert worst <= TOL["f16"], worst
+
+
+def test_mask_stack_device_choice_matches_host():
+    dev = need_gpu()
+    S, d = 512, 64
+    rng = np.random.default_rng(3)
+    for dens in (0.002, 0.5):
+        masks = rng.random((2, 1, S, S)) < dens
+        q, k, v = (x.to(dev) for x in make_qkv(2, 4, S, d, "f16", seed=3))
+        enc = smh.encode_mask(torch.from_numpy(masks).to(dev))
+        st = smh.mask_stats_get(enc)
+        which = smh.select_kernel(st, 2, 4, d, q.dtype)
+        a = smh.sparse_mha_fwd(q, k, v, enc, kernel="auto")
+        b = smh.sparse_mha_fwd(q, k, v, enc, kernel=which)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (dens, which)
+
+
+def test_mask_stack_shape_checks():
+    dev = need_gpu()
+    q = torch.zeros((2, 3, 64, 64), dtype=torch.float16, device=dev)
+    enc = smh.encode_mask(torch.ones((3, 1, 64, 64), dtype=torch.bool,
+                                     device=dev))
+    with pytest.raises(smh.SmhError) as e:     # 3 masks for B = 2
+        smh.sparse_mha_fwd(q, q, q, enc, kernel="blockwise")
+    assert e.value.status == 1
+    enc = smh.encode_mask(torch.ones((1, 3, 64, 64), dtype=torch.bool,
+                                     device=dev))
+    smh.sparse_mha_fwd(q, q, q, enc, kernel="blockwise")
+    st = smh.mask_stats_get(enc)
+    with pytest.raises(smh.SmhError):          # stats of another stack
+        smh.sparse_mha_fwd(q, q, q, enc, kernel="auto",
+                           stats=dict(st, mask_h=1))

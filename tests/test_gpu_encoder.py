@@ -95,14 +95,69 @@ def test_nonzero_bytes_count_as_valid():
     assert_same_encoding(got, encode_c(vals != 0))
 
 
-def test_empty_sequence_and_ragged():
+def test_empty_sequence():
     dev = need_gpu()
     enc = smh.encode_mask(torch.zeros((0, 0), dtype=torch.bool, device=dev))
     st = smh.mask_stats_get(enc)
     assert st["nnz"] == 0 and st["n_full"] == 0 and st["n_partial"] == 0
+
+
+@pytest.mark.parametrize("S,p", [(1, 1.0), (8, 0.5), (65, 0.3), (80, 0.9),
+                                 (100, 1.0), (130, 0.05), (200, 0.5),
+                                 (257, 0.02), (1000, 0.2), (1040, 0.6),
+                                 (3001, 0.01)])
+def test_ragged_sequence(S, p):
+    """S not a multiple of 64: elements past S are not valid, the cut tiles
+    are never full, rows past S are not counted.  S % 16 == 0 (80, 1040)
+    reads whole 16-byte pieces, other S read bytes."""
+    dev = need_gpu()
+    print(f"encoder ragged S={S}", flush=True)
+    m = mask_family("random", S, seed=S, p=p)
+    m[: S // 4, : S // 2] = True
+    check(m, dev)
+    check(np.tril(np.ones((S, S), bool)), dev)
+
+
+def stack_check(masks, dev):
+    from oracle.encode import encode_stack
+    mt = torch.from_numpy(np.ascontiguousarray(masks)).to(dev)
+    enc = smh.encode_mask(mt)
+    st = smh.mask_stats_get(enc)
+    assert (st["mask_b"], st["mask_h"]) == masks.shape[:2]
+    got = enc_to_host(enc, st)
+    ref = encode_stack(masks)
+    assert_same_encoding(got, ref)
+    order, mrt = expected_row_order(ref)
+    assert got["row_order"].tolist() == order
+    assert st["max_row_tiles"] == mrt
+
+
+@pytest.mark.parametrize("mb,mh,S", [(2, 3, 130), (1, 12, 512), (8, 1, 256),
+                                     (4, 4, 100), (1, 72, 1024),
+                                     (32, 32, 512)])
+def test_mask_stack(mb, mh, S):
+    """One encoding of a stack of masks, bit-exact with the masks'
+    encodings one after another.  72 x 16 rows is past the fused scan's
+    1024 rows (the scan runs as a launch of its own); 32 x 32 x 8 rows is
+    the largest stack accepted (8192 rows)."""
+    dev = need_gpu()
+    print(f"encoder stack {mb}x{mh} S={S}", flush=True)
+    rng = np.random.default_rng(mb * 1000 + mh * 10 + S)
+    dens = rng.uniform(0.0005, 0.7, (mb, mh, 1, 1))
+    masks = rng.random((mb, mh, S, S)) < dens
+    masks[0, -1] = np.tril(np.ones((S, S), bool))
+    stack_check(masks, dev)
+
+
+def test_stack_limits():
+    dev = need_gpu()
+    assert smh.encode_workspace_bytes(512, 32, 32) > 0
+    assert smh.encode_workspace_bytes(512, 32, 33) == 0     # 8448 rows
+    assert smh.encode_workspace_bytes(64, 0, 1) == 0
     with pytest.raises(smh.SmhError) as e:
-        smh.encode_mask(torch.ones((100, 100), dtype=torch.bool, device=dev))
-    assert e.value.status == 2
+        smh.encode_mask(torch.ones((1, 8193, 64, 64), dtype=torch.bool,
+                                   device=dev))
+    assert e.value.status == 1
 
 
 def test_deterministic_and_reusable_workspace():

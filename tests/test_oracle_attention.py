@@ -183,3 +183,33 @@ def test_workload_row0_has_single_key(cid, config_mask):
     q, k, v = make_qkv(1, 1, cfg.S, cfg.d, cfg.dtype, seed=cid)
     got = attention_rows(q, k, v, mask, 0, 0, [0])
     assert np.array_equal(got[0], v[0, 0, 0].double().numpy())
+
+
+@pytest.mark.parametrize("mb,mh,S", [(2, 1, 48), (1, 3, 70), (2, 3, 33),
+                                     (1, 1, 40)])
+def test_mask_stack_matches_sdpa(mb, mh, S):
+    """A mask per sequence and/or head: the library's broadcasting of a
+    boolean attn_mask [Bm, Hm, S, S] over [B, H] is the same rule."""
+    B, H, d = 2, 3, 16
+    rng = np.random.default_rng(mb * 10 + mh + S)
+    masks = rng.random((mb, mh, S, S)) < 0.3
+    masks[..., np.arange(S), np.arange(S)] = True     # no empty row
+    q, k, v = (_rand((B, H, S, d), s) for s in (21, 22, 23))
+    got = attention(q, k, v, masks)
+    np.testing.assert_allclose(got, _sdpa(q, k, v, mask=masks),
+                               rtol=0, atol=1e-12)
+    # rows of the per-row entry point see the same masks
+    rows = [0, S // 2, S - 1]
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_allclose(
+                attention_rows(q, k, v, masks, b, h, rows), got[b, h, rows],
+                rtol=0, atol=1e-13)
+
+
+def test_mask_stack_rejects_wrong_shape():
+    q = _rand((2, 3, 8, 4), 1)
+    with pytest.raises(AssertionError):
+        attention(q, q, q, np.ones((3, 1, 8, 8), bool))
+    with pytest.raises(AssertionError):
+        attention(q, q, q, np.ones((1, 2, 8, 8), bool))

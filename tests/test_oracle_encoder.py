@@ -278,3 +278,45 @@ def test_structured_twin(config_mask):
         enc = encode_c(m)
         check_structure(enc, 256)
         same(enc, encode_py(m))
+
+
+def section(enc, g, n):
+    """Mask g's part of a stacked encoding, as a one-mask encoding."""
+    out = {}
+    for key in ("full", "part"):
+        ptr = np.asarray(enc[key + "_row_ptr"][g * n:g * n + n + 1])
+        out[key + "_row_ptr"] = ptr - ptr[0]
+        out[key + "_col_idx"] = enc[key + "_col_idx"][ptr[0]:ptr[-1]]
+        if key == "part":
+            out["part_bitmaps"] = enc["part_bitmaps"][ptr[0]:ptr[-1]]
+    out["n_full"] = int(out["full_row_ptr"][-1])
+    out["n_partial"] = int(out["part_row_ptr"][-1])
+    return out
+
+
+@pytest.mark.parametrize("mb,mh,S", [(2, 3, 130), (1, 4, 64), (3, 1, 100),
+                                     (1, 1, 256)])
+def test_stack_sections_decode(mb, mh, S):
+    """Each mask of a stack decodes back from its rows of the stacked
+    encoding (mask g = gb * Hm + gh owns rows g * n_ot .. g * n_ot + n_ot-1),
+    counts are totals, and the Python twin builds the same stack."""
+    from oracle.encode import encode_stack
+    rng = np.random.default_rng(S + mb + mh)
+    dens = rng.uniform(0.001, 0.6, (mb, mh, 1, 1))
+    masks = rng.random((mb, mh, S, S)) < dens
+    masks[0, 0, :S // 3] = True          # some full tiles
+    enc = encode_stack(masks)
+    n = -(-S // 64)
+    assert len(enc["full_row_ptr"]) == mb * mh * n + 1
+    for gb in range(mb):
+        for gh in range(mh):
+            sec = section(enc, gb * mh + gh, n)
+            assert np.array_equal(decode(sec, S), masks[gb, gh])
+    assert enc["nnz"] == int(masks.sum())
+    assert enc["n_empty_rows"] == int((~masks.any(axis=3)).sum())
+    assert enc["nnz"] == 4096 * enc["n_full"] + int(
+        popcounts(enc["part_bitmaps"]).sum())
+    if S <= 130:
+        same(encode_stack(masks, encode=encode_py), enc)
+    if mb * mh == 1:
+        same(enc, encode_c(masks[0, 0]))
