@@ -110,11 +110,12 @@ __device__ inline int block_max(int x, int *sh) {
 constexpr int kMaxSegTiles = kWin * kMaxSegWin;  // 64
 constexpr int kMaxN = SMH_MAX_S / 64;              // outer tiles per side
 // Scan sizes: rows of the encoding it holds in LDS, and bins of its
-// stored-tile-count histogram (counts 0..n).  The fused form (scan as one
-// workgroup of the placement launch) is kept small because every placement
-// workgroup reserves its LDS.
+// stored-tile-count histogram (counts 0..n; 0 = rank by direct comparison
+// with every row instead).  The fused form (scan as one workgroup of the
+// placement launch) is kept small because every placement workgroup
+// reserves its LDS.
 constexpr int kScanRows = SMH_MAX_ENC_ROWS, kScanBins = kMaxN + 1;
-constexpr int kFusedRows = 1024, kFusedBins = kFusedRows + 1;
+constexpr int kFusedRows = 1024, kFusedBins = 0;
 constexpr int kFusedMaxSegs = 2048;
 
 struct Seg {  // per-segment scratch (EncLayout)
@@ -240,24 +241,29 @@ __device__ inline unsigned long long block_exclusive_scan(unsigned long long x,
 // set.  Thread t owns a run of whole rows; every load of the first pass is
 // independent of the others, so the pass costs one memory round trip.
 // Schedule: row J's rank = rows with more stored tiles + rows before J with
-// as many; the first term from a histogram of the counts, the second from
-// a running histogram over blocks of 256 rows plus a count inside J's block.
+// as many.  Up to a few hundred rows each thread compares its rows with
+// every row (a loop of uniform length, whose loads pipeline); for more, the
+// first term comes from a histogram of the counts and the second from a
+// running histogram over blocks of 256 rows plus a count inside J's block.
 template <int kRows, int kBins>
 __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
                           smh_mask_enc enc, bool offsets) {
+    constexpr int kH = kBins > 0 ? kBins : 1;
     __shared__ uint32_t rowc[kRows];  // full << 16 | partial (each <= n <= 2048)
-    __shared__ int above[kBins];      // histogram, then rows with a larger count
-    __shared__ int seen[kBins];       // rows of earlier blocks per count
+    __shared__ int above[kH];         // histogram, then rows with a larger count
+    __shared__ int seen[kH];          // rows of earlier blocks per count
     __shared__ unsigned long long sh_u[4];
     __shared__ long long sh_l[4];
     __shared__ int sh_i[4];
     const int t = threadIdx.x;
     const int C = plan.per_row;
-    for (int c = t; c <= n; c += 256) {
-        above[c] = 0;
-        seen[c] = 0;
+    if constexpr (kBins > 0) {
+        for (int c = t; c <= n; c += 256) {
+            above[c] = 0;
+            seen[c] = 0;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     const int rows_per = (R + 255) / 256;
     const int r_lo = min(R, t * rows_per), r_hi = min(R, r_lo + rows_per);
     unsigned long long own = 0;
@@ -274,7 +280,7 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
         }
         const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull);
         rowc[I] = ((uint32_t)f << 16) | (uint32_t)p;
-        atomicAdd(&above[f + p], 1);
+        if constexpr (kBins > 0) atomicAdd(&above[f + p], 1);
         mx = max(mx, f + p);
         empty += 64 - __popcll(an);
         own += rc;
@@ -302,30 +308,44 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     nnz = block_sum(nnz, sh_l);
     empty = block_sum(empty, sh_l);
     mx = block_max(mx, sh_i);
-    {   // histogram -> rows with a larger count: R - (rows with count <= c)
-        const int per = (n + 1 + 255) / 256;
-        const int c_lo = min(n + 1, t * per), c_hi = min(n + 1, c_lo + per);
-        unsigned long long h = 0;
-        for (int c = c_lo; c < c_hi; ++c) h += (unsigned long long)above[c];
-        unsigned long long below = block_exclusive_scan(h, sh_u);
-        for (int c = c_lo; c < c_hi; ++c) {
-            below += (unsigned long long)above[c];
-            above[c] = R - (int)below;
+    auto cnt_of = [&](int J) { return (int)((rowc[J] >> 16) + (rowc[J] & 0xFFFFu)); };
+    if constexpr (kBins == 0) {  // (every row's count is in LDS: barriers above)
+        for (int J = t; J < R; J += 256) {
+            const int cj = cnt_of(J);
+            int rank = 0;
+#pragma unroll 8
+            for (int J2 = 0; J2 < R; ++J2) {
+                const int c2 = cnt_of(J2);
+                rank += (c2 > cj) || (c2 == cj && J2 < J);
+            }
+            enc.row_order[rank] = J;
         }
-    }
-    __syncthreads();
-    for (int k0 = 0; k0 < R; k0 += 256) {
-        const int J = k0 + t;
-        const int cj = J < R ? (int)((rowc[J] >> 16) + (rowc[J] & 0xFFFFu)) : 0;
-        if (J < R) {
-            int ties = 0;
-            for (int J2 = k0; J2 < J; ++J2)
-                ties += (int)((rowc[J2] >> 16) + (rowc[J2] & 0xFFFFu)) == cj;
-            enc.row_order[above[cj] + seen[cj] + ties] = J;
+    } else {
+        {   // histogram -> rows with a larger count: R - (rows with count <= c)
+            const int per = (n + 1 + 255) / 256;
+            const int c_lo = min(n + 1, t * per), c_hi = min(n + 1, c_lo + per);
+            unsigned long long h = 0;
+            for (int c = c_lo; c < c_hi; ++c) h += (unsigned long long)above[c];
+            unsigned long long below = block_exclusive_scan(h, sh_u);
+            for (int c = c_lo; c < c_hi; ++c) {
+                below += (unsigned long long)above[c];
+                above[c] = R - (int)below;
+            }
         }
-        __syncthreads();  // every rank of this block read seen[]
-        if (J < R) atomicAdd(&seen[cj], 1);
         __syncthreads();
+        for (int k0 = 0; k0 < R; k0 += 256) {
+            const int J = k0 + t;
+            const int cj = J < R ? cnt_of(J) : 0;
+            const int k1 = min(R, k0 + 256);
+            int ties = 0;
+#pragma unroll 8
+            for (int J2 = k0; J2 < k1; ++J2)  // uniform length: loads pipeline
+                ties += (J2 < J) && cnt_of(J2) == cj;
+            if (J < R) enc.row_order[above[cj] + seen[cj] + ties] = J;
+            __syncthreads();  // every rank of this block read seen[]
+            if (J < R) atomicAdd(&seen[cj], 1);
+            __syncthreads();
+        }
     }
     if (t == 0) {
         enc.stats[0] = nnz;
