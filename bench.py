@@ -14,7 +14,9 @@ The headline value is effective TFLOP/s: 4*d FLOPs per valid (query, key)
 pair, summed over every (batch, head), divided by the step time.
 
 Default workload: BERT-base-shaped sliding window (B=8, H=12, S=512, d=64,
-fp16, |i-j| <= 64).  Prints one JSON line.
+fp16, |i-j| <= 64).  --seq-len changes S (any length: the last tiles are
+cut), --mask-stack batch gives each sequence its own mask (the pattern cut
+to a per-sequence length), encoded as one stack.  Prints one JSON line.
 """
 import argparse
 import json
@@ -54,6 +56,14 @@ def parse():
                          "bench (rocprofv3 --pmc, one counter per run), then "
                          "those of --copy-reference; writes the HBM bytes "
                          "per launch of the attention kernel to profiles/")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="override the workload's S (mask pattern and Q/K/V "
+                         "regenerated at that length)")
+    ap.add_argument("--mask-stack", default="shared",
+                    choices=["shared", "batch"],
+                    help="shared: one mask for every (batch, head); batch: "
+                         "one mask per sequence (padding to a seeded length "
+                         "in [S/2, S])")
     ap.add_argument("--out-dtype", default="auto",
                     choices=["auto", "in", "f32"],
                     help="output type; auto = input type for fp16, f32 for "
@@ -144,9 +154,17 @@ def write_traffic(args, cfg):
     print(json.dumps(rec))
 
 
-def encoding_bytes(st, n):
-    return 4 * 2 * (n + 1) + 4 * (st["n_full"] + st["n_partial"]) + \
+def encoding_bytes(st, rows):
+    return 4 * 2 * (rows + 1) + 4 * (st["n_full"] + st["n_partial"]) + \
         512 * st["n_partial"]
+
+
+def users_per_mask(mask, B, H):
+    """(batch, head) pairs that share each mask of a [S, S] mask or a
+    [mask_b, mask_h, S, S] stack."""
+    if mask.ndim == 2:
+        return B * H
+    return (1 if mask.shape[0] > 1 else B) * (1 if mask.shape[1] > 1 else H)
 
 
 def cpu_baseline(cfg, mask, qkv, budget_s):
@@ -163,8 +181,9 @@ def cpu_baseline(cfg, mask, qkv, budget_s):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
+    from oracle.encode import encode_stack
     t0 = time.perf_counter()
-    encode_c(mask)
+    encode_c(mask) if mask.ndim == 2 else encode_stack(mask)
     t_enc = time.perf_counter() - t0
     rows_done = 0
     t_attn = 0.0
@@ -173,10 +192,11 @@ def cpu_baseline(cfg, mask, qkv, budget_s):
     for b in range(cfg.B):
         for h in range(cfg.H):
             for r0 in range(0, cfg.S, blk):
+                r1 = min(cfg.S, r0 + blk)
                 t1 = time.perf_counter()
-                attention_rows(q, k, v, mask, b, h, np.arange(r0, r0 + blk))
+                attention_rows(q, k, v, mask, b, h, np.arange(r0, r1))
                 t_attn += time.perf_counter() - t1
-                rows_done += blk
+                rows_done += r1 - r0
                 if t_attn >= budget_s:
                     break
             if t_attn >= budget_s:
@@ -185,7 +205,7 @@ def cpu_baseline(cfg, mask, qkv, budget_s):
             break
     total_rows = cfg.B * cfg.H * cfg.S
     t_total = t_enc + t_attn * total_rows / rows_done
-    flops = 4.0 * cfg.d * cfg.B * cfg.H * float(mask.sum())
+    flops = 4.0 * cfg.d * users_per_mask(mask, cfg.B, cfg.H) * float(mask.sum())
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
             "cores": int(cores), "kind": "oracle",
             "sample": (f"scalar C encoder on the full mask + fp64 dense "
@@ -195,38 +215,56 @@ def cpu_baseline(cfg, mask, qkv, budget_s):
                        f"for the whole workload")}
 
 
+def workload(args):
+    """The Config and mask ([S, S], or a [B, 1, S, S] stack) the options
+    name."""
+    import dataclasses
+    from workloads import get_config, make_mask, padding_stack
+    cfg = get_config(args.config)
+    if args.seq_len:
+        cfg = dataclasses.replace(
+            cfg, S=args.seq_len, name=f"{cfg.name}-S{args.seq_len}",
+            desc=f"{cfg.desc}; S changed to {args.seq_len}")
+    mask = make_mask(cfg)
+    if args.mask_stack == "batch":
+        mask = padding_stack(mask, cfg.B, cfg.cid)
+        cfg = dataclasses.replace(
+            cfg, name=f"{cfg.name}-per-sequence",
+            desc=f"{cfg.desc}; one mask per sequence (cut to a seeded length "
+                 f"in [S/2, S])")
+    return cfg, mask
+
+
 def main():
     args = parse()
     if args.copy_reference:
         copy_reference()
         return
     if args.write_traffic:
-        from workloads import get_config
-        write_traffic(args, get_config(args.config))
+        write_traffic(args, workload(args)[0])
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus "
               f"{args.gpus} is not supported (the path needs no collective; "
               f"run --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import sparse_masked_head_amd as smh
-    from workloads import get_config, make_mask, make_qkv
+    from workloads import make_qkv
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg = get_config(args.config)
-    mask = make_mask(cfg)
+    cfg, mask = workload(args)
     qkv = make_qkv(cfg.B, cfg.H, cfg.S, cfg.d, cfg.dtype, seed=cfg.cid)
     q, k, v = (x.to(dev) for x in qkv)
     mask_d = torch.from_numpy(mask).to(dev)
     out_dt = {"auto": torch.float32 if cfg.dtype == "bf16" else q.dtype,
               "in": q.dtype, "f32": torch.float32}[args.out_dtype]
-    ws = torch.empty(smh.encode_workspace_bytes(cfg.S), dtype=torch.uint8,
-                     device=dev)
+    mb, mh = (1, 1) if mask.ndim == 2 else mask.shape[:2]
+    ws = torch.empty(smh.encode_workspace_bytes(cfg.S, mb, mh),
+                     dtype=torch.uint8, device=dev)
     out = torch.empty(q.shape, dtype=out_dt, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -311,15 +349,15 @@ def main():
     enc_ms = kernel_us(encode_only) / 1e3
     fwd_ms = kernel_us(fwd_only) / 1e3
 
-    nnz = st["nnz"]
+    nnz = st["nnz"]              # total over the masks of a stack
     BH = cfg.B * cfg.H
-    flops = 4.0 * cfg.d * BH * nnz
+    flops = 4.0 * cfg.d * users_per_mask(mask, cfg.B, cfg.H) * nnz
     value = flops / step_s / 1e12
     eb_in = 2
     eb_out = out.element_size()
-    n = cfg.S // 64
+    rows = mb * mh * cfg.n_ot
     attn_bytes = BH * cfg.S * cfg.d * (3 * eb_in + eb_out) + \
-        encoding_bytes(st, n)
+        encoding_bytes(st, rows)
     ai = flops / attn_bytes
     fwd_s = fwd_ms / 1e3
     if ai < RIDGE:
@@ -348,7 +386,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, seeded mask)",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S,
-                   "d": cfg.d, "mask": cfg.desc,
+                   "d": cfg.d, "mask": cfg.desc, "mask_stack": [mb, mh],
                    "out_dtype": str(out_dt).replace("torch.", ""),
                    "launch": "eager" if args.eager else
                    f"hip graph, {per_graph} steps per replay",

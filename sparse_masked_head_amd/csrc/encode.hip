@@ -52,9 +52,11 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 // How the strip pass reads a mask row: kAligned64 (S % 64 == 0: whole
 // 16-byte pieces, no bounds beyond the tile count), kAligned16 (S % 16 == 0:
-// whole pieces, rows and pieces past S read as zero), kBytes (rows are not
-// 16-byte aligned: byte loads, elements past S read as zero).
-enum LoadMode { kAligned64 = 0, kAligned16 = 1, kBytes = 2 };
+// whole pieces, rows and pieces past S read as zero), kDwords (rows are not
+// 16-byte aligned: the aligned dwords that hold the piece's valid bytes,
+// funnel-shifted into place; elements past S read as zero).  Every dword
+// loaded holds at least one byte of the mask.
+enum LoadMode { kAligned64 = 0, kAligned16 = 1, kDwords = 2 };
 
 // Loads of one window: thread t reads, for k = 0..7, mask row 8k + (t >> 5)
 // of the strip (strip row 0 = mask row row0), bytes 16*(t & 31) .. +15 of
@@ -78,10 +80,22 @@ __device__ __forceinline__ void load_window(u4v (&v)[8], const uint8_t *strip,
                                            : u4v{0, 0, 0, 0};
         } else {
             uint32_t wd[4] = {0, 0, 0, 0};
-            if (ok && row_ok) {
+            if (ok && row_ok && col < S) {
+                const int nb = min(16, S - col);  // valid bytes of the piece
+                const uintptr_t at = reinterpret_cast<uintptr_t>(p);
+                const uint32_t *w = reinterpret_cast<const uint32_t *>(at & ~(uintptr_t)3);
+                const int sh = (int)(at & 3);
+                const int nd = (sh + nb + 3) >> 2;  // dwords holding them, <= 5
+                uint32_t x[5];
 #pragma unroll
-                for (int b = 0; b < 16; ++b)
-                    if (col + b < S) wd[b >> 2] |= (uint32_t)p[b] << (8 * (b & 3));
+                for (int i = 0; i < 5; ++i) x[i] = i < nd ? w[i] : 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // bytes sh .. sh+3 of (x[i+1] : x[i]), then the bytes past S cleared
+                    const uint32_t y = __builtin_amdgcn_alignbyte(x[i + 1], x[i], sh);
+                    const int keep = nb - 4 * i;
+                    wd[i] = keep >= 4 ? y : keep <= 0 ? 0u : y & ((1u << (8 * keep)) - 1u);
+                }
             }
             v[k] = u4v{wd[0], wd[1], wd[2], wd[3]};
         }
@@ -442,7 +456,7 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
         hipLaunchKernelGGL(enc_strip<kAligned16>, dim3(plan.total), dim3(256), 0,
                            stream, mask, S, n, plan, sg);
     else
-        hipLaunchKernelGGL(enc_strip<kBytes>, dim3(plan.total), dim3(256), 0,
+        hipLaunchKernelGGL(enc_strip<kDwords>, dim3(plan.total), dim3(256), 0,
                            stream, mask, S, n, plan, sg);
     if (plan.total <= kFusedMaxSegs && R <= kFusedRows) {
         hipLaunchKernelGGL(enc_place<true>, dim3(plan.total + 1), dim3(256), 0,

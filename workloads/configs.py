@@ -25,7 +25,7 @@ class Config:
 
     @property
     def n_ot(self):
-        return self.S // 64
+        return -(-self.S // 64)
 
 
 CONFIGS = {

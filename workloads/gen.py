@@ -8,7 +8,10 @@ same bits):
   (round-to-nearest-even).  Nothing else is applied.
 * Masks: ``numpy.random.default_rng(seed)`` (PCG64).  True means the
   (query i, key j) pair takes part in attention.  One [S, S] mask serves
-  every (batch, head).
+  every (batch, head), or ``padding_stack`` gives each sequence of the
+  batch its own mask: the pattern cut to that sequence's length (query and
+  key positions past it take no part), lengths uniform in [S/2, S] from
+  ``default_rng(seed + 1000)``.
 """
 import numpy as np
 import torch
@@ -109,3 +112,15 @@ def mask_family(family, S, seed=0, **kw):
 def make_mask(cfg):
     """The [S, S] bool mask of a workload Config (seeded by cfg.cid)."""
     return mask_family(cfg.family, cfg.S, seed=cfg.cid)
+
+
+def padding_stack(mask, B, seed):
+    """[B, 1, S, S] bool: sequence b keeps mask[i, j] for i, j < L_b, with
+    L_b drawn uniformly from [S // 2, S] (variable-length batches)."""
+    S = mask.shape[0]
+    rng = np.random.default_rng(int(seed) + 1000)
+    lens = rng.integers(S // 2, S + 1, B)
+    out = np.zeros((B, 1, S, S), dtype=bool)
+    for b, L in enumerate(lens):
+        out[b, 0, :L, :L] = mask[:L, :L]
+    return out
