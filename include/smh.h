@@ -90,6 +90,13 @@ typedef enum {
  *       max_row_tiles (stored tiles in the fullest outer-tile row).
  *   row_order[R] (device int32): the encoding's rows sorted by their number
  *       of stored tiles, most first, ties by ascending row (a schedule).
+ *   row_info[R][16] (device int32): a summary of each row that a kernel
+ *       reads in one load: [0] full_row_ptr[r], [1] its full-tile count,
+ *       [2] part_row_ptr[r], [3] its partial-tile count, [4..7] the columns
+ *       of the row's first four stored tiles in list order (full tiles,
+ *       then partial tiles), -1 past the row's last tile, [8..12] the
+ *       encoding's nnz (low, high 32 bits), n_full, n_partial and
+ *       max_row_tiles, [13..15] 0.
  * Capacities reserved in the workspace: col_idx arrays R * n_ot, bitmaps
  * R * n_ot * 64 words. */
 typedef struct {
@@ -104,6 +111,7 @@ typedef struct {
     uint64_t *part_bitmaps;
     int64_t *stats;
     int32_t *row_order;
+    int32_t *row_info;
 } smh_mask_enc;
 
 /* Host copy of the encoding statistics (totals over the masks of the

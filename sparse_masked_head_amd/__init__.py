@@ -87,7 +87,8 @@ class MaskEncoding:
             part_col_idx=view(e.part_col_idx, st["n_partial"], torch.int32, 4),
             part_bitmaps=view(e.part_bitmaps, st["n_partial"] * 64,
                               torch.int64, 8).view(-1, 64),
-            row_order=view(e.row_order, n, torch.int32, 4))
+            row_order=view(e.row_order, n, torch.int32, 4),
+            row_info=view(e.row_info, 16 * n, torch.int32, 4).view(-1, 16))
 
 
 def encode_mask(mask, workspace=None):

@@ -27,7 +27,8 @@ class MaskEnc(ctypes.Structure):
                 ("part_col_idx", ctypes.c_void_p),
                 ("part_bitmaps", ctypes.c_void_p),
                 ("stats", ctypes.c_void_p),
-                ("row_order", ctypes.c_void_p)]
+                ("row_order", ctypes.c_void_p),
+                ("row_info", ctypes.c_void_p)]
 
 
 class MaskStats(ctypes.Structure):

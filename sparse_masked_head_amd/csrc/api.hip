@@ -116,6 +116,7 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
         e.part_bitmaps = (uint64_t *)(ws + L.part_bitmaps);
         e.stats = (int64_t *)(ws + L.stats);
         e.row_order = (int32_t *)(ws + L.row_order);
+        e.row_info = (int32_t *)(ws + L.row_info);
         if (launch_encode(masks, S, ws, L, e, (hipStream_t)stream) !=
             hipSuccess)
             return SMH_EHIP;
@@ -214,7 +215,8 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
             !aligned(o, 16))
             return SMH_EINVAL;
         if (!enc->full_row_ptr || !enc->full_col_idx || !enc->part_row_ptr ||
-            !enc->part_col_idx || !enc->part_bitmaps || !enc->row_order)
+            !enc->part_col_idx || !enc->part_bitmaps || !enc->row_order ||
+            !enc->row_info)
             return SMH_EINVAL;
         const size_t in_b = n_el * 2;
         const size_t out_b = n_el * (out_dt == SMH_F32 ? 4 : 2);

@@ -16,13 +16,16 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TO
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int oi = blockIdx.x / a.U;
     const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
-    if (device_choice<D>(a) == 2) {
-        blockwise_row<D, TIn, TOut>(a, smem, sl.row, sl.I, sl.bh);
+    // the row summary carries the statistics the choice reads (both paths
+    // need the summary)
+    const RowInfo ri = load_row_info(a, sl.row);
+    if (device_choice<D>(a, ri) == 2) {
+        blockwise_row<D, TIn, TOut>(a, smem, sl.I, sl.bh, ri);
     } else {
         const int w = threadIdx.x >> 6;
         char *slice = smem + w * RowLds<D>::BYTES;
-        rowwise_group<D, TIn, TOut>(a, slice, sl.row, sl.I, w, sl.bh);
-        rowwise_group<D, TIn, TOut>(a, slice, sl.row, sl.I, w + 4, sl.bh);
+        rowwise_group<D, TIn, TOut>(a, slice, sl.I, w, sl.bh, ri);
+        rowwise_group<D, TIn, TOut>(a, slice, sl.I, w + 4, sl.bh, ri);
     }
 }
 

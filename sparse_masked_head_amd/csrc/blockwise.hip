@@ -11,7 +11,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TI
     // heavy rows first across all heads (slot_of)
     const int oi = blockIdx.x / a.U;
     const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
-    blockwise_row<D, TIn, TOut>(a, smem, sl.row, sl.I, sl.bh);
+    blockwise_row<D, TIn, TOut>(a, smem, sl.I, sl.bh, load_row_info(a, sl.row));
 }
 
 template <int D, typename TIn, typename TOut>

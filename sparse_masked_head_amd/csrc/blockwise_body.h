@@ -281,8 +281,9 @@ struct TileList {
     const int32_t *fci, *pci;
     const uint64_t *bm;
     int f0, nF, p0, nT, nmax, S;
+    int c4[4];  // columns of the first four tiles (row_info)
     __device__ int col(int idx) const {
-        const int J = idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
+        const int J = idx < 4 ? c4[idx] : idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
         return (int)min((unsigned)J, (unsigned)nmax);
     }
     template <int D> __device__ int lim(int J) const {
@@ -293,11 +294,11 @@ struct TileList {
     }
 };
 
-// Workgroup work: encoding row `row` (outer-tile row I of its mask) of
-// head bh.
+// Workgroup work: encoding row `row` (outer-tile row I of its mask, summary
+// ri) of head bh.
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void blockwise_row(
-    const FwdArgs<TIn, TOut> &a, char *smem, int row, int I, int bh) {
+    const FwdArgs<TIn, TOut> &a, char *smem, int I, int bh, const RowInfo &ri) {
     using frag = typename Frag<TIn>::type;
     using L = Lds<D>;
     const size_t head = (size_t)bh * a.S * D;
@@ -313,10 +314,12 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     tl.bm = a.bm;
     tl.nmax = a.n - 1;
     tl.S = a.S;
-    tl.f0 = a.frp[row];
-    tl.nF = a.frp[row + 1] - tl.f0;
-    tl.p0 = a.prp[row];
-    tl.nT = tl.nF + a.prp[row + 1] - tl.p0;
+    tl.f0 = ri.f0;
+    tl.nF = ri.nF;
+    tl.p0 = ri.p0;
+    tl.nT = ri.nF + ri.nP;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tl.c4[k] = ri.c[k];
     const int nT = tl.nT, nF = tl.nF;
 
     // this lane's Q rows as the B operand: query r, d = 32s + 8g + 0..7

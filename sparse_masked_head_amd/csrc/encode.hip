@@ -19,7 +19,8 @@
 //   scan (one workgroup): exclusive prefix of the segments' tile counts,
 //     row pointers, statistics and the heavy-first row order;
 //   placement (one workgroup per segment): copy the segment's columns and
-//     words to their final places.
+//     words to their final places, and the columns among its row's first
+//     four stored tiles to the row's summary (row_info).
 // With at most kFusedMaxSegs segments and kFusedRows rows the scan runs as
 // one extra workgroup of the placement launch and each placement workgroup adds up the counts
 // before it itself (cheap at that size, and one launch fewer).  No
@@ -269,6 +270,7 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     __shared__ unsigned long long sh_u[4];
     __shared__ long long sh_l[4];
     __shared__ int sh_i[4];
+    __shared__ unsigned long long sh_tot;  // full << 32 | partial, all rows
     const int t = threadIdx.x;
     const int C = plan.per_row;
     if constexpr (kBins > 0) {
@@ -303,6 +305,13 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     for (int I = r_lo; I < r_hi; ++I) {
         enc.full_row_ptr[I] = (int32_t)(run >> 32);
         enc.part_row_ptr[I] = (int32_t)(run & 0xFFFFFFFFull);
+        {   // row summary: list starts and counts; columns past the row's
+            // last tile are -1 (the placement writes the others)
+            const int f = (int)(rowc[I] >> 16), p = (int)(rowc[I] & 0xFFFFu);
+            int4 *ri = reinterpret_cast<int4 *>(enc.row_info + 16 * (size_t)I);
+            ri[0] = make_int4((int)(run >> 32), f, (int)(run & 0xFFFFFFFFull), p);
+            for (int k = f + p; k < 4; ++k) enc.row_info[16 * (size_t)I + 4 + k] = -1;
+        }
         if (offsets) {
             unsigned long long r2 = run;
             for (int c = 0; c < C; ++c) {
@@ -318,6 +327,7 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
         enc.part_row_ptr[R] = (int32_t)(run & 0xFFFFFFFFull);
         enc.stats[1] = (int64_t)(run >> 32);
         enc.stats[2] = (int64_t)(run & 0xFFFFFFFFull);
+        sh_tot = run;
     }
     nnz = block_sum(nnz, sh_l);
     empty = block_sum(empty, sh_l);
@@ -367,6 +377,16 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
         enc.stats[3] = empty - (long long)G * (64LL * n - S);
         enc.stats[4] = mx;
     }
+    // the statistics the kernel choice reads, in every row's summary (one
+    // load per workgroup instead of a line that every workgroup waits on);
+    // sh_tot was set before the reductions' barriers
+    for (int I = t; I < R; I += 256) {
+        int4 *ri = reinterpret_cast<int4 *>(enc.row_info + 16 * (size_t)I + 8);
+        ri[0] = make_int4((int)(uint32_t)((unsigned long long)nnz & 0xFFFFFFFFull),
+                          (int)(nnz >> 32), (int)(sh_tot >> 32),
+                          (int)(sh_tot & 0xFFFFFFFFull));
+        ri[1] = make_int4(mx, 0, 0, 0);
+    }
 }
 
 __global__ __launch_bounds__(256) void enc_scan(int S, int n, int R, int G,
@@ -394,6 +414,12 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
     }
     const size_t base = (size_t)s * sg.cap;
     const uint64_t cnt = sg.cnt[s];
+    // the segment's place in its row (wavefront 0, lane = segment of the
+    // row; per_row <= 64): tiles of the row's segments before it, and the
+    // row's full tiles in all, so that the row's first four stored tiles
+    // can go to its row_info
+    const int row = s / plan.per_row, s0 = row * plan.per_row;
+    const uint64_t rcnt = t < plan.per_row ? sg.cnt[s0 + t] : 0;
     // columns (t < cap) and the first 256 16-byte chunks of the words
     const int colf = t < sg.cap ? sg.fcol[base + t] : 0;
     const int colp = t < sg.cap ? sg.pcol[base + t] : 0;
@@ -409,8 +435,26 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
     }
     const int pf = (int)(off >> 32), pp = (int)(off & 0xFFFFFFFFull);
     const int nf = (int)(cnt >> 32), np = (int)(cnt & 0xFFFFFFFFull);
-    if (t < nf) enc.full_col_idx[pf + t] = colf;
-    if (t < np) enc.part_col_idx[pp + t] = colp;
+    if (t < 64) {  // a segment holds at most 64 tiles: wavefront 0 places them
+        const bool before = s0 + t < s;
+        int bf = before ? (int)(rcnt >> 32) : 0;
+        int bp = before ? (int)(rcnt & 0xFFFFFFFFull) : 0;
+        int rf = (int)(rcnt >> 32);
+        for (int o = 32; o > 0; o >>= 1) {
+            bf += __shfl_xor(bf, o);
+            bp += __shfl_xor(bp, o);
+            rf += __shfl_xor(rf, o);
+        }
+        int32_t *ri = enc.row_info + 16 * (size_t)row + 4;
+        if (t < nf) {
+            enc.full_col_idx[pf + t] = colf;
+            if (bf + t < 4) ri[bf + t] = colf;
+        }
+        if (t < np) {
+            enc.part_col_idx[pp + t] = colp;
+            if (rf + bp + t < 4) ri[rf + bp + t] = colp;
+        }
+    }
     u4v *dst = reinterpret_cast<u4v *>(enc.part_bitmaps + (size_t)pp * 64);
     if (t < np * 32) dst[t] = w0;
     for (int e = t + 256; e < np * 32; e += 256) dst[e] = src[e];
@@ -437,8 +481,8 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
     const int n = (int)L.n, R = (int)L.rows;
     const int G = enc.mask_b * enc.mask_h;
     const SegPlan plan = L.plan;
-    if (plan.total <= 0 || plan.win > kMaxSegWin || n > kMaxN || R > kScanRows ||
-        (int64_t)G * n != L.rows)
+    if (plan.total <= 0 || plan.win > kMaxSegWin || plan.per_row > 64 ||
+        n > kMaxN || R > kScanRows || (int64_t)G * n != L.rows)
         return hipErrorInvalidValue;
     Seg sg;
     sg.cnt = (uint64_t *)(ws + L.seg_cnt);

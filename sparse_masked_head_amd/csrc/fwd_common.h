@@ -37,8 +37,28 @@ template <typename TIn, typename TOut> struct FwdArgs {
     const int32_t *frp, *fci, *prp, *pci;
     const uint64_t *bm;
     const int32_t *row_order;
+    const int32_t *info;  // row_info [R][8]
     const int64_t *stats;
 };
+
+// A row's summary (row_info): where its full and partial lists start, their
+// lengths, the columns of its first four stored tiles (full, then partial)
+// and the encoding's statistics.  One scalar load, so that a kernel has its
+// kernel choice and the K and V addresses of its first tiles one memory
+// round trip after it starts.
+struct RowInfo {
+    int f0, nF, p0, nP;
+    int c[4];
+    int64_t stats[5];  // nnz, n_full, n_partial, (unused), max_row_tiles
+};
+template <typename TIn, typename TOut>
+__device__ inline RowInfo load_row_info(const FwdArgs<TIn, TOut> &a, int row) {
+    const int4 *p = reinterpret_cast<const int4 *>(a.info + 16 * (size_t)row);
+    const int4 h = p[0], c = p[1], s = p[2], m = p[3];
+    return RowInfo{h.x, h.y, h.z, h.w, {c.x, c.y, c.z, c.w},
+                   {(int64_t)(((uint64_t)(uint32_t)s.y << 32) | (uint32_t)s.x),
+                    s.z, s.w, 0, m.x}};
+}
 
 template <typename TIn, typename TOut>
 inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
@@ -66,6 +86,7 @@ inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
     a.pci = enc.part_col_idx;
     a.bm = enc.part_bitmaps;
     a.row_order = enc.row_order;
+    a.info = enc.row_info;
     a.stats = enc.stats;
     return a;
 }
@@ -256,8 +277,8 @@ inline long long resident_workgroups(Kernel kern, int lds) {
 // The launch's kernel choice when decided on the device: 1 row-wise,
 // 2 block-wise (same function as smh_select_kernel on the host).
 template <int D, typename TIn, typename TOut>
-__device__ inline int device_choice(const FwdArgs<TIn, TOut> &a) {
-    return select_on_device(a.stats, a.U, a.R, D, is_bf16<TIn>());
+__device__ inline int device_choice(const FwdArgs<TIn, TOut> &a, const RowInfo &ri) {
+    return select_on_device(ri.stats, a.U, a.R, D, is_bf16<TIn>());
 }
 
 }  // namespace smh

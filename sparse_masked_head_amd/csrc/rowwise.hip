@@ -19,8 +19,8 @@ __global__ __launch_bounds__(256) void rowwise_fwd(FwdArgs<TIn, TOut> a,
     const int oi = (int)(gw / per_oi);
     const int rem = (int)(gw - (long long)oi * per_oi);
     const Slot sl = slot_of(a, oi, rem >> 3);
-    rowwise_group<D, TIn, TOut>(a, lds + w * RowLds<D>::BYTES, sl.row, sl.I,
-                                rem & 7, sl.bh);
+    rowwise_group<D, TIn, TOut>(a, lds + w * RowLds<D>::BYTES, sl.I, rem & 7,
+                                sl.bh, load_row_info(a, sl.row));
 }
 
 template <int D, typename TIn, typename TOut>

@@ -181,12 +181,13 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
     }
 }
 
-// Wavefront work: inner-tile row ir of encoding row `row` (outer-tile row I
-// of its mask) of head bh.  Query rows past S (S cuts the last outer tile)
-// see no key, read zeros for Q and are not stored.
+// Wavefront work: inner-tile row ir of an encoding row (outer-tile row I
+// of its mask, summary ri) of head bh.  Query rows past S (S cuts the last
+// outer tile) see no key, read zeros for Q and are not stored.
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void rowwise_group(
-    const FwdArgs<TIn, TOut> &a, char *slice, int row, int I, int ir, int bh) {
+    const FwdArgs<TIn, TOut> &a, char *slice, int I, int ir, int bh,
+    const RowInfo &ri) {
     constexpr int R = kRowsPerWave;
     constexpr int E = RwState<D>::E;
     constexpr int CAP = RowLds<D>::CAP;
@@ -206,8 +207,7 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
             dst[e] = row0 + e / (D / 8) < a.S ? src[e] : u4_t{0, 0, 0, 0};
     }
 
-    const int f0 = a.frp[row], nF = a.frp[row + 1] - f0;
-    const int p0 = a.prp[row], nP = a.prp[row + 1] - p0;
+    const int f0 = ri.f0, nF = ri.nF, p0 = ri.p0, nP = ri.nP;
     const int nT = nF + nP;
 
     RwState<D> st;

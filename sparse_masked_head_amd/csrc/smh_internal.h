@@ -44,7 +44,7 @@ struct EncLayout {
     int64_t rows;  // outer-tile rows of the stack (G * n)
     SegPlan plan;
     size_t full_row_ptr, part_row_ptr, full_col_idx, part_col_idx,
-        part_bitmaps, stats, row_order;
+        part_bitmaps, stats, row_order, row_info;
     // per segment: tile counts (full << 32 | partial), exclusive offsets
     // (same packing), valid pairs, covered query rows (bit 8k + r = strip
     // row 8k + r), and its tiles' columns and partial-tile words (room for
@@ -78,6 +78,7 @@ inline EncLayout enc_layout(int32_t S, int64_t G) {
     L.part_bitmaps = take(sizeof(uint64_t) * 64 * cap);
     L.stats = take(sizeof(int64_t) * 8);  // nnz, n_full, n_partial, empty rows, max row tiles
     L.row_order = take(sizeof(int32_t) * rows);
+    L.row_info = take(sizeof(int32_t) * 16 * rows);
     const size_t T = (size_t)L.plan.total;
     L.seg_cap = (size_t)L.plan.win * kWin;
     L.seg_cnt = take(sizeof(uint64_t) * T);

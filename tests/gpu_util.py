@@ -32,6 +32,30 @@ def assert_same_encoding(got, ref):
     assert bad.size == 0, f"bitmaps of partial tiles {bad[:8]} differ"
     for key in ("nnz", "n_full", "n_partial", "n_empty_rows"):
         assert got[key] == ref[key], key
+    if "row_info" in got:
+        assert np.array_equal(got["row_info"], expected_row_info(ref)), \
+            "row_info"
+
+
+def expected_row_info(ref):
+    """Per row: list starts and counts, then its first four stored tiles'
+    columns (full tiles, then partial), -1 past the row's last tile, then
+    the statistics (nnz low and high words, n_full, n_partial,
+    max_row_tiles) and three zeros."""
+    frp, prp = ref["full_row_ptr"], ref["part_row_ptr"]
+    R = len(frp) - 1
+    out = np.full((R, 16), -1, np.int32)
+    cnt = np.diff(frp) + np.diff(prp)
+    nnz = int(ref["nnz"])
+    stats = [nnz & 0xFFFFFFFF, nnz >> 32, ref["n_full"], ref["n_partial"],
+             int(cnt.max()) if R else 0, 0, 0, 0]
+    for r in range(R):
+        cols = list(ref["full_col_idx"][frp[r]:frp[r + 1]]) + \
+            list(ref["part_col_idx"][prp[r]:prp[r + 1]])
+        out[r, :4] = [frp[r], frp[r + 1] - frp[r], prp[r], prp[r + 1] - prp[r]]
+        out[r, 4:8] = (cols[:4] + [-1] * 4)[:4]
+        out[r, 8:16] = np.array(stats, np.int64).astype(np.uint32).view(np.int32)
+    return out
 
 
 def expected_row_order(ref):

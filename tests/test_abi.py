@@ -161,7 +161,8 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, o=ctypes.c_void_p(1 << 30), B=1, H=1, S=128,
     e = L.MaskEnc()
     e.S, e.n_ot, e.mask_b, e.mask_h = enc_S, -(-enc_S // 64), mb, mh
     for name in ("full_row_ptr", "full_col_idx", "part_row_ptr",
-                 "part_col_idx", "part_bitmaps", "stats", "row_order"):
+                 "part_col_idx", "part_bitmaps", "stats", "row_order",
+                 "row_info"):
         setattr(e, name, 1 << 28)
     return L.lib().smh_sparse_mha_fwd(
         q, k, v, o, B, H, S, d, in_dt, out_dt, scale,

@@ -205,26 +205,26 @@ def _stats_candidates(S):
 @pytest.mark.parametrize("d,dt", [(64, "f16"), (128, "bf16")])
 def test_fused_kernel_both_branches(d, dt):
     """The single-launch SMH_AUTO kernel runs whichever algorithm the device
-    model picks.  The statistics words in the workspace are rewritten (they
-    feed only the decision) to steer it into each branch; each branch's
-    output is bitwise the forced kernel's."""
+    model picks.  The statistics copies in every row's summary (row_info
+    words 8..12, which feed only the decision) are rewritten to steer it
+    into each branch; each branch's output is bitwise the forced kernel's."""
     dev = need_gpu()
     S, B, H = 512, 1, 3   # long enough rows for the model to pick each kernel
     mask = mask_family("random", S, seed=31, p=0.08)
     q, k, v = make_qkv(B, H, S, d, dt, seed=31)
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
     enc = smh.encode_mask(torch.from_numpy(mask).to(dev))
-    off = enc.enc.stats - enc.workspace.data_ptr()
-    words = enc.workspace[off:off + 40].view(torch.int64)
+    info = enc.arrays()["row_info"]          # [rows, 16] int32 view
     seen = set()
     for cand in _stats_candidates(S):
         which = smh.select_kernel(cand, B, H, d, qd.dtype)
         if which in seen:
             continue
         seen.add(which)
-        words.copy_(torch.tensor([cand["nnz"], cand["n_full"],
-                                  cand["n_partial"], 0,
-                                  cand["max_row_tiles"]], dtype=torch.int64))
+        nnz = cand["nnz"]
+        info[:, 8:13] = torch.tensor(
+            [nnz & 0xFFFFFFFF, nnz >> 32, cand["n_full"], cand["n_partial"],
+             cand["max_row_tiles"]], dtype=torch.int64).to(torch.int32)
         a = smh.sparse_mha_fwd(qd, kd, vd, enc, kernel="auto",
                                out_dtype=torch.float32)
         b = smh.sparse_mha_fwd(qd, kd, vd, enc, kernel=which,
