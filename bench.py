@@ -64,6 +64,13 @@ def parse():
                     help="shared: one mask for every (batch, head); batch: "
                          "one mask per sequence (padding to a seeded length "
                          "in [S/2, S])")
+    ap.add_argument("--mask-source", default="dense",
+                    choices=["dense", "pattern"],
+                    help="dense: encode the stored [S, S] mask; pattern: "
+                         "encode from the workload's pattern (no dense mask "
+                         "on the device; BigBird and long_random then draw "
+                         "their random elements from the pattern's "
+                         "generator)")
     ap.add_argument("--out-dtype", default="auto",
                     choices=["auto", "in", "f32"],
                     help="output type; auto = input type for fp16, f32 for "
@@ -225,6 +232,17 @@ def workload(args):
         cfg = dataclasses.replace(
             cfg, S=args.seq_len, name=f"{cfg.name}-S{args.seq_len}",
             desc=f"{cfg.desc}; S changed to {args.seq_len}")
+    if args.mask_source == "pattern":
+        from oracle.pattern import pattern_mask   # the mask, for FLOPs and the CPU leg
+        from workloads import pattern_of
+        if args.mask_stack != "shared":
+            raise SystemExit("--mask-source pattern takes one shared mask")
+        pat = pattern_of(cfg)
+        mask = pattern_mask(cfg.S, **pat)
+        cfg = dataclasses.replace(
+            cfg, name=f"{cfg.name}-pattern",
+            desc=f"{cfg.desc}; encoded from its pattern")
+        return cfg, mask
     mask = make_mask(cfg)
     if args.mask_stack == "batch":
         mask = padding_stack(mask, cfg.B, cfg.cid)
@@ -259,7 +277,8 @@ def main():
     cfg, mask = workload(args)
     qkv = make_qkv(cfg.B, cfg.H, cfg.S, cfg.d, cfg.dtype, seed=cfg.cid)
     q, k, v = (x.to(dev) for x in qkv)
-    mask_d = torch.from_numpy(mask).to(dev)
+    mask_d = torch.from_numpy(mask).to(dev) \
+        if args.mask_source == "dense" else None
     out_dt = {"auto": torch.float32 if cfg.dtype == "bf16" else q.dtype,
               "in": q.dtype, "f32": torch.float32}[args.out_dtype]
     mb, mh = (1, 1) if mask.ndim == 2 else mask.shape[:2]
@@ -270,18 +289,30 @@ def main():
 
     # the selector's statistics and choice, read once for the report (the
     # timed steps decide on the device from the same statistics)
-    enc0 = smh.encode_mask(mask_d, workspace=ws)
+    if args.mask_source == "pattern":
+        from workloads import pattern_of
+        pat = dict(pattern_of(cfg))
+        if pat.get("blocks") is not None:
+            pat["blocks"] = torch.from_numpy(pat["blocks"]).to(dev)
+
+        def encode():
+            return smh.encode_pattern(cfg.S, device=dev, workspace=ws, **pat)
+    else:
+        def encode():
+            return smh.encode_mask(mask_d, workspace=ws)
+
+    enc0 = encode()
     st = smh.mask_stats_get(enc0)
     which = args.kernel if args.kernel != "auto" else smh.select_kernel(
         st, cfg.B, cfg.H, cfg.d, q.dtype)
 
     def step():
-        enc = smh.encode_mask(mask_d, workspace=ws)
+        enc = encode()
         smh.sparse_mha_fwd(q, k, v, enc, kernel=args.kernel,
                            out_dtype=out_dt, out=out)
 
     def encode_only():
-        smh.encode_mask(mask_d, workspace=ws)
+        encode()
 
     def fwd_only():
         smh.sparse_mha_fwd(q, k, v, enc0, kernel=args.kernel,

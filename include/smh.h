@@ -176,6 +176,42 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
                             size_t ws_bytes, smh_mask_enc *enc_out,
                             void *stream);
 
+/* A mask described by its pattern instead of stored ([EXP] storage-format
+ * items: the encoding is built without the dense S x S mask).  Element
+ * (i, j), i, j < S, is valid iff
+ *     (causal == 0 or j <= i)  and  (
+ *         |i - j| <= window                       (window >= 0; -1: no band)
+ *      or i < global_rows  or  j < global_cols    (global tokens)
+ *      or blocks[i/64][j/64] == 1                 (a listed 64x64 block)
+ *      or blocks[i/64][j/64] not in {0, 1} and u(i, j) < keep16
+ *      or blocks[i/64][j/64] == 0 (or no map) and u(i, j) < rand16 )
+ * with keep16 = floor(block_keep * 65536), rand16 = floor(random_p * 65536)
+ * (float arithmetic) and u(i, j) the element's 16-bit draw: with
+ * e = i * S + j, bits 16 (e % 4) .. 16 (e % 4) + 15 of output number e / 4
+ * (from 0) of SplitMix64 seeded with `seed` (Steele, Lea and Flood, OOPSLA
+ * 2014: output k = mix(seed + (k + 1) * 0x9E3779B97F4A7C15)).  With
+ * block_keep == 1 and random_p == 0 the pattern has no random part. */
+typedef struct {
+    int32_t causal;        /* nonzero: keys j <= i only */
+    int32_t window;        /* band half-width, >= 0, or -1 for no band */
+    int32_t global_rows;   /* >= 0 */
+    int32_t global_cols;   /* >= 0 */
+    const uint8_t *blocks; /* device [ceil(S/64)][ceil(S/64)] block map, or NULL */
+    float block_keep;      /* in [0, 1] */
+    float random_p;        /* in [0, 1] */
+    uint64_t seed;
+} smh_pattern;
+
+/* Encode the mask a pattern describes.  Same launches, output, workspace
+ * (smh_encode_workspace_bytes(S)) and errors as smh_encode_mask, with
+ * the strip pass computing each inner-tile row from the pattern instead of
+ * reading mask bytes; the result equals smh_encode_mask of the dense mask
+ * the pattern describes.  SMH_EINVAL for a NULL pattern, window < -1,
+ * negative global counts or probabilities outside [0, 1]. */
+smh_status smh_encode_pattern(const smh_pattern *pattern, int32_t S,
+                              void *workspace, size_t ws_bytes,
+                              smh_mask_enc *enc_out, void *stream);
+
 /* Copy the encoding statistics to the host.  Synchronises `stream`. */
 smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
                               void *stream);

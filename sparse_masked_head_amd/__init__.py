@@ -19,9 +19,10 @@ import torch
 
 from ._lib import (SMH_AUTO, SMH_BF16, SMH_BLOCKWISE, SMH_F16, SMH_F32,
                    SMH_MAX_S, SMH_OK, SMH_ROWWISE, MaskEnc, MaskStats,
-                   SmhError, check, lib, status_string)
+                   Pattern, SmhError, check, lib, status_string)
 
-__all__ = ["encode_mask", "encode_workspace_bytes", "mask_stats_get",
+__all__ = ["encode_mask", "encode_pattern", "encode_workspace_bytes",
+           "mask_stats_get",
            "select_kernel", "select_costs", "sparse_mha_fwd", "version",
            "MaskEncoding", "SmhError", "KERNELS"]
 
@@ -121,6 +122,44 @@ def encode_mask(mask, workspace=None):
         ctypes.byref(enc), _stream(mask.device))
     check(st, "smh_encode_masks")
     return MaskEncoding(workspace, enc, S, mb, mh)
+
+
+def encode_pattern(S, causal=False, window=-1, global_rows=0, global_cols=0,
+                   blocks=None, block_keep=1.0, random_p=0.0, seed=0,
+                   device=None, workspace=None):
+    """Encode the mask a pattern describes (include/smh.h, smh_pattern),
+    without a dense mask: causal limit, band |i - j| <= window, global rows
+    and columns, a [n_ot, n_ot] uint8 device block map (1: block valid,
+    other nonzero: its elements kept with probability block_keep), and
+    other elements valid with probability random_p (SplitMix64 draws from
+    `seed`)."""
+    S = int(S)
+    if blocks is not None:
+        n = -(-S // 64)
+        if blocks.dtype != torch.uint8 or tuple(blocks.shape) != (n, n) or \
+                not blocks.is_cuda:
+            raise ValueError(f"blocks must be a device uint8 [{n}, {n}] map")
+        blocks = blocks.contiguous()
+        device = blocks.device
+    device = torch.device("cuda", torch.cuda.current_device()) \
+        if device is None else torch.device(device)
+    pat = Pattern(int(bool(causal)), int(window), int(global_rows),
+                  int(global_cols),
+                  ctypes.c_void_p(blocks.data_ptr()) if blocks is not None
+                  else None, float(block_keep), float(random_p),
+                  int(seed) & ((1 << 64) - 1))
+    nbytes = encode_workspace_bytes(S)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8,
+                                device=device)
+    enc = MaskEnc()
+    check(lib().smh_encode_pattern(
+        ctypes.byref(pat), S, ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel(), ctypes.byref(enc), _stream(device)),
+        "smh_encode_pattern")
+    enc_obj = MaskEncoding(workspace, enc, S)
+    enc_obj.blocks = blocks          # the map must outlive the launches
+    return enc_obj
 
 
 def mask_stats_get(enc):

@@ -13,7 +13,8 @@ SMH_MAX_ENC_ROWS = 8192
 
 # every exported name of include/smh.h
 EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_masks_workspace_bytes",
-           "smh_encode_mask", "smh_encode_masks", "smh_mask_stats_get",
+           "smh_encode_mask", "smh_encode_masks", "smh_encode_pattern",
+           "smh_mask_stats_get",
            "smh_select_kernel", "smh_select_costs", "smh_sparse_mha_fwd",
            "smh_status_string", "smh_version")
 
@@ -29,6 +30,14 @@ class MaskEnc(ctypes.Structure):
                 ("stats", ctypes.c_void_p),
                 ("row_order", ctypes.c_void_p),
                 ("row_info", ctypes.c_void_p)]
+
+
+class Pattern(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("global_rows", ctypes.c_int32),
+                ("global_cols", ctypes.c_int32),
+                ("blocks", ctypes.c_void_p), ("block_keep", ctypes.c_float),
+                ("random_p", ctypes.c_float), ("seed", ctypes.c_uint64)]
 
 
 class MaskStats(ctypes.Structure):
@@ -71,6 +80,9 @@ def lib():
         L.smh_encode_masks.argtypes = [p, i32, i32, i32, p, sz,
                                        ctypes.POINTER(MaskEnc), p]
         L.smh_encode_masks.restype = ctypes.c_int
+        L.smh_encode_pattern.argtypes = [ctypes.POINTER(Pattern), i32, p, sz,
+                                         ctypes.POINTER(MaskEnc), p]
+        L.smh_encode_pattern.restype = ctypes.c_int
         L.smh_mask_stats_get.argtypes = [ctypes.POINTER(MaskEnc),
                                          ctypes.POINTER(MaskStats), p]
         L.smh_mask_stats_get.restype = ctypes.c_int

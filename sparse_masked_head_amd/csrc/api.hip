@@ -57,6 +57,23 @@ smh_status check_select(const smh_mask_stats *st, int32_t B, int32_t H,
     return SMH_OK;
 }
 
+// The encoding's pointers into workspace `ws` laid out as L.
+void fill_enc(smh_mask_enc &e, char *ws, const EncLayout &L, int32_t S,
+              int32_t mask_b, int32_t mask_h) {
+    e.S = S;
+    e.n_ot = (int32_t)L.n;
+    e.mask_b = mask_b;
+    e.mask_h = mask_h;
+    e.full_row_ptr = (int32_t *)(ws + L.full_row_ptr);
+    e.full_col_idx = (int32_t *)(ws + L.full_col_idx);
+    e.part_row_ptr = (int32_t *)(ws + L.part_row_ptr);
+    e.part_col_idx = (int32_t *)(ws + L.part_col_idx);
+    e.part_bitmaps = (uint64_t *)(ws + L.part_bitmaps);
+    e.stats = (int64_t *)(ws + L.stats);
+    e.row_order = (int32_t *)(ws + L.row_order);
+    e.row_info = (int32_t *)(ws + L.row_info);
+}
+
 // (batch, head) pairs that share each mask of the stack.
 int64_t heads_per_mask(const smh_mask_stats *st, int32_t B, int32_t H) {
     return (int64_t)(st->mask_b > 1 ? 1 : B) * (st->mask_h > 1 ? 1 : H);
@@ -105,19 +122,37 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
             return SMH_EINVAL;
         char *ws = (char *)workspace;
         smh_mask_enc e;
-        e.S = S;
-        e.n_ot = (int32_t)L.n;
-        e.mask_b = mask_b;
-        e.mask_h = mask_h;
-        e.full_row_ptr = (int32_t *)(ws + L.full_row_ptr);
-        e.full_col_idx = (int32_t *)(ws + L.full_col_idx);
-        e.part_row_ptr = (int32_t *)(ws + L.part_row_ptr);
-        e.part_col_idx = (int32_t *)(ws + L.part_col_idx);
-        e.part_bitmaps = (uint64_t *)(ws + L.part_bitmaps);
-        e.stats = (int64_t *)(ws + L.stats);
-        e.row_order = (int32_t *)(ws + L.row_order);
-        e.row_info = (int32_t *)(ws + L.row_info);
+        fill_enc(e, ws, L, S, mask_b, mask_h);
         if (launch_encode(masks, S, ws, L, e, (hipStream_t)stream) !=
+            hipSuccess)
+            return SMH_EHIP;
+        *enc_out = e;
+        return SMH_OK;
+    } catch (...) {
+        return SMH_EHIP;
+    }
+}
+
+smh_status smh_encode_pattern(const smh_pattern *pat, int32_t S,
+                              void *workspace, size_t ws_bytes,
+                              smh_mask_enc *enc_out, void *stream) {
+    try {
+        if (!pat || stack_rows(1, 1, S) < 0) return SMH_EINVAL;
+        if (!enc_out || !workspace || !aligned(workspace, 256)) return SMH_EINVAL;
+        if (pat->window < -1 || pat->global_rows < 0 || pat->global_cols < 0)
+            return SMH_EINVAL;
+        if (!(pat->block_keep >= 0.f && pat->block_keep <= 1.f) ||
+            !(pat->random_p >= 0.f && pat->random_p <= 1.f))
+            return SMH_EINVAL;
+        const EncLayout L = enc_layout(S, 1);
+        if (ws_bytes < L.total) return SMH_ENOSPACE;
+        const size_t n = (size_t)L.n;
+        if (pat->blocks && overlaps(pat->blocks, n * n, workspace, L.total))
+            return SMH_EINVAL;
+        char *ws = (char *)workspace;
+        smh_mask_enc e;
+        fill_enc(e, ws, L, S, 1, 1);
+        if (launch_encode_pattern(*pat, S, ws, L, e, (hipStream_t)stream) !=
             hipSuccess)
             return SMH_EHIP;
         *enc_out = e;

@@ -27,6 +27,8 @@
 // workgroup ever waits for another.  Every output is a pure function of
 // the mask: the result is deterministic and equals appending tiles row by
 // row, column by column.
+#include <math.h>
+
 #include "smh_internal.h"
 
 namespace smh {
@@ -140,6 +142,44 @@ struct Seg {  // per-segment scratch (EncLayout)
     int cap;  // tiles of room per segment
 };
 
+// Shared tail of the strip passes: classify the segment's tiles (wavefront
+// 0, lane = tile), write its columns, counts, valid pairs and covered rows
+// (any64, read in lane 0 of wavefront 0: bit r = query row r of the strip),
+// then its partial-tile words (one wavefront per tile).  wsum[l][0..3] add
+// up to tile l's valid elements.
+__device__ void strip_classify(int s, int nwin, int w0, int n, Seg sg,
+                               uint64_t (*lw)[64], int (*wsum)[4], int *tkind,
+                               uint64_t any64) {
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    if (w == 0) {
+        const int wi = lane >> 3, J = kWin * (w0 + wi) + (lane & 7);
+        const bool valid = wi < nwin && J < n;
+        const int cnt = valid ? wsum[lane][0] + wsum[lane][1] + wsum[lane][2] +
+                                    wsum[lane][3]
+                              : 0;
+        const bool full = cnt == 64 * 64, part = cnt > 0 && !full;
+        const uint64_t mf = __ballot(full), mp = __ballot(part);
+        const uint64_t below = (1ull << lane) - 1;
+        const int rf = __popcll(mf & below), rp = __popcll(mp & below);
+        tkind[lane] = full ? (1 << 17) | rf : part ? (1 << 16) | rp : 0;
+        if (full) sg.fcol[(size_t)s * sg.cap + rf] = J;
+        if (part) sg.pcol[(size_t)s * sg.cap + rp] = J;
+        long long nz = cnt;
+        for (int off = 32; off > 0; off >>= 1) nz += __shfl_xor(nz, off);
+        if (lane == 0) {
+            sg.cnt[s] = ((uint64_t)__popcll(mf) << 32) | (uint64_t)__popcll(mp);
+            sg.nnz[s] = (uint64_t)nz;
+            sg.any[s] = any64;
+        }
+    }
+    __syncthreads();
+    for (int l = w; l < kWin * nwin; l += 4) {
+        const int k = tkind[l];
+        if (k & (1 << 16))
+            sg.words[((size_t)s * sg.cap + (k & 0xFFFF)) * 64 + lane] = lw[l][lane];
+    }
+}
+
 template <int kMode>
 __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mask,
                                                  int S, int n, SegPlan plan, Seg sg) {
@@ -196,40 +236,134 @@ __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mas
         if (c == 0) rows_any[r0] = a;
     }
     __syncthreads();
+    uint64_t any64 = 0;  // bit 8k + r: query row 8k + r of the strip
+    if (t == 0)
+        for (int r = 0; r < 8; ++r)
+            for (int k = 0; k < 8; ++k)
+                any64 |= (uint64_t)((rows_any[r] >> k) & 1u) << (8 * k + r);
+    strip_classify(s, nwin, w0, n, sg, lw, wsum, tkind, any64);
+}
 
-    // classify the tiles (wavefront 0, lane = tile), write columns and counts
-    if (w == 0) {
-        const int wi = lane >> 3, J = kWin * (w0 + wi) + (lane & 7);
-        const bool valid = wi < nwin && J < n;
-        const int cnt = valid ? wsum[lane][0] + wsum[lane][1] + wsum[lane][2] +
-                                    wsum[lane][3]
-                              : 0;
-        const bool full = cnt == 64 * 64, part = cnt > 0 && !full;
-        const uint64_t mf = __ballot(full), mp = __ballot(part);
-        const uint64_t below = (1ull << lane) - 1;
-        const int rf = __popcll(mf & below), rp = __popcll(mp & below);
-        tkind[lane] = full ? (1 << 17) | rf : part ? (1 << 16) | rp : 0;
-        if (full) sg.fcol[(size_t)s * sg.cap + rf] = J;
-        if (part) sg.pcol[(size_t)s * sg.cap + rp] = J;
-        long long nz = cnt;
-        for (int off = 32; off > 0; off >>= 1) nz += __shfl_xor(nz, off);
-        if (lane == 0) {
-            uint64_t any64 = 0;  // bit 8k + r: query row 8k + r of the strip
-            for (int r = 0; r < 8; ++r)
-                for (int k = 0; k < 8; ++k)
-                    any64 |= (uint64_t)((rows_any[r] >> k) & 1u) << (8 * k + r);
-            sg.cnt[s] = ((uint64_t)__popcll(mf) << 32) | (uint64_t)__popcll(mp);
-            sg.nnz[s] = (uint64_t)nz;
-            sg.any[s] = any64;
+// ---- masks described by a pattern (smh_pattern) instead of stored ----
+
+struct Pattern {
+    int causal, window, grow, gcol;
+    const uint8_t *blocks;    // [n][n] block map or null
+    uint32_t keep16, rand16;  // probabilities as thresholds out of 2^16
+    uint64_t seed;
+};
+
+// Bits lo .. hi of a 64-bit word (0 <= lo <= hi <= 63).
+__device__ inline uint64_t bit_range(int lo, int hi) {
+    return (~0ull >> (63 - hi)) & (~0ull << lo);
+}
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): output number k (from 0) of the stream seeded
+// with `seed` is the mix function applied to the state seed + (k + 1) *
+// gamma; consecutive outputs step the state by gamma.
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+__device__ inline uint64_t splitmix64_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Bit c (c < 64) set iff element e0 + c of the row-major S x S mask draws
+// below thr: element e draws bits 16 (e % 4) .. 16 (e % 4) + 15 of
+// SplitMix64 output e / 4.  The 17 outputs from e0 / 4 on cover elements
+// 4 (e0 / 4) .. +67; their 68 decisions are built four at a time (one
+// nibble per output) and shifted into place once.
+__device__ inline uint64_t draw_bits(uint64_t seed, uint64_t e0, uint32_t thr) {
+    if (thr == 0) return 0;
+    if (thr >= 65536u) return ~0ull;
+    const uint64_t g0 = e0 >> 2;
+    const int sh = (int)(e0 & 3);
+    uint64_t lo = 0;  // decisions of elements 4 g0 .. 4 g0 + 63
+    uint32_t hi = 0;  // elements 4 g0 + 64 .. + 67
+    uint64_t state = seed + (g0 + 1) * kGamma;  // of output g0
+#pragma unroll
+    for (int q = 0; q < 17; ++q, state += kGamma) {
+        const uint64_t x = splitmix64_mix(state);
+        const uint32_t a = (uint32_t)x, b = (uint32_t)(x >> 32);
+        const uint32_t nib = (uint32_t)((a & 0xFFFFu) < thr) |
+                             ((uint32_t)((a >> 16) < thr) << 1) |
+                             ((uint32_t)((b & 0xFFFFu) < thr) << 2) |
+                             ((uint32_t)((b >> 16) < thr) << 3);
+        if (q < 16)
+            lo |= (uint64_t)nib << (4 * q);
+        else
+            hi = nib;
+    }
+    return sh ? (lo >> sh) | ((uint64_t)hi << (64 - sh)) : lo;
+}
+
+// Row i of the pattern's mask over columns 64J .. 64J+63 (bit c = column
+// 64J + c).  Valid: inside S x S, j <= i when causal, and any of: the band
+// |i - j| <= window, a global row or column, a listed block (map value 1:
+// every element; other nonzero values: elements drawn with keep16), else
+// an element drawn with rand16.
+__device__ inline uint64_t pattern_row_bits(const Pattern &p, int S, int n,
+                                            int i, int J) {
+    const int c0 = 64 * J;
+    if (i >= S || c0 >= S) return 0;
+    uint64_t lim = S - c0 >= 64 ? ~0ull : bit_range(0, S - c0 - 1);
+    if (p.causal) {
+        if (i < c0) return 0;
+        if (i - c0 < 63) lim &= bit_range(0, i - c0);
+    }
+    if (i < p.grow) return lim;
+    uint64_t m = 0;
+    if (p.window >= 0) {
+        const long long lo = max((long long)i - p.window, (long long)c0);
+        const long long hi = min((long long)i + p.window, (long long)c0 + 63);
+        if (lo <= hi) m |= bit_range((int)(lo - c0), (int)(hi - c0));
+    }
+    if (p.gcol > c0) m |= p.gcol - c0 >= 64 ? ~0ull : bit_range(0, p.gcol - c0 - 1);
+    const int blk = p.blocks ? p.blocks[(size_t)(i >> 6) * n + J] : 0;
+    if (blk == 1) return lim;
+    if ((~m & lim) != 0)
+        m |= draw_bits(p.seed, (uint64_t)i * S + c0, blk ? p.keep16 : p.rand16);
+    return m & lim;
+}
+
+// Strip pass of a pattern: the same segments and outputs as enc_strip, with
+// the inner-tile words computed instead of loaded.  Lane = query row of the
+// strip; wavefront w takes tiles w and w + 4 of each window.
+__global__ __launch_bounds__(256) void enc_pattern_strip(Pattern p, int S, int n,
+                                                         SegPlan plan, Seg sg) {
+    __shared__ uint64_t lw[kMaxSegTiles][64];
+    __shared__ int wsum[kMaxSegTiles][4];
+    __shared__ int tkind[kMaxSegTiles];
+    __shared__ uint64_t wany[4];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int s = blockIdx.x;
+    const int I = s / plan.per_row, seg_c = s - I * plan.per_row;
+    const int nw = (n + kWin - 1) / kWin;
+    const int w0 = seg_c * plan.win;
+    const int nwin = min(plan.win, nw - w0);
+    const int i = 64 * I + lane, ir = lane >> 3, r = lane & 7;
+    uint8_t *wb = reinterpret_cast<uint8_t *>(&lw[0][0]);
+    bool any = false;
+    for (int wi = 0; wi < nwin; ++wi) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int jj = w + 4 * h, J = kWin * (w0 + wi) + jj;
+            const uint64_t m = J < n ? pattern_row_bits(p, S, n, i, J) : 0;
+            any |= m != 0;
+            uint8_t *tb = wb + (size_t)(kWin * wi + jj) * 512;
+#pragma unroll
+            for (int ic = 0; ic < 8; ++ic) tb[(ir * 8 + ic) * 8 + r] = (uint8_t)(m >> (8 * ic));
+            int cnt = __popcll(m);
+            for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+            if (lane < 4) wsum[kWin * wi + jj][lane] = lane == 0 ? cnt : 0;
         }
     }
+    const uint64_t a = __ballot(any);
+    if (lane == 0) wany[w] = a;
     __syncthreads();
-    // partial-tile words, one wavefront per tile
-    for (int l = w; l < kWin * nwin; l += 4) {
-        const int k = tkind[l];
-        if (k & (1 << 16))
-            sg.words[((size_t)s * sg.cap + (k & 0xFFFF)) * 64 + lane] = lw[l][lane];
-    }
+    strip_classify(s, nwin, w0, n, sg, lw, wsum, tkind,
+                   wany[0] | wany[1] | wany[2] | wany[3]);
 }
 
 // Exclusive scan over the 256 threads of a workgroup.
@@ -471,9 +605,14 @@ __global__ void enc_empty(smh_mask_enc enc) {
 
 }  // namespace
 
-hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
-                         const EncLayout &L, const smh_mask_enc &enc,
-                         hipStream_t stream) {
+namespace {
+
+// The launches of an encode: strip pass (`strip` enqueues it on the
+// segments), then the scan and placement.
+template <typename StripLaunch>
+hipError_t encode_launches(StripLaunch strip, int32_t S, char *ws,
+                           const EncLayout &L, const smh_mask_enc &enc,
+                           hipStream_t stream) {
     if (S == 0) {
         hipLaunchKernelGGL(enc_empty, dim3(1), dim3(64), 0, stream, enc);
         return hipGetLastError();
@@ -493,15 +632,7 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
     sg.pcol = (int32_t *)(ws + L.seg_pcol);
     sg.words = (uint64_t *)(ws + L.seg_words);
     sg.cap = (int)L.seg_cap;
-    if (S % 64 == 0)
-        hipLaunchKernelGGL(enc_strip<kAligned64>, dim3(plan.total), dim3(256), 0,
-                           stream, mask, S, n, plan, sg);
-    else if (S % 16 == 0)
-        hipLaunchKernelGGL(enc_strip<kAligned16>, dim3(plan.total), dim3(256), 0,
-                           stream, mask, S, n, plan, sg);
-    else
-        hipLaunchKernelGGL(enc_strip<kDwords>, dim3(plan.total), dim3(256), 0,
-                           stream, mask, S, n, plan, sg);
+    strip(n, plan, sg);
     if (plan.total <= kFusedMaxSegs && R <= kFusedRows) {
         hipLaunchKernelGGL(enc_place<true>, dim3(plan.total + 1), dim3(256), 0,
                            stream, S, n, R, G, plan, sg, enc);
@@ -512,6 +643,44 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
                            stream, S, n, R, G, plan, sg, enc);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
+                         const EncLayout &L, const smh_mask_enc &enc,
+                         hipStream_t stream) {
+    auto strip = [&](int n, SegPlan plan, Seg sg) {
+        if (S % 64 == 0)
+            hipLaunchKernelGGL(enc_strip<kAligned64>, dim3(plan.total), dim3(256),
+                               0, stream, mask, S, n, plan, sg);
+        else if (S % 16 == 0)
+            hipLaunchKernelGGL(enc_strip<kAligned16>, dim3(plan.total), dim3(256),
+                               0, stream, mask, S, n, plan, sg);
+        else
+            hipLaunchKernelGGL(enc_strip<kDwords>, dim3(plan.total), dim3(256), 0,
+                               stream, mask, S, n, plan, sg);
+    };
+    return encode_launches(strip, S, ws, L, enc, stream);
+}
+
+hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S, char *ws,
+                                 const EncLayout &L, const smh_mask_enc &enc,
+                                 hipStream_t stream) {
+    Pattern p;
+    p.causal = pat.causal != 0;
+    p.window = pat.window;
+    p.grow = pat.global_rows;
+    p.gcol = pat.global_cols;
+    p.blocks = pat.blocks;
+    p.keep16 = (uint32_t)floorf(pat.block_keep * 65536.0f);
+    p.rand16 = (uint32_t)floorf(pat.random_p * 65536.0f);
+    p.seed = pat.seed;
+    auto strip = [&](int n, SegPlan plan, Seg sg) {
+        hipLaunchKernelGGL(enc_pattern_strip, dim3(plan.total), dim3(256), 0,
+                           stream, p, S, n, plan, sg);
+    };
+    return encode_launches(strip, S, ws, L, enc, stream);
 }
 
 }  // namespace smh

@@ -98,6 +98,12 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
                          const EncLayout &L, const smh_mask_enc &enc,
                          hipStream_t stream);
 
+// Encoder of the mask a pattern describes (one mask, enc.mask_b = mask_h =
+// 1): the pattern strip pass, then the same scan and placement.
+hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S, char *ws,
+                                 const EncLayout &L, const smh_mask_enc &enc,
+                                 hipStream_t stream);
+
 // Block-wise kernel launcher.  in_dt: 0 f16, 1 bf16; out_dt: 0/1/2 (f32).
 hipError_t launch_blockwise(const void *q, const void *k, const void *v,
                             void *o, int B, int H, int S, int d, int in_dt,

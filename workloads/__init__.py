@@ -7,7 +7,7 @@ arithmetic, so neither the oracle nor the HIP path depends on the other
 through it.
 """
 from .configs import CONFIGS, Config, get_config
-from .gen import make_mask, make_qkv, mask_family, padding_stack
+from .gen import make_mask, make_qkv, mask_family, padding_stack, pattern_of
 
 __all__ = ["CONFIGS", "Config", "get_config", "make_mask", "make_qkv",
-           "mask_family", "padding_stack"]
+           "mask_family", "padding_stack", "pattern_of"]

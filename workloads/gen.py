@@ -47,8 +47,9 @@ def _band(S, w):
     return m
 
 
-def _bigbird(S, rng, block=64, n_random=3, drop=0.2):
-    nb = S // block
+def _bigbird_blocks(nb, rng, n_random=3):
+    """Block rows of BigBird: sliding {I-1, I, I+1} and global {0, nb-1}
+    blocks (base), and n_random seeded random blocks among the rest."""
     base = np.zeros((nb, nb), dtype=bool)
     rand = np.zeros((nb, nb), dtype=bool)
     for I in range(nb):
@@ -59,6 +60,12 @@ def _bigbird(S, rng, block=64, n_random=3, drop=0.2):
             base[I, J] = True
         for J in picks:
             rand[I, J] = True
+    return base, rand
+
+
+def _bigbird(S, rng, block=64, n_random=3, drop=0.2):
+    nb = S // block
+    base, rand = _bigbird_blocks(nb, rng, n_random)
     keep = rng.random((S, S), dtype=np.float32) >= drop
     one = np.ones((block, block), dtype=bool)
     return np.kron(base, one) | (np.kron(rand, one) & keep)
@@ -124,3 +131,27 @@ def padding_stack(mask, B, seed):
     for b, L in enumerate(lens):
         out[b, 0, :L, :L] = mask[:L, :L]
     return out
+
+
+def pattern_of(cfg):
+    """The workload's mask family as a pattern (keyword arguments of the
+    pattern encoder and of oracle.pattern.pattern_mask).  Causal, window and
+    Longformer masks are the same masks as make_mask's; BigBird keeps the
+    same block choice (rng seeded the same) and long_random the same band,
+    with their element draws from the pattern's SplitMix64 stream (seed =
+    workload id) instead of PCG64, so those two are the same families with
+    other random elements."""
+    S, fam = cfg.S, cfg.family
+    if fam == "causal":
+        return dict(causal=True, window=S)
+    if fam == "window64":
+        return dict(window=64)
+    if fam == "longformer":
+        return dict(causal=True, window=256, global_rows=16, global_cols=16)
+    if fam == "bigbird":
+        base, rand = _bigbird_blocks(S // 64, np.random.default_rng(cfg.cid))
+        blocks = base.astype(np.uint8) + 2 * (rand & ~base).astype(np.uint8)
+        return dict(blocks=blocks, block_keep=0.8, seed=cfg.cid)
+    if fam == "long_random":
+        return dict(causal=True, window=1024, random_p=0.02, seed=cfg.cid)
+    raise ValueError(f"no pattern for family {fam!r}")
