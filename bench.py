@@ -71,6 +71,10 @@ def parse():
                          "on the device; BigBird and long_random then draw "
                          "their random elements from the pattern's "
                          "generator)")
+    ap.add_argument("--epilogue", default="none", choices=["none", "out_proj"],
+                    help="out_proj: the step also runs the fused output "
+                         "projection (attention output x W^T + bias + "
+                         "residual, D = H*d) on the attention output")
     ap.add_argument("--out-dtype", default="auto",
                     choices=["auto", "in", "f32"],
                     help="output type; auto = input type for fp16, f32 for "
@@ -306,10 +310,25 @@ def main():
     which = args.kernel if args.kernel != "auto" else smh.select_kernel(
         st, cfg.B, cfg.H, cfg.d, q.dtype)
 
+    proj = None
+    if args.epilogue == "out_proj":
+        if out_dt != q.dtype:
+            raise SystemExit("--epilogue out_proj needs the attention output "
+                             "in the input type (--out-dtype in)")
+        D = cfg.H * cfg.d
+        g = torch.Generator().manual_seed(cfg.cid + 77)
+        pw = (torch.randn(D, D, generator=g) / D ** 0.5).to(q.dtype).to(dev)
+        pb = (0.1 * torch.randn(D, generator=g)).to(q.dtype).to(dev)
+        pr = torch.randn(cfg.B, cfg.S, D, generator=g).to(q.dtype).to(dev)
+        pout = torch.empty_like(pr)
+        proj = (pw, pb, pr, pout)
+
     def step():
         enc = encode()
         smh.sparse_mha_fwd(q, k, v, enc, kernel=args.kernel,
                            out_dtype=out_dt, out=out)
+        if proj is not None:
+            smh.out_proj(out, proj[0], proj[1], proj[2], out=proj[3])
 
     def encode_only():
         encode()
@@ -379,6 +398,23 @@ def main():
 
     enc_ms = kernel_us(encode_only) / 1e3
     fwd_ms = kernel_us(fwd_only) / 1e3
+    epi = None
+    if proj is not None:
+        def proj_only():
+            smh.out_proj(out, proj[0], proj[1], proj[2], out=proj[3])
+        p_us = kernel_us(proj_only)
+        M, K, D = cfg.B * cfg.S, cfg.H * cfg.d, proj[0].shape[0]
+        p_flops = 2.0 * M * K * D
+        p_bytes = 2.0 * (M * K + D * K + D + 2 * M * D)
+        p_roof = ({"bound": "hbm", "achieved": p_bytes / p_us / 1e3,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+                  if p_flops / p_bytes < RIDGE else
+                  {"bound": "mfma", "achieved": p_flops / p_us / 1e6,
+                   "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s"})
+        p_roof["frac"] = p_roof["achieved"] / p_roof["peak"]
+        epi = {"kernel": "out_proj", "us": p_us, "M": M, "K": K, "N": int(D),
+               "tflops": p_flops / p_us / 1e6, "algorithmic_flops": p_flops,
+               "algorithmic_bytes": p_bytes, "roofline": p_roof}
 
     nnz = st["nnz"]              # total over the masks of a stack
     BH = cfg.B * cfg.H
@@ -431,6 +467,7 @@ def main():
         "selector_pred_us": {"rowwise": pred_row, "blockwise": pred_blk},
         "mask_stats": st,
         "roofline": roof,
+        "epilogue": epi,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -267,6 +267,29 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
                               smh_kernel which, const smh_mask_stats *st,
                               void *stream);
 
+/* Output projection of the attention result, with bias and residual added
+ * in the same pass (the pages' operator-fusion module fuses MHA with the
+ * operators that follow it: [EXP] Methodology > 2. operator fusion; this
+ * is one such fused operator, written by hand):
+ *   out[b, s, n] = sum_{h < H, k < d} O[b, h, s, k] * W[n, h*d + k]
+ *                  + bias[n] + residual[b, s, n]
+ *   o: device [B][H][S][d] (the layout smh_sparse_mha_fwd writes), dt.
+ *   w: device [D][H*d] row-major (a linear layer's weight: out = x W^T), dt.
+ *   bias: device [D] or NULL (no bias), dt.
+ *   residual: device [B][S][D] or NULL (no residual), dt.
+ *   out: device [B][S][D], dt, not overlapping o, w or bias; it may be
+ *        residual itself (in place) but not overlap it otherwise.
+ *   B, H, S >= 0 (an empty product is a no-op); d in {64, 128}; D > 0 and
+ *   D % 64 == 0 (else SMH_EUNSUPPORTED); dt in {SMH_F16, SMH_BF16}.
+ *   All pointers 16-byte aligned.
+ * Products on the matrix cores with fp32 accumulation; bias and residual
+ * are added in fp32 and the sum is rounded once to dt.  One launch,
+ * asynchronous on `stream`. */
+smh_status smh_out_proj(const void *o, const void *w, const void *bias,
+                        const void *residual, void *out, int32_t B,
+                        int32_t H, int32_t S, int32_t d, int32_t D,
+                        smh_dtype dt, void *stream);
+
 /* Static description of a status code. */
 const char *smh_status_string(smh_status s);
 

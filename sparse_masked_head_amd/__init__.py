@@ -23,7 +23,8 @@ from ._lib import (SMH_AUTO, SMH_BF16, SMH_BLOCKWISE, SMH_F16, SMH_F32,
 
 __all__ = ["encode_mask", "encode_pattern", "encode_workspace_bytes",
            "mask_stats_get",
-           "select_kernel", "select_costs", "sparse_mha_fwd", "version",
+           "select_kernel", "select_costs", "sparse_mha_fwd", "out_proj",
+           "version",
            "MaskEncoding", "SmhError", "KERNELS"]
 
 KERNELS = {"auto": SMH_AUTO, "rowwise": SMH_ROWWISE,
@@ -227,4 +228,37 @@ def sparse_mha_fwd(q, k, v, enc, kernel="auto", out_dtype=None, scale=0.0,
         B, H, S, d, _dt(q.dtype), _dt(out_dtype), float(scale),
         ctypes.byref(enc.enc), KERNELS[kernel], st, _stream(q.device))
     check(rc, "smh_sparse_mha_fwd")
+    return out
+
+
+def out_proj(o, w, bias=None, residual=None, out=None):
+    """out[b, s, :] = sum_h o[b, h, s, :] @ w[:, h*d:(h+1)*d].T + bias +
+    residual[b, s, :] in one fused launch.  o: [B, H, S, d] (the attention
+    output), w: [D, H*d] (a linear layer's weight), bias: [D], residual and
+    out: [B, S, D]; one dtype (fp16 or bf16); out may be residual."""
+    if o.dim() != 4:
+        raise ValueError("o must be [B, H, S, d]")
+    B, H, S, d = (int(x) for x in o.shape)
+    if w.dim() != 2 or w.shape[1] != H * d:
+        raise ValueError("w must be [D, H*d]")
+    D = int(w.shape[0])
+    for name, t, shape in (("bias", bias, (D,)), ("residual", residual,
+                                                 (B, S, D))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != o.dtype
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {shape} tensor "
+                             f"of o's dtype")
+    if not (o.is_contiguous() and w.is_contiguous()) or w.dtype != o.dtype:
+        raise ValueError("o and w must be contiguous and share a dtype")
+    if out is None:
+        out = torch.empty((B, S, D), dtype=o.dtype, device=o.device)
+    elif tuple(out.shape) != (B, S, D) or out.dtype != o.dtype or \
+            not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, S, D] tensor")
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    check(lib().smh_out_proj(ptr(o), ptr(w), ptr(bias), ptr(residual),
+                             ptr(out), B, H, S, d, D, _dt(o.dtype),
+                             _stream(o.device)), "smh_out_proj")
     return out

@@ -16,6 +16,7 @@ EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_masks_workspace_bytes",
            "smh_encode_mask", "smh_encode_masks", "smh_encode_pattern",
            "smh_mask_stats_get",
            "smh_select_kernel", "smh_select_costs", "smh_sparse_mha_fwd",
+           "smh_out_proj",
            "smh_status_string", "smh_version")
 
 
@@ -102,6 +103,9 @@ def lib():
                                          ctypes.c_int,
                                          ctypes.POINTER(MaskStats), p]
         L.smh_sparse_mha_fwd.restype = ctypes.c_int
+        L.smh_out_proj.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32,
+                                   ctypes.c_int, p]
+        L.smh_out_proj.restype = ctypes.c_int
         L.smh_status_string.argtypes = [ctypes.c_int]
         L.smh_status_string.restype = ctypes.c_char_p
         L.smh_version.argtypes = []

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["encode.hip", "blockwise.hip", "rowwise.hip", "auto_fwd.hip",
-           "select.hip", "api.hip"]
+           "out_proj.hip", "select.hip", "api.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -280,4 +280,38 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
     }
 }
 
+smh_status smh_out_proj(const void *o, const void *w, const void *bias,
+                        const void *residual, void *out, int32_t B,
+                        int32_t H, int32_t S, int32_t d, int32_t D,
+                        smh_dtype dt, void *stream) {
+    try {
+        if (B < 0 || H < 0 || S < 0 || S > SMH_MAX_S) return SMH_EINVAL;
+        if (d != 64 && d != 128) return SMH_EUNSUPPORTED;
+        if (D <= 0 || D % 64) return SMH_EUNSUPPORTED;
+        if (dt != SMH_F16 && dt != SMH_BF16) return SMH_EUNSUPPORTED;
+        const int64_t M = (int64_t)B * S, K = (int64_t)H * d;
+        if (M > INT32_MAX / 2 || K > INT32_MAX / 2 || M * D > INT64_MAX / 4)
+            return SMH_EINVAL;
+        if ((M + 63) / 64 > 65535) return SMH_EINVAL;  // grid rows
+        if (M == 0) return SMH_OK;
+        if (K == 0) return SMH_EINVAL;  // no heads: nothing to project
+        if (!o || !w || !out) return SMH_EINVAL;
+        if (!aligned(o, 16) || !aligned(w, 16) || !aligned(out, 16) ||
+            (bias && !aligned(bias, 16)) || (residual && !aligned(residual, 16)))
+            return SMH_EINVAL;
+        const size_t ob = (size_t)M * D * 2;
+        if (overlaps(out, ob, o, (size_t)M * K * 2) ||
+            overlaps(out, ob, w, (size_t)D * K * 2) ||
+            (bias && overlaps(out, ob, bias, (size_t)D * 2)) ||
+            (residual && residual != out && overlaps(out, ob, residual, ob)))
+            return SMH_EINVAL;
+        return launch_out_proj(o, w, bias, residual, out, B, H, S, d, D, dt,
+                               (hipStream_t)stream) == hipSuccess
+                   ? SMH_OK
+                   : SMH_EHIP;
+    } catch (...) {
+        return SMH_EHIP;
+    }
+}
+
 }  // extern "C"

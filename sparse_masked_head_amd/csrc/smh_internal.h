@@ -123,6 +123,11 @@ hipError_t launch_auto(const void *q, const void *k, const void *v, void *o,
                        float scale, const smh_mask_enc &enc,
                        hipStream_t stream);
 
+// Output projection with bias and residual (dt: SMH_F16 or SMH_BF16).
+hipError_t launch_out_proj(const void *o, const void *w, const void *bias,
+                           const void *res, void *out, int B, int H, int S,
+                           int d, int D, int dt, hipStream_t stream);
+
 // Cost model of the selector (host only).  heads = (batch, head) pairs per
 // mask of the stack.
 smh_kernel select_kernel(const smh_mask_stats &st, int64_t heads, int d,
