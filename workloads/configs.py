@@ -41,6 +41,9 @@ CONFIGS = {
     5: Config(5, "long_unstructured_s16384", 1, 32, 16384, 128, "bf16",
               "long_random",
               "causal AND (|i-j|<=1024 OR Bernoulli(0.02)), S=16384"),
+    # the row-wise kernel's regime (highly sparse): a measurement workload
+    6: Config(6, "random_sparse_s4096", 1, 64, 4096, 64, "f16",
+              "sparse_random", "Bernoulli(0.001) per element, S=4096"),
 }
 
 

@@ -89,7 +89,8 @@ def mask_family(family, S, seed=0, **kw):
     families: ``causal``; ``window64`` (|i-j| <= 64); ``window`` (|i-j| <=
     kw['w']); ``longformer`` (causal AND (|i-j| <= 256 OR i < 16 OR j < 16));
     ``bigbird``; ``long_random`` (causal AND (|i-j| <= 1024 OR U < 0.02));
-    ``random`` (Bernoulli(kw['p']) per element); ``full``; ``empty``.
+    ``random`` (Bernoulli(kw['p']) per element); ``sparse_random``
+    (Bernoulli(0.001)); ``full``; ``empty``.
     """
     rng = np.random.default_rng(int(seed))
     if family == "causal":
@@ -109,6 +110,8 @@ def mask_family(family, S, seed=0, **kw):
                             p=float(kw.get("p", 0.02)))
     if family == "random":
         return rng.random((S, S), dtype=np.float32) < float(kw["p"])
+    if family == "sparse_random":
+        return rng.random((S, S), dtype=np.float32) < float(kw.get("p", 0.001))
     if family == "full":
         return np.ones((S, S), dtype=bool)
     if family == "empty":
@@ -154,4 +157,6 @@ def pattern_of(cfg):
         return dict(blocks=blocks, block_keep=0.8, seed=cfg.cid)
     if fam == "long_random":
         return dict(causal=True, window=1024, random_p=0.02, seed=cfg.cid)
+    if fam == "sparse_random":
+        return dict(random_p=0.001, seed=cfg.cid)
     raise ValueError(f"no pattern for family {fam!r}")
