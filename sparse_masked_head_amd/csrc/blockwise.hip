@@ -7,25 +7,24 @@ namespace {
 
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TIn, TOut> a) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(16))) char k0[Lds<D>::KBUF], k1[Lds<D>::KBUF];
+    __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
+    const TileBufs<D> bufs{{k0, k1}, {v0, v1}};
     // heavy rows first across all heads (slot_of)
     const int oi = blockIdx.x / a.U;
     const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
-    blockwise_row<D, TIn, TOut>(a, smem, sl.I, sl.bh, load_row_info(a, sl.row));
+    blockwise_row<D, TIn, TOut>(a, bufs, sl.I, sl.bh, load_row_info(a, sl.row));
 }
 
 template <int D, typename TIn, typename TOut>
 hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
                     int B, int H, int S, float scale, const smh_mask_enc &enc,
                     hipStream_t stream) {
-    const int smem = Lds<D>::BYTES;
     auto kern = blockwise_fwd<D, TIn, TOut>;
-    hipError_t e = ensure_lds_limit(kern, smem);
-    if (e != hipSuccess) return e;
     FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, B, H, S, scale, enc);
     const long long slots = (long long)a.R * a.U;  // = n * B * H
-    a.use_order = slots > resident_workgroups(kern, smem);
-    hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(256), smem, stream, a);
+    a.use_order = slots > resident_workgroups(kern, 0);
+    hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

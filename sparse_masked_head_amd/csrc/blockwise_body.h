@@ -12,13 +12,16 @@
 //
 // The workgroup owns the 64 query rows of outer-tile row I of head bh and
 // walks the full tiles of the row, then its partial tiles.  Per tile J:
-//   * K and V sit row-major in separate LDS double buffers (plain 16-byte
-//     writes; the transpose that V^T needs is done by ds_read_b64_tr_b16
-//     when the P V operand is read);
-//     K is staged two tiles ahead of its use and V one, so iteration t
-//     issues the QK^T MFMAs of tile t+1 before the softmax of tile t and
-//     the matrix cores work while the VALU does the softmax; one barrier
-//     per tile, global loads one tile ahead of staging;
+//   * K and V sit row-major in separate LDS double buffers, 16-byte chunks
+//     XOR-swizzled within each row (no padding), filled straight from
+//     global memory by global_load_lds_dwordx4 (no staging registers, no
+//     LDS write instructions); the transpose that V^T needs is done by
+//     ds_read_b64_tr_b16 when the P V operand is read.  K is loaded two
+//     tiles ahead of its use and V one, each into the buffer the previous
+//     barrier freed, so iteration t issues the QK^T MFMAs of tile t+1
+//     before the softmax of tile t and the matrix cores work while the VALU
+//     does the softmax; one barrier per tile, before which every wave waits
+//     for its own loads;
 //   * wavefront w owns queries 16w..16w+15 and computes S^T = K Q^T with
 //     v_mfma_f32_16x16x32 (A = K rows from LDS, B = its Q rows held in
 //     registers for the whole row).  In this accumulator layout lane l holds
@@ -39,66 +42,89 @@
 // Epilogue: O / l (0 for a row with no valid key), stored in the output type.
 #pragma once
 
+#include <type_traits>
+
 #include "fwd_common.h"
 
 namespace smh {
 
 template <int D> struct Lds {
-    // Row stride (elements) of the K and V tiles, chosen on gfx950 so that
-    // the operand reads are conflict-free: rows shifted by 32 bytes (a probe
-    // of the access patterns: 16-byte shifts conflict, 32-byte do not).
-    static constexpr int KLD = D + 16;
-    static constexpr int KBUF = 64 * KLD * 2;  // K tile, row-major
-    static constexpr int VBUF = 64 * KLD * 2;  // V tile, row-major
-    static constexpr int BYTES = 2 * KBUF + 2 * VBUF;
-    static __device__ char *kbuf(char *smem, int i) { return smem + i * KBUF; }
-    static __device__ char *vbuf(char *smem, int i) {
-        return smem + 2 * KBUF + i * VBUF;
+    // A tile is 64 rows of D elements = CPR 16-byte chunks per row, no
+    // padding.  Chunk c of row r sits at chunk position c ^ sw(r) of the
+    // row: sw spreads the 16 rows a K operand read touches (and the rows of
+    // a V^T read) over distinct bank groups.
+    static constexpr int CPR = D / 8;
+    static constexpr int KBUF = 64 * D * 2;
+    static constexpr int VBUF = 64 * D * 2;
+    static __device__ int sw(int row) {
+        return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
+    }
+    // byte offset of chunk c of row r inside a tile buffer
+    static __device__ int chunk_off(int r, int c) {
+        return (r * CPR + (c ^ sw(r))) * 16;
     }
 };
 
-// Registers carrying one K tile (and, for a partial tile, the four mask
-// bytes this lane needs) or one V tile from global memory to LDS.
-template <int D> struct KRegs {
-    static constexpr int N = 64 * D / 8 / 256;  // 16-byte chunks per thread
-    u4_t kr[N];
-    uint32_t mb[4];
-};
-template <int D> struct VRegs {
-    static constexpr int N = 64 * D / 8 / 256;  // 16-byte chunks per thread
-    u4_t vr[N];
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// Global loads of K tile J (one contiguous block: thread t takes 16-byte
-// chunks t, t+256, ...; a chunk at element offset above `lim` is read from
-// `lim` instead, so that the rows of a tile cut by S come from inside K:
-// they are masked, and any finite value serves) and, for a partial tile,
-// this lane's mask bytes:
+// One tile (K or V) of 64 rows from global memory into a tile buffer with
+// global_load_lds_dwordx4: wave w's instruction i fills chunk positions
+// 64 (4i + w) .. +63 (1 KB, lane l the position 64 (4i + w) + l) and each
+// lane reads the global chunk that belongs there.  The lane's byte offsets
+// inside a tile are fixed (TileOffs); a tile adds only its base address,
+// which is the same for the whole wave.  A chunk at a byte offset above
+// `lim` is read from `lim` instead, so that the rows of a tile cut by S come
+// from inside the tensor: they are masked (K) or multiplied by a zero
+// probability (V), and any finite value serves.  The data lands
+// asynchronously: the loads count in vmcnt.
+template <int D> struct TileOffs {
+    uint32_t off[D / 32];  // byte offset of this lane's chunk i in the tile
+};
+template <int D> __device__ inline TileOffs<D> tile_offsets(int w, int l) {
+    using L = Lds<D>;
+    TileOffs<D> o;
+#pragma unroll
+    for (int i = 0; i < L::CPR / 4; ++i) {
+        const int pos = 64 * (4 * i + w) + l;  // chunk position in the buffer
+        const int r = pos / L::CPR, c = (pos % L::CPR) ^ L::sw(r);
+        o.off[i] = 2u * (uint32_t)(r * D + 8 * c);
+    }
+    return o;
+}
+template <int D>
+__device__ __attribute__((always_inline)) inline void load_tile(
+    char *buf, const char *tile, uint32_t lim, const TileOffs<D> &to, int w) {
+    using L = Lds<D>;
+#pragma unroll
+    for (int i = 0; i < L::CPR / 4; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(tile + min(to.off[i], lim)),
+                                         (lds_void_t *)(buf + 1024 * (4 * i + w)),
+                                         16, 0, 0);
+}
+
+// This lane's mask bytes of a partial tile (global loads into registers):
 // keys 16st + 4g + i of query row r are bits 4(g&1)+i of byte r&7 of inner
 // tile (r>>3, 2st + (g>>1)); b_off is that byte's offset for st = 0, each
 // further st is two words (16 bytes) on.
-template <int D, typename TIn>
-__device__ __attribute__((always_inline)) inline void fetch_k(
-    KRegs<D> &r, const TIn *__restrict__ Kh, int J, int lim,
-    const uint64_t *__restrict__ words, int b_off, int t) {
-    const TIn *kt = Kh + (size_t)J * 64 * D;
-#pragma unroll
-    for (int i = 0; i < KRegs<D>::N; ++i)
-        r.kr[i] = *reinterpret_cast<const u4_t *>(kt + min((t + 256 * i) * 8, lim));
+struct MaskRegs {
+    uint32_t mb[4];
+};
+__device__ __attribute__((always_inline)) inline void load_mask(
+    MaskRegs &m, const uint64_t *__restrict__ words, int b_off) {
     if (words) {
         const uint8_t *wb = reinterpret_cast<const uint8_t *>(words) + b_off;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) r.mb[st] = wb[16 * st];
+        for (int st = 0; st < 4; ++st) m.mb[st] = wb[16 * st];
     }
 }
 
-// The lane's mask bits of a fetched partial tile: bit 8st + i (i < 4) =
-// key 16st + 4g + i of its query row (nib = 4(g&1)); the other bits are
-// not used.
-template <int D>
+// The lane's mask bits of a partial tile: bit 8st + i (i < 4) = key
+// 16st + 4g + i of its query row (nib = 4(g&1)); the other bits are not
+// used.
 __device__ __attribute__((always_inline)) inline uint32_t mask_bits(
-    const KRegs<D> &r, int nib) {
-    return (r.mb[0] | (r.mb[1] << 8) | (r.mb[2] << 16) | (r.mb[3] << 24)) >> nib;
+    const MaskRegs &m, int nib) {
+    return (m.mb[0] | (m.mb[1] << 8) | (m.mb[2] << 16) | (m.mb[3] << 24)) >> nib;
 }
 
 // Bit `off` of x as 0 or -1 (v_bfe_i32; written out so that the compiler
@@ -109,44 +135,10 @@ template <int off> __device__ __attribute__((always_inline)) inline int bit_mask
     return r;
 }
 
-// Global loads of V tile J, the same contiguous chunks and limit as K (a
-// masked key's V row is multiplied by a zero probability).
-template <int D, typename TIn>
-__device__ __attribute__((always_inline)) inline void fetch_v(
-    VRegs<D> &r, const TIn *__restrict__ Vh, int J, int lim, int t) {
-    const TIn *vt = Vh + (size_t)J * 64 * D;
-#pragma unroll
-    for (int i = 0; i < VRegs<D>::N; ++i)
-        r.vr[i] = *reinterpret_cast<const u4_t *>(vt + min((t + 256 * i) * 8, lim));
-}
-
-// K tile row-major into a K buffer (padded rows).
-template <int D, typename TIn>
-__device__ __attribute__((always_inline)) inline void stage_k(
-    const KRegs<D> &r, char *kb, int t) {
-    using L = Lds<D>;
-    TIn *ks = reinterpret_cast<TIn *>(kb);
-#pragma unroll
-    for (int i = 0; i < KRegs<D>::N; ++i) {
-        const int e = t + 256 * i;
-        const int row = e / (D / 8), col = (e % (D / 8)) * 8;
-        *reinterpret_cast<u4_t *>(ks + row * L::KLD + col) = r.kr[i];
-    }
-}
-
-// V tile row-major into a V buffer (padded rows, like K); the transpose
-// that the P V product needs is done by the transposing LDS reads.
-template <int D>
-__device__ __attribute__((always_inline)) inline void stage_v(
-    const VRegs<D> &r, char *vb, int t) {
-    using L = Lds<D>;
-    uint16_t *vs = reinterpret_cast<uint16_t *>(vb);
-#pragma unroll
-    for (int i = 0; i < VRegs<D>::N; ++i) {
-        const int e = t + 256 * i;
-        const int row = e / (D / 8), col = (e % (D / 8)) * 8;
-        *reinterpret_cast<u4_t *>(vs + row * L::KLD + col) = r.vr[i];
-    }
+// Wait for this wave's outstanding global loads (the tile loads into LDS
+// among them), before the barrier that hands their buffers to every wave.
+__device__ __attribute__((always_inline)) inline void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Running state of one lane: O^T accumulators of its query (d = 16dt +
@@ -162,13 +154,28 @@ template <int D> struct RowState {
 // scores leave the matrix cores as -inf and the softmax needs no masking.
 // The two cases are separate code so that a full tile's first products
 // take the constant zero accumulator.
+// This lane's byte offsets into a K buffer for the A operand of S^T = K Q^T:
+// row 16st + lq (st added by the caller), chunk 4s + g, s < D/32.
+template <int D> struct KOff {
+    int base;          // row lq
+    int x[D / 32];     // swizzled chunk position of chunk 4s + g, times 16
+};
+template <int D> __device__ inline KOff<D> k_offsets(int lq, int g) {
+    using L = Lds<D>;
+    KOff<D> o;
+    o.base = lq * L::CPR * 16;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) o.x[s] = ((4 * s + g) ^ L::sw(lq)) * 16;
+    return o;
+}
+
 template <int D, typename TIn, bool kPartial>
 __device__ __attribute__((always_inline)) inline void qk_tile_k(
     f4_t (&sc)[4], const typename Frag<TIn>::type (&qf)[D / 32],
-    const char *kb, int k_off, uint32_t mbits) {
+    const char *kb, const KOff<D> &ko, uint32_t mbits) {
     using F = Frag<TIn>;
     using frag = typename F::type;
-    const TIn *ks = reinterpret_cast<const TIn *>(kb) + k_off;
+    const char *ks = kb + ko.base;
     const int inv = (int)~mbits;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -178,12 +185,12 @@ __device__ __attribute__((always_inline)) inline void qk_tile_k(
                       __int_as_float(bit_mask<1>(inv >> (8 * st)) & (int)0xFF800000u),
                       __int_as_float(bit_mask<2>(inv >> (8 * st)) & (int)0xFF800000u),
                       __int_as_float(bit_mask<3>(inv >> (8 * st)) & (int)0xFF800000u)};
-        const frag a0 = *reinterpret_cast<const frag *>(ks + 16 * st * Lds<D>::KLD);
+        const char *row = ks + 16 * st * Lds<D>::CPR * 16;
+        const frag a0 = *reinterpret_cast<const frag *>(row + ko.x[0]);
         sc[st] = F::mfma(a0, qf[0], c0);
 #pragma unroll
         for (int s = 1; s < D / 32; ++s) {
-            const frag a = *reinterpret_cast<const frag *>(
-                ks + 16 * st * Lds<D>::KLD + 32 * s);
+            const frag a = *reinterpret_cast<const frag *>(row + ko.x[s]);
             sc[st] = F::mfma(a, qf[s], sc[st]);
         }
     }
@@ -192,18 +199,38 @@ __device__ __attribute__((always_inline)) inline void qk_tile_k(
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void qk_tile(
     f4_t (&sc)[4], const typename Frag<TIn>::type (&qf)[D / 32],
-    const char *kb, int k_off, bool partial, uint32_t mbits) {
+    const char *kb, const KOff<D> &ko, bool partial, uint32_t mbits) {
     if (partial)
-        qk_tile_k<D, TIn, true>(sc, qf, kb, k_off, mbits);
+        qk_tile_k<D, TIn, true>(sc, qf, kb, ko, mbits);
     else
-        qk_tile_k<D, TIn, false>(sc, qf, kb, k_off, mbits);
+        qk_tile_k<D, TIn, false>(sc, qf, kb, ko, mbits);
+}
+
+// This lane's byte offsets into a V buffer for the transposing reads of
+// V^T: key row 32u + 4g + (lq >> 2) (+16 for the upper slots; u added by
+// the caller), elements 16dt + 4 (lq & 3) .. +3, i.e. half (lq & 1) of
+// chunk 2dt + ((lq & 3) >> 1).  The swizzle of those rows does not depend
+// on u or the +16.
+template <int D> struct VOff {
+    int base;          // row 4g + (lq >> 2), plus the half-chunk
+    int x[D / 16];     // swizzled chunk position of chunk 2dt + ..., times 16
+};
+template <int D> __device__ inline VOff<D> v_offsets(int lq, int g) {
+    using L = Lds<D>;
+    VOff<D> o;
+    const int r = 4 * g + (lq >> 2);
+    o.base = r * L::CPR * 16 + 8 * (lq & 1);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        o.x[dt] = ((2 * dt + ((lq & 3) >> 1)) ^ L::sw(r)) * 16;
+    return o;
 }
 
 // Softmax of one tile's scores (masked ones already -inf) and
 // O^T += V^T P^T.  c = scale * log2(e) > 0.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void softmax_pv(
-    RowState<D> &rs, f4_t (&sc)[4], const char *vb, float c, int v_off) {
+    RowState<D> &rs, f4_t (&sc)[4], const char *vb, float c, const VOff<D> &vo) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     using L = Lds<D>;
@@ -252,15 +279,15 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
     // the P^T slots) read with ds_read_b64_tr_b16 from row-major V: within
     // each 16-lane group, lane j = a + 4q points at V[key0 + q][d0 + 4a]
     // and lane i receives V[key0 .. key0+3][d0 + i]; key0 = 32u + 4g for
-    // slots 0..3 and 32u + 16 + 4g for slots 4..7.  v_off is the lane's
-    // (q, a) offset in elements.
-    const char *vs = vb + 2 * v_off;
+    // slots 0..3 and 32u + 16 + 4g for slots 4..7.  vo holds the lane's
+    // (q, a) offsets in the swizzled buffer.
+    const char *vs = vb + vo.base;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const char *p0 = vs + 2 * (32 * u * L::KLD + 16 * dt);
-            const char *p1 = p0 + 2 * 16 * L::KLD;
+            const char *p0 = vs + 32 * u * L::CPR * 16 + vo.x[dt];
+            const char *p1 = p0 + 16 * L::CPR * 16;
             const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_s4_t *)(p0));
             const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -275,19 +302,21 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
 
 // The stored tiles of one outer-tile row: full tiles first, then partial.
 // Columns are clamped to [0, n): an encoding that is not this library's
-// then gives wrong numbers, never an access outside K and V.  lim(J) is the
-// last in-bounds 8-element chunk offset of tile J (S cuts the last tile).
+// then gives wrong numbers, never an access outside K and V.  The columns
+// of the first four tiles come with the row summary; the tile loop reads
+// each later column one step before it needs it (a column read in the step
+// that uses it would put a memory round trip in front of every tile load).
 struct TileList {
     const int32_t *fci, *pci;
     const uint64_t *bm;
     int f0, nF, p0, nT, nmax, S;
-    int c4[4];  // columns of the first four tiles (row_info)
-    __device__ int col(int idx) const {
-        const int J = idx < 4 ? c4[idx] : idx < nF ? fci[f0 + idx] : pci[p0 + idx - nF];
-        return (int)min((unsigned)J, (unsigned)nmax);
+    __device__ int clamp(int J) const { return (int)min((unsigned)J, (unsigned)nmax); }
+    __device__ const int32_t *col_ptr(int idx) const {
+        return idx < nF ? fci + f0 + idx : pci + p0 + idx - nF;
     }
-    template <int D> __device__ int lim(int J) const {
-        return min(64, S - 64 * J) * D - 8;
+    // last in-bounds 16-byte chunk offset (bytes) of tile J (S cuts the last tile)
+    template <int D> __device__ uint32_t lim(int J) const {
+        return 2u * (uint32_t)(min(64, S - 64 * J) * D - 8);
     }
     __device__ const uint64_t *words(int idx) const {
         return idx < nF ? nullptr : bm + (size_t)(p0 + idx - nF) * 64;
@@ -296,9 +325,18 @@ struct TileList {
 
 // Workgroup work: encoding row `row` (outer-tile row I of its mask, summary
 // ri) of head bh.
+// The four tile buffers (K0, K1, V0, V1) are separate LDS objects, and
+// the tile loop picks them at compile time, so that the compiler can tell
+// the loads filling one buffer from the reads of another and does not make
+// those reads wait for the loads.
+template <int D> struct TileBufs {
+    char *k[2], *v[2];
+};
+
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void blockwise_row(
-    const FwdArgs<TIn, TOut> &a, char *smem, int I, int bh, const RowInfo &ri) {
+    const FwdArgs<TIn, TOut> &a, const TileBufs<D> &bufs, int I, int bh,
+    const RowInfo &ri) {
     using frag = typename Frag<TIn>::type;
     using L = Lds<D>;
     const size_t head = (size_t)bh * a.S * D;
@@ -318,8 +356,6 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     tl.nF = ri.nF;
     tl.p0 = ri.p0;
     tl.nT = ri.nF + ri.nP;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) tl.c4[k] = ri.c[k];
     const int nT = tl.nT, nF = tl.nF;
 
     // this lane's Q rows as the B operand: query r, d = 32s + 8g + 0..7
@@ -339,87 +375,78 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     rs.m = -INFINITY;
     rs.l = 0.f;
 
-    // per-lane LDS offsets (elements / bytes), the same in every buffer
-    const int k_off = lq * L::KLD + 8 * g;
-    const int v_off = (4 * g + (lq >> 2)) * L::KLD + 4 * (lq & 3);
+    // per-lane LDS offsets, the same in every buffer
+    const KOff<D> ko = k_offsets<D>(lq, g);
+    const VOff<D> vo = v_offsets<D>(lq, g);
     const int b_off = ((r >> 3) * 8 + (g >> 1)) * 8 + (r & 7);
     const int nib = 4 * (g & 1);
 
-    // Pipeline: K (with its words) is staged two tiles ahead of its use and
-    // V one tile ahead, so that tile step `it` can issue QK^T of tile it+1
-    // before the softmax of tile it (matrix cores busy during the VALU
-    // work).  Buffers: K(it) in kbuf(it&1), V(it) in vbuf(it&1).  The mask
-    // bits ride along in registers, taken from the K registers when they
-    // are staged.  At d = 64 the loop is unrolled by two so that the two
-    // score buffers and mask slots swap roles instead of being copied.
-    KRegs<D> kr, kr1;
-    VRegs<D> vr;
+    // Pipeline: K is loaded two tiles ahead of its use and V one tile
+    // ahead, each straight into the buffer the previous barrier freed, so
+    // that tile step `it` can issue QK^T of tile it+1 before the softmax of
+    // tile it (matrix cores busy during the VALU work).  Buffers: K(it) in
+    // bufs.k[it&1], V(it) in bufs.v[it&1].  The mask bytes of a partial tile
+    // come into registers with its K load.  The loop is unrolled by two so
+    // that the buffers are picked at compile time and the two score buffers
+    // and mask slots swap roles instead of being copied.
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // w, known uniform
+    const TileOffs<D> to = tile_offsets<D>(wu, l);
+    const char *Kb = reinterpret_cast<const char *>(Kh);
+    const char *Vb = reinterpret_cast<const char *>(Vh);
+    MaskRegs mk0, mk1;
     f4_t s_a[4], s_b[4];
     uint32_t m_a = 0, m_b = 0;
-    // loads of stored tile idx: K (with its mask bytes) or V
-    auto load_k = [&](KRegs<D> &dst, int idx) __attribute__((always_inline)) {
-        const int J = tl.col(idx);
-        fetch_k<D, TIn>(dst, Kh, J, tl.lim<D>(J), tl.words(idx), b_off, t);
+    // loads of stored tile idx (column J): K (with its mask bytes) or V
+    auto load_k = [&](char *buf, MaskRegs &mk, int idx, int J) __attribute__((always_inline)) {
+        load_tile<D>(buf, Kb + (size_t)J * 64 * D * 2, tl.lim<D>(J), to, wu);
+        load_mask(mk, tl.words(idx), b_off);
     };
-    auto load_v = [&](int idx) __attribute__((always_inline)) {
-        const int J = tl.col(idx);
-        fetch_v<D, TIn>(vr, Vh, J, tl.lim<D>(J), t);
+    auto load_v = [&](char *buf, int J) __attribute__((always_inline)) {
+        load_tile<D>(buf, Vb + (size_t)J * 64 * D * 2, tl.lim<D>(J), to, wu);
     };
+    // columns of the K tile (jk, tile it+2) and V tile (jv, tile it+1) that
+    // tile step it loads
+    int jv = tl.clamp(ri.c[1]), jk = tl.clamp(ri.c[2]);
     if (nT > 0) {
-        load_k(kr, 0);
-        load_v(0);
-        if (nT > 1) load_k(kr1, 1);
-        stage_k<D, TIn>(kr, L::kbuf(smem, 0), t);
-        if (nF == 0) m_a = mask_bits<D>(kr, nib);
-        stage_v<D>(vr, L::vbuf(smem, 0), t);
-        if (nT > 1) {
-            stage_k<D, TIn>(kr1, L::kbuf(smem, 1), t);
-            if (1 >= nF) m_b = mask_bits<D>(kr1, nib);
-        }
-        if (nT > 2) load_k(kr, 2);
-        if (nT > 1) load_v(1);
+        load_k(bufs.k[0], mk0, 0, tl.clamp(ri.c[0]));
+        load_v(bufs.v[0], tl.clamp(ri.c[0]));
+        if (nT > 1) load_k(bufs.k[1], mk1, 1, jv);
     }
+    wait_loads();
+    if (nT > 0 && nF == 0) m_a = mask_bits(mk0, nib);
+    if (nT > 1 && 1 >= nF) m_b = mask_bits(mk1, nib);
     __syncthreads();
-    if (nT > 0) qk_tile<D, TIn>(s_a, qf, L::kbuf(smem, 0), k_off, nF == 0, m_a);
-    // every wave has read K(0) before tile step 0 overwrites its buffer
+    if (nT > 0) qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a);
+    // every wave has read K(0) before tile step 0 loads into its buffer
     __syncthreads();
 
-    // One tile step: scores of tile it in `cur` (mask mc), of tile it+1 go
-    // to `nxt` (mask mn); mc is then reused for tile it+2's mask.
-    auto step = [&](int it, f4_t(&cur)[4], f4_t(&nxt)[4], uint32_t &mc,
+    // One tile step (cb = it & 1, a compile-time constant): scores of tile
+    // it in `cur` (mask mc), of tile it+1 go to `nxt` (mask mn); mc is then
+    // reused for tile it+2's mask.
+    auto step = [&](int it, auto cbc, f4_t(&cur)[4], f4_t(&nxt)[4], uint32_t &mc,
                     const uint32_t mn) __attribute__((always_inline)) {
-        const int cb = it & 1, nb = cb ^ 1;
-        if (it + 1 < nT)
-            qk_tile<D, TIn>(nxt, qf, L::kbuf(smem, nb), k_off, it + 1 >= nF, mn);
-        softmax_pv<D, TIn>(rs, cur, L::vbuf(smem, cb), a.c, v_off);
+        constexpr int cb = decltype(cbc)::value, nb = cb ^ 1;
+        // column of tile it+3 (tile step it+1 loads its K); from memory past
+        // the four of the row summary
+        int jn_raw = ri.c[3];
+        if (it + 3 < nT && it + 3 >= 4) jn_raw = *tl.col_ptr(it + 3);
         // K(it+2) replaces K(it) (read in the previous step); V(it+1)
-        // replaces V(it-1)
-        uint32_t m2 = 0;
-        if (it + 2 < nT) {
-            stage_k<D, TIn>(kr, L::kbuf(smem, cb), t);
-            if (it + 2 >= nF) m2 = mask_bits<D>(kr, nib);
-        }
-        if (it + 1 < nT) stage_v<D>(vr, L::vbuf(smem, nb), t);
-        if (it + 3 < nT) load_k(kr, it + 3);
-        if (it + 2 < nT) load_v(it + 2);
+        // replaces V(it-1) (read in the previous step)
+        if (it + 2 < nT) load_k(bufs.k[cb], mk0, it + 2, jk);
+        if (it + 1 < nT) load_v(bufs.v[nb], jv);
+        if (it + 1 < nT)
+            qk_tile<D, TIn>(nxt, qf, bufs.k[nb], ko, it + 1 >= nF, mn);
+        softmax_pv<D, TIn>(rs, cur, bufs.v[cb], a.c, vo);
+        wait_loads();
+        mc = it + 2 < nT && it + 2 >= nF ? mask_bits(mk0, nib) : 0u;
+        jv = jk;
+        jk = tl.clamp(__builtin_amdgcn_readfirstlane(jn_raw));
         __syncthreads();
-        mc = m2;
     };
-    if constexpr (D == 64) {
-        for (int it = 0; it < nT; it += 2) {
-            step(it, s_a, s_b, m_a, m_b);
-            if (it + 1 >= nT) break;
-            step(it + 1, s_b, s_a, m_b, m_a);
-        }
-    } else {  // measured: the unrolled body is slower at d = 128
-        for (int it = 0; it < nT; ++it) {
-            step(it, s_a, s_b, m_a, m_b);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) s_a[st] = s_b[st];
-            const uint32_t m2 = m_a;
-            m_a = m_b;
-            m_b = m2;
-        }
+    for (int it = 0; it < nT; it += 2) {
+        step(it, std::integral_constant<int, 0>(), s_a, s_b, m_a, m_b);
+        if (it + 1 >= nT) break;
+        step(it + 1, std::integral_constant<int, 1>(), s_b, s_a, m_b, m_a);
     }
 
     // epilogue: total l over the 4 lanes of this query
