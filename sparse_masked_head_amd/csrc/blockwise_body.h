@@ -51,13 +51,19 @@ namespace smh {
 template <int D> struct Lds {
     // A tile is 64 rows of D elements = CPR 16-byte chunks per row, no
     // padding.  Chunk c of row r sits at chunk position c ^ sw(r) of the
-    // row: sw spreads the 16 rows a K operand read touches (and the rows of
-    // a V^T read) over distinct bank groups.
+    // row.  The 64 banks span 256 bytes: one row at d = 128, two at d = 64.
+    // sw puts both read patterns on distinct 16-byte bank slots: a K
+    // operand read (16 consecutive rows, one chunk: sw distinct over them,
+    // within each row parity at d = 64) and the V^T reads of two lane
+    // groups (8 consecutive rows, chunks 2dt and 2dt+1: sw >> 1 distinct
+    // over them, within each row parity at d = 64).  sw depends on row % 16
+    // only.
     static constexpr int CPR = D / 8;
     static constexpr int KBUF = 64 * D * 2;
     static constexpr int VBUF = 64 * D * 2;
     static __device__ int sw(int row) {
-        return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
+        return CPR == 16 ? (((row & 7) << 1) | ((row >> 3) & 1))
+                         : ((((row >> 1) & 3) << 1) | ((row >> 3) & 1));
     }
     // byte offset of chunk c of row r inside a tile buffer
     static __device__ int chunk_off(int r, int c) {
