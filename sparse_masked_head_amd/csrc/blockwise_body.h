@@ -152,6 +152,7 @@ __device__ __attribute__((always_inline)) inline void wait_loads() {
 template <int D> struct RowState {
     f4_t acc[D / 16];
     float m, l;
+    float mc;  // m * c, or 0 while m is -inf (the exponent offset)
 };
 
 // S^T = K Q^T for one tile (four 16-key sub-tiles), raw scores.  For a
@@ -218,17 +219,19 @@ __device__ __attribute__((always_inline)) inline void qk_tile(
 // chunk 2dt + ((lq & 3) >> 1).  The swizzle of those rows does not depend
 // on u or the +16.
 template <int D> struct VOff {
-    int base;          // row 4g + (lq >> 2), plus the half-chunk
-    int x[D / 16];     // swizzled chunk position of chunk 2dt + ..., times 16
+    // byte offset of row 4g + (lq >> 2), half-chunk lq & 1, swizzled
+    // chunk 2dt + ((lq & 3) >> 1); a buffer address plus a constant row
+    // offset completes the address
+    int x[D / 16];
 };
 template <int D> __device__ inline VOff<D> v_offsets(int lq, int g) {
     using L = Lds<D>;
     VOff<D> o;
     const int r = 4 * g + (lq >> 2);
-    o.base = r * L::CPR * 16 + 8 * (lq & 1);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-        o.x[dt] = ((2 * dt + ((lq & 3) >> 1)) ^ L::sw(r)) * 16;
+        o.x[dt] = r * L::CPR * 16 + 8 * (lq & 1) +
+                  ((2 * dt + ((lq & 3) >> 1)) ^ L::sw(r)) * 16;
     return o;
 }
 
@@ -257,11 +260,12 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
         const float m_new = grow ? mx : rs.m;
         const float alpha = grow ? __builtin_amdgcn_exp2f((rs.m - m_new) * c) : 1.f;
         rs.m = m_new;
+        rs.mc = grow ? mx * c : rs.mc;  // a growing max is finite
         rs.l *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
     }
-    const float mc = (rs.m == -INFINITY ? 0.f : rs.m) * c;
+    const float mc = rs.mc;
 
     // P^T as B operand: keys 32u + 4g + j (j < 4), 32u + 16 + 4g + j - 4
     frag pf[2];
@@ -287,12 +291,11 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
     // and lane i receives V[key0 .. key0+3][d0 + i]; key0 = 32u + 4g for
     // slots 0..3 and 32u + 16 + 4g for slots 4..7.  vo holds the lane's
     // (q, a) offsets in the swizzled buffer.
-    const char *vs = vb + vo.base;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const char *p0 = vs + 32 * u * L::CPR * 16 + vo.x[dt];
+            const char *p0 = vb + vo.x[dt] + 32 * u * L::CPR * 16;
             const char *p1 = p0 + 16 * L::CPR * 16;
             const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_s4_t *)(p0));
@@ -379,6 +382,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) rs.acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
     rs.m = -INFINITY;
+    rs.mc = 0.f;
     rs.l = 0.f;
 
     // per-lane LDS offsets, the same in every buffer

@@ -211,13 +211,21 @@ __device__ inline float wave_sum(float x) {
 // Max / sum of x over lanes l and l^16 (then l^32) with the gfx950 row
 // swaps: swapping odd rows of one copy with even rows of the other leaves
 // the two partners' values side by side in every lane.
+// (The max is v_max_f32 written out: fmaxf on values from a lane swap
+// makes the compiler quiet possible signalling NaNs first, two more
+// instructions; no such NaN occurs here.)
+__device__ inline float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 __device__ inline float max_xor16(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float max_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float sum_xor16(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
