@@ -39,8 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id 1..6 (default 2; 6 = the row-wise "
-                         "kernel's regime, a 0.1%% random mask)")
+                    help="workload id 1..7 (default 2; 6 = the row-wise "
+                         "kernel's regime, a 0.1%% random mask; 7 = "
+                         "workload 5's far tiles alone)")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "rowwise", "blockwise"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,

@@ -10,7 +10,8 @@ def test_config_shapes():
     assert [(c.B, c.H, c.S, c.d, c.dtype) for c in CONFIGS.values()] == [
         (1, 2, 256, 64, "f16"), (8, 12, 512, 64, "f16"),
         (4, 32, 2048, 128, "bf16"), (2, 16, 4096, 64, "f16"),
-        (1, 32, 16384, 128, "bf16"), (1, 64, 4096, 64, "f16")]
+        (1, 32, 16384, 128, "bf16"), (1, 64, 4096, 64, "f16"),
+        (1, 32, 16384, 128, "bf16")]
 
 
 def test_qkv_seeded_and_rounded():

@@ -44,6 +44,10 @@ CONFIGS = {
     # the row-wise kernel's regime (highly sparse): a measurement workload
     6: Config(6, "random_sparse_s4096", 1, 64, 4096, 64, "f16",
               "sparse_random", "Bernoulli(0.001) per element, S=4096"),
+    # workload 5 without its band: the partial tiles a per-tile hybrid
+    # would hand to a gather path, on their own (a measurement workload)
+    7: Config(7, "far_random_s16384", 1, 32, 16384, 128, "bf16",
+              "far_random", "causal AND Bernoulli(0.02), S=16384"),
 }
 
 

@@ -90,7 +90,8 @@ def mask_family(family, S, seed=0, **kw):
     kw['w']); ``longformer`` (causal AND (|i-j| <= 256 OR i < 16 OR j < 16));
     ``bigbird``; ``long_random`` (causal AND (|i-j| <= 1024 OR U < 0.02));
     ``random`` (Bernoulli(kw['p']) per element); ``sparse_random``
-    (Bernoulli(0.001)); ``full``; ``empty``.
+    (Bernoulli(0.001)); ``far_random`` (causal AND U < 0.02: long_random
+    without its band); ``full``; ``empty``.
     """
     rng = np.random.default_rng(int(seed))
     if family == "causal":
@@ -108,6 +109,8 @@ def mask_family(family, S, seed=0, **kw):
     if family == "long_random":
         return _long_random(S, rng, w=int(kw.get("w", 1024)),
                             p=float(kw.get("p", 0.02)))
+    if family == "far_random":
+        return _long_random(S, rng, w=-1, p=float(kw.get("p", 0.02)))
     if family == "random":
         return rng.random((S, S), dtype=np.float32) < float(kw["p"])
     if family == "sparse_random":
@@ -159,4 +162,6 @@ def pattern_of(cfg):
         return dict(causal=True, window=1024, random_p=0.02, seed=cfg.cid)
     if fam == "sparse_random":
         return dict(random_p=0.001, seed=cfg.cid)
+    if fam == "far_random":
+        return dict(causal=True, random_p=0.02, seed=cfg.cid)
     raise ValueError(f"no pattern for family {fam!r}")
