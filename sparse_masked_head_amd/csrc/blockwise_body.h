@@ -71,9 +71,6 @@ template <int D> struct Lds {
     }
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
 // One tile (K or V) of 64 rows from global memory into a tile buffer with
 // global_load_lds_dwordx4: wave w's instruction i fills chunk positions
 // 64 (4i + w) .. +63 (1 KB, lane l the position 64 (4i + w) + l) and each
