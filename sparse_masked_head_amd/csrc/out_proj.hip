@@ -157,21 +157,20 @@ __global__ __launch_bounds__(256) void out_proj(ProjArgs<T> a) {
     }
 }
 
-// Large shapes: 256 x 256 outputs per workgroup of 1024 threads (16
-// wavefronts, 4 along n x 4 along m, each 64 x 64: 16 MFMA tiles), k in
-// blocks of 32 through a ring of four LDS stages filled straight from global
-// memory (global_load_lds_dwordx4, no staging registers), three blocks
-// ahead.  A 256 x 256 tile needs half the bytes per flop of a 128 x 128 one:
-// at the matrix cores' rate 32 bytes per clock into the CU instead of 64,
+// Load-to-LDS ring kernel: BT x BT outputs per workgroup of NW wavefronts
+// (BT = 256: 16 wavefronts in 4 x 4, each 64 x 64; BT = 128: 4 in 2 x 2,
+// 64 x 64; BT = 64: 4 in 2 x 2, 32 x 32), k in blocks of 32 through a ring
+// of four LDS stages filled straight from global memory
+// (global_load_lds_dwordx4, no staging registers), three blocks ahead.  The
+// bigger the tile, the fewer bytes per flop: at the matrix cores' rate a
+// 256 x 256 tile needs 32 bytes per clock into the CU, a 128 x 128 one 64,
 // which is all a CU's load path gives.  A stage holds the W block (rows n)
 // then the O block (rows m), 64 bytes per row; the 16-byte chunk c of row r
 // sits at chunk c ^ ((r >> 2) & 3), so the 16 rows of an operand read fall
 // on 16 distinct bank slots.  The four stages are separate LDS objects and
 // the k loop is unrolled by four so that each is picked at compile time:
 // the loads into one stage then never hold up the reads of another.
-constexpr int kGB = 256, kGK = 32;
-constexpr int kGOp = kGB * kGK * 2;  // bytes of one operand block
-constexpr int kGStage = 2 * kGOp;    // W block, then O block
+constexpr int kGK = 32;
 
 // p as a wave-uniform value (two v_readfirstlane): the compiler then keeps
 // a k block's base in scalar registers and adds each lane's fixed 32-bit
@@ -193,27 +192,37 @@ __device__ __attribute__((always_inline)) inline uint32_t lds_addr(const char *p
 // 16-byte LDS read written out: the compiler does not see it as a read of
 // the stage, so it adds no wait of its own for the stage's loads (it cannot
 // count them across the k loop and would wait for all of them); the caller
-// waits for the results (lds_wait) before using them.
+// waits for the results before using them.
 template <int off, typename F>
 __device__ __attribute__((always_inline)) inline void lds_read16(F &f, uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(off));
 }
 
-template <typename T>
-__device__ __attribute__((always_inline)) inline void big_load(
-    char *stage, const char *wk, const char *ok, uint32_t wo, uint32_t oo, int w) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t *)(wk + wo),
-                                     (lds_void_t *)(stage + 1024 * w), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void_t *)(ok + oo),
-                                     (lds_void_t *)(stage + kGOp + 1024 * w), 16, 0, 0);
-}
+// Wait until at most n of this wave's LDS reads are outstanding.
+template <int n> __device__ __attribute__((always_inline)) inline void lds_wait_asm();
+#define SMH_LGKM(n)                                                      \
+    template <> __device__ __attribute__((always_inline)) inline void   \
+    lds_wait_asm<n>() { asm volatile("s_waitcnt lgkmcnt(" #n ")" ::: "memory"); }
+SMH_LGKM(0) SMH_LGKM(1) SMH_LGKM(2) SMH_LGKM(3)
+#undef SMH_LGKM
 
-template <int D, typename T>
-__global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
+template <int BT, int NW> struct Ring {
+    static constexpr int OP = BT * kGK * 2;           // bytes of one operand block
+    static constexpr int STAGE = 2 * OP;              // W block, then O block
+    static constexpr int LPW = BT / 16 / NW;          // 1 KB loads per wave and operand
+    static constexpr int WSIDE = NW == 16 ? 4 : 2;    // wavefronts per side
+    static constexpr int WT = BT / WSIDE;             // wavefront tile side
+    static constexpr int TW = WT / 16;                // MFMA tiles per side
+};
+
+template <int BT, int NW, int D, typename T>
+__global__ __launch_bounds__(NW * 64) void out_proj_ring(ProjArgs<T> a) {
     using F = Frag<T>;
     using frag = typename F::type;
-    __shared__ __attribute__((aligned(16))) char st0[kGStage], st1[kGStage];
-    __shared__ __attribute__((aligned(16))) char st2[kGStage], st3[kGStage];
+    using R = Ring<BT, NW>;
+    constexpr int TW = R::TW, LPW = R::LPW;
+    __shared__ __attribute__((aligned(16))) char st0[R::STAGE], st1[R::STAGE];
+    __shared__ __attribute__((aligned(16))) char st2[R::STAGE], st3[R::STAGE];
     const int t = threadIdx.x, l = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lq = l & 15, g = l >> 4;
@@ -222,7 +231,7 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
     // contiguous range of tiles in row-grouped order (4 row blocks, then
     // every column block), so that its concurrent workgroups share their O
     // rows and W columns in its L2 instead of every XCD streaming all of O.
-    const int mt = (a.M + kGB - 1) / kGB, nt = a.N / kGB;
+    const int mt = (a.M + BT - 1) / BT, nt = a.N / BT;
     int tm, tn;
     {
         const int nt_all = mt * nt, i = blockIdx.x;
@@ -233,19 +242,20 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
         tm = first + r % gs;
         tn = r / gs;
     }
-    const int n0 = tn * kGB, m0 = tm * kGB;
-    const int wn = 64 * (w & 3), wm = 64 * (w >> 2);
+    const int n0 = tn * BT, m0 = tm * BT;
+    const int wn = R::WT * (w % R::WSIDE), wm = R::WT * (w / R::WSIDE);
 
-    // loads: wave w fills rows 16w .. 16w+15 of both operand blocks, lane l
-    // row 16w + l / 4, chunk position l % 4
-    const int row = 16 * w + (l >> 2);
-    const int cs = (l & 3) ^ ((row >> 2) & 3);  // the chunk stored there
-    const uint32_t wo = 2u * (uint32_t)((size_t)(n0 + row) * a.K + 8 * cs);
-    uint32_t oo;
-    {
+    // loads: wave w's instruction i fills rows 16 (LPW w + i) .. +15 of both
+    // operand blocks, lane l row 16 (LPW w + i) + l / 4, chunk position l % 4
+    uint32_t wo[LPW], oo[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int row = 16 * (LPW * w + i) + (l >> 2);
+        const int cs = (l & 3) ^ ((row >> 2) & 3);  // the chunk stored there
+        wo[i] = 2u * (uint32_t)((size_t)(n0 + row) * a.K + 8 * cs);
         const int m = min(m0 + row, a.M - 1);  // rows past M read row M-1
         const int b = m / a.S, s = m - b * a.S;
-        oo = 2u * (uint32_t)(((size_t)b * a.H * a.S + s) * D + 8 * cs);
+        oo[i] = 2u * (uint32_t)(((size_t)b * a.H * a.S + s) * D + 8 * cs);
     }
     const char *Wb = reinterpret_cast<const char *>(a.W);
     const char *Ob = reinterpret_cast<const char *>(a.O);
@@ -255,17 +265,29 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
         const int k0 = kb * kGK, h = k0 / D;
         return uniform_ptr(Ob + 2 * ((size_t)h * a.S * D + (k0 - h * D)));
     };
+    auto load = [&](char *stage, int kb) __attribute__((always_inline)) {
+        const char *wp = wk(kb), *op = ok(kb);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(wp + wo[i]),
+                                             (lds_void_t *)(stage + 1024 * (LPW * w + i)),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(op + oo[i]),
+                                             (lds_void_t *)(stage + R::OP + 1024 * (LPW * w + i)),
+                                             16, 0, 0);
+        }
+    };
 
     // operand reads: rows wn + 16 i + lq (W) and wm + 16 j + lq (O), chunk
     // g (k = 8g .. 8g+7); the swizzle depends on lq only
     const int sx = (g ^ ((lq >> 2) & 3)) * 16;
-    const int rw = (wn + lq) * 64 + sx, ro = kGOp + (wm + lq) * 64 + sx;
+    const int rw = (wn + lq) * 64 + sx, ro = R::OP + (wm + lq) * 64 + sx;
 
-    f4_t acc[4][4];
+    f4_t acc[TW][TW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TW; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nk = a.K / kGK;
     // stage i's buffer, i a compile-time constant
@@ -273,23 +295,25 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
         constexpr int i = decltype(ic)::value & 3;
         return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3;
     };
-    // nk >= 4 (launch condition).  Every step issues the same two loads, so
-    // that the compiler's own wait before the operand reads can count them:
-    // past the last block a step reloads the last block into the stage it
-    // frees, which nothing reads again.
-    big_load<T>(st0, wk(0), ok(0), wo, oo, w);
-    big_load<T>(st1, wk(1), ok(1), wo, oo, w);
-    big_load<T>(st2, wk(2), ok(2), wo, oo, w);
+    // nk is a multiple of 4 (launch condition).  Every step issues the same
+    // loads, so that the count of each wait is fixed: past the last block a
+    // step reloads the last block into the stage it frees, which nothing
+    // reads again.
+    load(st0, 0);
+    load(st1, 1);
+    load(st2, 2);
 
     auto step = [&](int kb, auto sc) __attribute__((always_inline)) {
         constexpr int S_ = decltype(sc)::value;
         // keep each block's reads and products inside its step (the
-        // scheduler would otherwise hoist later blocks' operands and run
-        // out of registers)
+        // scheduler would otherwise hoist later blocks' operands)
         __builtin_amdgcn_sched_barrier(0);
         // this wave's loads of block kb are in; the two later blocks'
-        // loads stay in flight
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        // loads (2 LPW each) stay in flight
+        if constexpr (LPW == 1)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         // every wave's block kb is in, and every wave is done with block
         // kb - 1, whose stage block kb + 3 takes.  A bare s_barrier: the
         // workgroup fence of __syncthreads would wait for the later blocks'
@@ -299,39 +323,44 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int kn = min(kb + 3, nk - 1);
-        big_load<T>(stage(std::integral_constant<int, S_ + 3>()), wk(kn), ok(kn), wo, oo, w);
+        load(stage(std::integral_constant<int, S_ + 3>()), min(kb + 3, nk - 1));
         const uint32_t aw = lds_addr(stage(std::integral_constant<int, S_>())) + rw;
         const uint32_t ao = aw - rw + ro;
-        frag fw[4], fo[4];
+        frag fw[TW], fo[TW];
         lds_read16<0>(fw[0], aw);
         lds_read16<1024>(fw[1], aw);
-        lds_read16<2048>(fw[2], aw);
-        lds_read16<3072>(fw[3], aw);
+        if constexpr (TW == 4) {
+            lds_read16<2048>(fw[2], aw);
+            lds_read16<3072>(fw[3], aw);
+        }
         lds_read16<0>(fo[0], ao);
         lds_read16<1024>(fo[1], ao);
-        lds_read16<2048>(fo[2], ao);
-        lds_read16<3072>(fo[3], ao);
+        if constexpr (TW == 4) {
+            lds_read16<2048>(fo[2], ao);
+            lds_read16<3072>(fo[3], ao);
+        }
         // LDS reads return in order: the products of O fragment j start as
         // soon as it is in (after the W fragments), while the later reads
-        // are still on their way.  Each wait names the fragments it makes
-        // ready, which ties their products to it.
-        asm volatile("s_waitcnt lgkmcnt(3)"
-                     : "+v"(fw[0]), "+v"(fw[1]), "+v"(fw[2]), "+v"(fw[3]), "+v"(fo[0]));
+        // are still on their way.  The "+v" operands tie each fragment's
+        // products to its wait.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][0] = F::mfma(fw[i], fo[0], acc[i][0]);
-        __builtin_amdgcn_sched_barrier(0);  // these products before the next wait
-        asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(fo[1]));
+        for (int j = 0; j < TW; ++j) {
+            if (j == 0) {
+                lds_wait_asm<TW - 1>();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][1] = F::mfma(fw[i], fo[1], acc[i][1]);
-        __builtin_amdgcn_sched_barrier(0);  // these products before the next wait
-        asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(fo[2]));
+                for (int i = 0; i < TW; ++i) asm volatile("" : "+v"(fw[i]));
+            } else if (j == 1) {
+                lds_wait_asm<TW - 2>();
+            } else if (j == 2) {
+                lds_wait_asm<(TW > 2 ? TW - 3 : 0)>();
+            } else {
+                lds_wait_asm<0>();
+            }
+            asm volatile("" : "+v"(fo[j]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][2] = F::mfma(fw[i], fo[2], acc[i][2]);
-        __builtin_amdgcn_sched_barrier(0);  // these products before the next wait
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fo[3]));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][3] = F::mfma(fw[i], fo[3], acc[i][3]);
+            for (int i = 0; i < TW; ++i) acc[i][j] = F::mfma(fw[i], fo[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);  // these products before the next wait
+        }
     };
     for (int kb = 0; kb < nk; kb += 4) {  // nk % 4 == 0 (launch condition)
         step(kb, std::integral_constant<int, 0>());
@@ -346,11 +375,11 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
     // epilogue: lane holds out[m][n .. n+3], m = wm + 16j + lq,
     // n = wn + 16i + 4g
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TW; ++j) {
         const int m = m0 + wm + 16 * j + lq;
         if (m >= a.M) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TW; ++i) {
             const int n = n0 + wn + 16 * i + 4 * g;
             f4_t v = acc[i][j];
             if (a.bias) {
@@ -365,6 +394,16 @@ __global__ __launch_bounds__(1024) void out_proj_big(ProjArgs<T> a) {
             store4<T>(a.out + (size_t)m * a.N + n, v);
         }
     }
+}
+
+template <int BT, int NW, typename T>
+hipError_t launch_ring(const ProjArgs<T> &a, hipStream_t stream) {
+    dim3 grid((unsigned)((a.N / BT) * ((a.M + BT - 1) / BT)));
+    if (a.d == 64)
+        hipLaunchKernelGGL((out_proj_ring<BT, NW, 64, T>), grid, dim3(NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((out_proj_ring<BT, NW, 128, T>), grid, dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <int BT, int P, typename T>
@@ -394,23 +433,21 @@ hipError_t launch_t(const void *o, const void *w, const void *bias,
     a.d = d;
     a.K = H * d;
     a.N = D;
-    // the bigger tile when it divides N and still gives every CU a
-    // workgroup (measured at M = 4096, N = K = 768: 768 workgroups of
-    // 64 x 64 take 15.5 us, 192 of 128 x 128 take 22.4 us)
-    // 256 x 256 tiles when they divide N, still give every CU a workgroup,
-    // K is a multiple of four k blocks and every byte offset of a lane fits
-    // 32 bits
-    const long long huge = (long long)((a.M + 255) / 256) * (D / 256);
-    if (D % 256 == 0 && huge >= 256 && a.K % (4 * kGK) == 0 &&
-        (size_t)a.M * a.K * 2 < (1ull << 32) &&
+    // The ring kernel when K is a multiple of four k blocks and every byte
+    // offset of a lane fits 32 bits: 256 x 256 tiles when they divide N and
+    // still give every CU a workgroup, else 128 x 128 on the same terms,
+    // else 64 x 64.
+    if (a.K % (4 * kGK) == 0 && (size_t)a.M * a.K * 2 < (1ull << 32) &&
         (size_t)D * a.K * 2 < (1ull << 32)) {
-        dim3 grid((unsigned)((D / 256) * ((a.M + 255) / 256)));
-        if (d == 64)
-            hipLaunchKernelGGL((out_proj_big<64, T>), grid, dim3(1024), 0, stream, a);
-        else
-            hipLaunchKernelGGL((out_proj_big<128, T>), grid, dim3(1024), 0, stream, a);
-        return hipGetLastError();
+        const long long t256 = (long long)((a.M + 255) / 256) * (D / 256);
+        const long long t128 = (long long)((a.M + 127) / 128) * (D / 128);
+        if (D % 256 == 0 && t256 >= 256) return launch_ring<256, 16, T>(a, stream);
+        if (D % 128 == 0 && t128 >= 256) return launch_ring<128, 4, T>(a, stream);
+        return launch_ring<64, 4, T>(a, stream);
     }
+    // else the register-staged kernel: the bigger tile when it divides N and
+    // still gives every CU a workgroup (measured at M = 4096, N = K = 768:
+    // 768 workgroups of 64 x 64 take 15.5 us, 192 of 128 x 128 take 22.4 us)
     const long long big = (long long)((a.M + 127) / 128) * (D / 128);
     if (D % 128 == 0 && big >= 256) return launch_bt<128, 1, T>(a, stream);
     return launch_bt<64, 1, T>(a, stream);

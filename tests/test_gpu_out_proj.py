@@ -50,6 +50,9 @@ def check(got, o, w, b, r, dt):
     (2, 12, 512, 64, 768, "f16"),       # BERT-base shaped
     (1, 4, 33, 128, 256, "bf16"),
     (4, 32, 70, 128, 512, "bf16"),      # K = 4096
+    # 128 x 128 tiles (>= 256 of them, fewer than 256 of 256 x 256)
+    (2, 4, 2048, 64, 1024, "f16"),
+    (1, 2, 4000, 128, 1024, "bf16"),    # ragged last row tile
     # 256 x 256 tiles (N % 256 == 0, >= 256 workgroups, K % 128 == 0)
     (2, 4, 2000, 64, 4096, "f16"),      # ragged last row tile (M = 4000)
     (1, 8, 4096, 128, 4096, "bf16"),    # K = 1024: the stage ring wraps
