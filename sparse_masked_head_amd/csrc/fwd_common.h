@@ -15,6 +15,18 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+// p as a wave-uniform value (two v_readfirstlane; p must be the same in
+// every lane): the compiler then keeps such a base in scalar registers and
+// adds each lane's fixed 32-bit offset in the load itself, instead of
+// carrying a 64-bit address per lane and load.
+template <typename P>
+__device__ __attribute__((always_inline)) inline P *uniform_ptr(P *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<P *>(((uint64_t)hi << 32) | lo);
+}
+
 // pointer types of the load-to-LDS builtin (global source, LDS destination)
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;

@@ -172,17 +172,6 @@ __global__ __launch_bounds__(256) void out_proj(ProjArgs<T> a) {
 // the loads into one stage then never hold up the reads of another.
 constexpr int kGK = 32;
 
-// p as a wave-uniform value (two v_readfirstlane): the compiler then keeps
-// a k block's base in scalar registers and adds each lane's fixed 32-bit
-// offset in the load itself, instead of carrying a 64-bit address per lane
-// and k block.
-__device__ __attribute__((always_inline)) inline const char *uniform_ptr(const char *p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
-}
-
 // 32-bit LDS address of a pointer into a __shared__ array.
 typedef __attribute__((address_space(3))) const char lds_char_t;
 __device__ __attribute__((always_inline)) inline uint32_t lds_addr(const char *p) {

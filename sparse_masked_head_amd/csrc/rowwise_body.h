@@ -137,20 +137,37 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
     }
     wave_lds_sync();
 
-    // P V: lane = output columns lane*E .. +E-1, 8 entries per batch, the
-    // next batch's V loads issued before this batch's products
-    constexpr int BATCH = 8;
+    // P V: lane = output columns lane*E .. +E-1, 4 entries per batch, the
+    // next batch's V loads issued before this batch's products (batches of 8
+    // hold more registers and measured slower: fewer wavefronts per SIMD)
+    constexpr int BATCH = 4;
     const TIn *vcol = Vh + lane * E;
-    float vv[2][BATCH][E];
+    TIn vv[2][BATCH][E];
+    // The loads are unconditional (an entry past the chunk reads key 0) and
+    // keep the raw values; the products convert them and use 0 for entries
+    // past the chunk.  A load under a condition, converted in place, ends up
+    // in a branch of its own with a wait for it, and the batch's loads
+    // would run one after another.
     auto load = [&](int slot, int b0) __attribute__((always_inline)) {
+        // a batch's loads stay where they are issued (hoisted together with
+        // later batches' they would hold too many registers)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             const int ei = b0 + u;
-            const int k = ei < n ? (int)(ring[(head + ei) & (CAP - 1)] & 0xFFFFFFu) : 0;
+            // the same entry in every lane: a scalar, so the load's address
+            // is a scalar base plus the lane's column offset
+            const uint32_t ent = __builtin_amdgcn_readfirstlane(ring[(head + ei) & (CAP - 1)]);
+            const int k = ei < n ? (int)(ent & 0xFFFFFFu) : 0;
+            typedef __attribute__((address_space(1))) const TIn gbl_t;
+            gbl_t *vk = (gbl_t *)uniform_ptr(Vh + (size_t)k * D);
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                vv[slot][u][e] = ei < n ? (float)vcol[(size_t)k * D + e] : 0.f;
+            for (int e = 0; e < E; ++e) vv[slot][u][e] = vk[lane * E + e];
         }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto val = [&](int ei, TIn x) __attribute__((always_inline)) {
+        return ei < n ? (float)x : 0.f;
     };
     load(0, 0);
     for (int b0 = 0; b0 < n; b0 += 2 * BATCH) {
@@ -163,7 +180,8 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int e = 0; e < E; ++e) st.o[r][e] = fmaf(pr[r], vv[0][u][e], st.o[r][e]);
+                for (int e = 0; e < E; ++e)
+                    st.o[r][e] = fmaf(pr[r], val(b0 + u, vv[0][u][e]), st.o[r][e]);
         }
         if (b0 + BATCH >= n) break;
         if (b0 + 2 * BATCH < n) load(0, b0 + 2 * BATCH);
@@ -176,7 +194,8 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int e = 0; e < E; ++e) st.o[r][e] = fmaf(pr[r], vv[1][u][e], st.o[r][e]);
+                for (int e = 0; e < E; ++e)
+                    st.o[r][e] = fmaf(pr[r], val(ei, vv[1][u][e]), st.o[r][e]);
         }
     }
 }
@@ -273,7 +292,8 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
         J_cur = J_nxt;
         w_cur = w_nxt;
     }
-    if (tail != head) rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qbuf, pbuf, Kh, Vh, a.c);
+    if (tail != head)
+        rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qbuf, pbuf, Kh, Vh, a.c);
 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
