@@ -106,6 +106,29 @@ __device__ __attribute__((always_inline)) inline void load_tile(
                                          16, 0, 0);
 }
 
+// The chunks load_tile would bring in for this lane, into registers
+// instead (ordinary global loads, which the compiler waits for before the
+// registers are used), and their later store to the chunk positions
+// load_tile fills.
+template <int D> struct TileRegs {
+    u4_t c[D / 32];
+};
+template <int D>
+__device__ __attribute__((always_inline)) inline void load_tile_regs(
+    TileRegs<D> &rg, const char *tile, uint32_t lim, const TileOffs<D> &to) {
+    typedef __attribute__((address_space(1))) const u4_t gbl_u4_t;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+        rg.c[i] = *(gbl_u4_t *)(tile + min(to.off[i], lim));
+}
+template <int D>
+__device__ __attribute__((always_inline)) inline void store_tile_regs(
+    char *buf, const TileRegs<D> &rg, int w, int l) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+        *reinterpret_cast<u4_t *>(buf + 1024 * (4 * i + w) + 16 * l) = rg.c[i];
+}
+
 // This lane's mask bytes of a partial tile (global loads into registers):
 // keys 16st + 4g + i of query row r are bits 4(g&1)+i of byte r&7 of inner
 // tile (r>>3, 2st + (g>>1)); b_off is that byte's offset for st = 0, each
@@ -120,6 +143,14 @@ __device__ __attribute__((always_inline)) inline void load_mask(
 #pragma unroll
         for (int st = 0; st < 4; ++st) m.mb[st] = wb[16 * st];
     }
+}
+
+// The same four loads from `src` (the lane's first mask byte, or any
+// readable address when the bytes are not used), issued unconditionally.
+__device__ __attribute__((always_inline)) inline void load_mask_at(
+    MaskRegs &m, const uint8_t *src) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) m.mb[st] = src[16 * st];
 }
 
 // The lane's mask bits of a partial tile: bit 8st + i (i < 4) = key
@@ -142,6 +173,22 @@ template <int off> __device__ __attribute__((always_inline)) inline int bit_mask
 // among them), before the barrier that hands their buffers to every wave.
 __device__ __attribute__((always_inline)) inline void wait_loads() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// Wait until at most N (< 64) of this wave's global loads are outstanding.
+// The builtin rather than inline assembly, so that the compiler knows those
+// loads are complete and adds no wait of its own before their data is used.
+// Encoding: vmcnt bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at
+// their maxima, i.e. not waited for.
+template <int N> __device__ __attribute__((always_inline)) inline void wait_loads_but() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_barrier without the workgroup fence of __syncthreads (which would also
+// wait for every global load still in flight).
+__device__ __attribute__((always_inline)) inline void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Running state of one lane: O^T accumulators of its query (d = 16dt +
@@ -411,49 +458,107 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     auto load_v = [&](char *buf, int J) __attribute__((always_inline)) {
         load_tile<D>(buf, Vb + (size_t)J * 64 * D * 2, tl.lim<D>(J), to, wu);
     };
-    // columns of the K tile (jk, tile it+2) and V tile (jv, tile it+1) that
-    // tile step it loads
-    int jv = tl.clamp(ri.c[1]), jk = tl.clamp(ri.c[2]);
-    if (nT > 0) {
-        load_k(bufs.k[0], mk0, 0, tl.clamp(ri.c[0]));
-        load_v(bufs.v[0], tl.clamp(ri.c[0]));
-        if (nT > 1) load_k(bufs.k[1], mk1, 1, jv);
-    }
-    wait_loads();
-    if (nT > 0 && nF == 0) m_a = mask_bits(mk0, nib);
-    if (nT > 1 && 1 >= nF) m_b = mask_bits(mk1, nib);
-    __syncthreads();
-    if (nT > 0) qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a);
-    // every wave has read K(0) before tile step 0 loads into its buffer
-    __syncthreads();
-
-    // One tile step (cb = it & 1, a compile-time constant): scores of tile
-    // it in `cur` (mask mc), of tile it+1 go to `nxt` (mask mn); mc is then
-    // reused for tile it+2's mask.
-    auto step = [&](int it, auto cbc, f4_t(&cur)[4], f4_t(&nxt)[4], uint32_t &mc,
-                    const uint32_t mn) __attribute__((always_inline)) {
-        constexpr int cb = decltype(cbc)::value, nb = cb ^ 1;
-        // column of tile it+3 (tile step it+1 loads its K); from memory past
-        // the four of the row summary
-        int jn_raw = ri.c[3];
-        if (it + 3 < nT && it + 3 >= 4) jn_raw = *tl.col_ptr(it + 3);
-        // K(it+2) replaces K(it) (read in the previous step); V(it+1)
-        // replaces V(it-1) (read in the previous step)
-        if (it + 2 < nT) load_k(bufs.k[cb], mk0, it + 2, jk);
-        if (it + 1 < nT) load_v(bufs.v[nb], jv);
-        if (it + 1 < nT)
-            qk_tile<D, TIn>(nxt, qf, bufs.k[nb], ko, it + 1 >= nF, mn);
-        softmax_pv<D, TIn>(rs, cur, bufs.v[cb], a.c, vo);
+    if (nT >= 1 && nT <= 3) {
+        // A row of at most three tiles requests all of them at once: tiles
+        // 0 and 1 into the four buffers, tile 2 into registers, stored into
+        // the buffers of tile 0 once every wave is done with them.  The row
+        // then waits for memory once instead of once per tile (such rows
+        // are common at small S, where all workgroups of a launch start
+        // together and each wait is a full memory round trip).  Every load
+        // is issued whatever nT and the tile kinds are (a missing tile
+        // re-reads tile 0; a full tile's mask bytes come from the row
+        // summary and go unused), so the loads are one fixed sequence and a
+        // constant count waits for exactly those of tiles 0 and 1.  Tiles
+        // go through the softmax in the loop's order (same results).
+        const int c0 = tl.clamp(ri.c[0]);
+        const int c1 = nT > 1 ? tl.clamp(ri.c[1]) : c0;
+        const int c2 = nT > 2 ? tl.clamp(ri.c[2]) : c0;
+        const uint8_t *any_src = reinterpret_cast<const uint8_t *>(a.info);
+        auto mask_src = [&](int idx) __attribute__((always_inline)) {
+            return idx < nT && idx >= nF
+                       ? reinterpret_cast<const uint8_t *>(tl.words(idx)) + b_off
+                       : any_src;
+        };
+        TileRegs<D> k2, v2;
+        MaskRegs mk2;
+        load_tile<D>(bufs.k[0], Kb + (size_t)c0 * 64 * D * 2, tl.lim<D>(c0), to, wu);
+        load_mask_at(mk0, mask_src(0));
+        load_tile<D>(bufs.v[0], Vb + (size_t)c0 * 64 * D * 2, tl.lim<D>(c0), to, wu);
+        load_tile<D>(bufs.k[1], Kb + (size_t)c1 * 64 * D * 2, tl.lim<D>(c1), to, wu);
+        load_mask_at(mk1, mask_src(1));
+        load_tile<D>(bufs.v[1], Vb + (size_t)c1 * 64 * D * 2, tl.lim<D>(c1), to, wu);
+        // tile 2's loads after all of those (the wait below counts on it)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile_regs<D>(k2, Kb + (size_t)c2 * 64 * D * 2, tl.lim<D>(c2), to);
+        load_mask_at(mk2, mask_src(2));
+        load_tile_regs<D>(v2, Vb + (size_t)c2 * 64 * D * 2, tl.lim<D>(c2), to);
+        __builtin_amdgcn_sched_barrier(0);
+        // tiles 0 and 1 are in; tile 2's 2 * D/32 chunk loads and 4 mask
+        // byte loads stay in flight
+        wait_loads_but<2 * (D / 32) + 4>();
+        m_a = nF == 0 ? mask_bits(mk0, nib) : 0u;
+        m_b = nT > 1 && nF <= 1 ? mask_bits(mk1, nib) : 0u;
+        bare_barrier();
+        qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a);
+        if (nT > 1) qk_tile<D, TIn>(s_b, qf, bufs.k[1], ko, nF <= 1, m_b);
+        softmax_pv<D, TIn>(rs, s_a, bufs.v[0], a.c, vo);
+        if (nT > 2) {
+            const uint32_t m_c = nF <= 2 ? mask_bits(mk2, nib) : 0u;
+            bare_barrier();  // every wave is done with K(0) and V(0)
+            store_tile_regs<D>(bufs.k[0], k2, wu, l);
+            store_tile_regs<D>(bufs.v[0], v2, wu, l);
+            __syncthreads();
+            qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF <= 2, m_c);
+        }
+        if (nT > 1) softmax_pv<D, TIn>(rs, s_b, bufs.v[1], a.c, vo);
+        if (nT > 2) softmax_pv<D, TIn>(rs, s_a, bufs.v[0], a.c, vo);
+    } else {
+        // columns of the K tile (jk, tile it+2) and V tile (jv, tile it+1) that
+        // tile step it loads
+        int jv = tl.clamp(ri.c[1]), jk = tl.clamp(ri.c[2]);
+        if (nT > 0) {
+            load_k(bufs.k[0], mk0, 0, tl.clamp(ri.c[0]));
+            load_v(bufs.v[0], tl.clamp(ri.c[0]));
+            if (nT > 1) load_k(bufs.k[1], mk1, 1, jv);
+        }
         wait_loads();
-        mc = it + 2 < nT && it + 2 >= nF ? mask_bits(mk0, nib) : 0u;
-        jv = jk;
-        jk = tl.clamp(__builtin_amdgcn_readfirstlane(jn_raw));
+        if (nT > 0 && nF == 0) m_a = mask_bits(mk0, nib);
+        if (nT > 1 && 1 >= nF) m_b = mask_bits(mk1, nib);
         __syncthreads();
-    };
-    for (int it = 0; it < nT; it += 2) {
-        step(it, std::integral_constant<int, 0>(), s_a, s_b, m_a, m_b);
-        if (it + 1 >= nT) break;
-        step(it + 1, std::integral_constant<int, 1>(), s_b, s_a, m_b, m_a);
+        if (nT > 0) qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a);
+        // every wave has read K(0) before tile step 0 loads into its buffer
+        __syncthreads();
+
+        // One tile step (cb = it & 1, a compile-time constant): scores of tile
+        // it in `cur` (mask mc), of tile it+1 go to `nxt` (mask mn); mc is then
+        // reused for tile it+2's mask.
+        auto step = [&](int it, auto cbc, f4_t(&cur)[4], f4_t(&nxt)[4], uint32_t &mc,
+                        const uint32_t mn) __attribute__((always_inline)) {
+            constexpr int cb = decltype(cbc)::value, nb = cb ^ 1;
+            // column of tile it+3 (tile step it+1 loads its K); from memory past
+            // the four of the row summary
+            int jn_raw = ri.c[3];
+            if (it + 3 < nT && it + 3 >= 4) jn_raw = *tl.col_ptr(it + 3);
+            // K(it+2) replaces K(it) (read in the previous step); V(it+1)
+            // replaces V(it-1) (read in the previous step)
+            if (it + 2 < nT) load_k(bufs.k[cb], mk0, it + 2, jk);
+            if (it + 1 < nT) load_v(bufs.v[nb], jv);
+            if (it + 1 < nT)
+                qk_tile<D, TIn>(nxt, qf, bufs.k[nb], ko, it + 1 >= nF, mn);
+            softmax_pv<D, TIn>(rs, cur, bufs.v[cb], a.c, vo);
+            wait_loads();
+            mc = it + 2 < nT && it + 2 >= nF ? mask_bits(mk0, nib) : 0u;
+            jv = jk;
+            jk = tl.clamp(__builtin_amdgcn_readfirstlane(jn_raw));
+            __syncthreads();
+        };
+        for (int it = 0; it < nT; it += 2) {
+            step(it, std::integral_constant<int, 0>(), s_a, s_b, m_a, m_b);
+            if (it + 1 >= nT) break;
+            step(it + 1, std::integral_constant<int, 1>(), s_b, s_a, m_b, m_a);
+        }
+
     }
 
     // epilogue: total l over the 4 lanes of this query
