@@ -445,8 +445,11 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     // and mask slots swap roles instead of being copied.
     const int wu = __builtin_amdgcn_readfirstlane(w);  // w, known uniform
     const TileOffs<D> to = tile_offsets<D>(wu, l);
-    const char *Kb = reinterpret_cast<const char *>(Kh);
-    const char *Vb = reinterpret_cast<const char *>(Vh);
+    // the K and V bases in scalar registers, whatever else in the kernel
+    // uses the same values per lane (the tile addresses are then scalar
+    // arithmetic and the loads take the scalar-base form)
+    const char *Kb = reinterpret_cast<const char *>(uniform_ptr(Kh));
+    const char *Vb = reinterpret_cast<const char *>(uniform_ptr(Vh));
     MaskRegs mk0, mk1;
     f4_t s_a[4], s_b[4];
     uint32_t m_a = 0, m_b = 0;

@@ -13,9 +13,9 @@
 // wavefront never executes s_barrier; it uses its own slice of LDS.  Its
 // work follows the live keys, not the stored tiles:
 //   * gather: 8 stored tiles per step, lane = (tile, inner-tile column ic);
-//     the lane's 64-bit word transposed as an 8x8 bit matrix gives, in byte
-//     c, the set of rows that see key 8ic + c (all rows for a full tile);
-//     every key with a non-empty set is appended to a ring of pending
+//     the OR of the bytes of the lane's 64-bit word gives the keys 8ic + c
+//     that some row sees (all of them for a full tile), and for each such
+//     key the set of rows seeing it is appended to a ring of pending
 //     entries (rows << 24 | key) in LDS (a wave prefix sum places them);
 //   * chunks of 64 entries, lane = entry: the lane's K row against the 8
 //     query rows (v_dot2, fp32 accumulation; pairs outside the mask -inf),
@@ -44,22 +44,41 @@ template <int D> struct RowLds {
     static constexpr int BYTES = Q_BYTES + RING_BYTES + P_BYTES;
 };
 
-// 8x8 bit-matrix transpose: bit 8r + c -> bit 8c + r (three delta swaps).
-__device__ inline uint64_t transpose8x8(uint64_t x) {
-    uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
-    x = x ^ t ^ (t << 7);
-    t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
-    x = x ^ t ^ (t << 14);
-    t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
-    return x ^ t ^ (t << 28);
+// The columns of an inner tile that some of its rows see: bit c set iff
+// bit c of any byte of w is (byte r of w is row r).
+__device__ inline uint32_t live_columns(uint64_t w) {
+    uint32_t t = (uint32_t)w | (uint32_t)(w >> 32);
+    t |= t >> 16;
+    t |= t >> 8;
+    return t & 0xFFu;
 }
 
-// Bit b set iff byte b of x is nonzero (b < 8).
-__device__ inline uint32_t nonzero_byte_mask(uint64_t x) {
-    uint32_t m = 0;
+// Exclusive prefix sum over the wavefront of a per-lane count below 16,
+// and the wavefront's total: the count's four bits as ballots, v_mbcnt
+// counting the lanes below this one in each (no cross-lane data moves).
+__device__ inline int wave_prefix16(int cnt, int &total) {
+    int excl = 0, tot = 0;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) m |= (uint32_t)(((x >> (8 * b)) & 0xFFu) != 0) << b;
-    return m;
+    for (int b = 0; b < 4; ++b) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64((cnt >> b) & 1);
+        excl += (int)__builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))
+                << b;
+        tot += __popcll(m) << b;
+    }
+    total = tot;
+    return excl;
+}
+
+// The rows of an inner tile that see its column c: bit r = bit 8r + c of
+// w.  Each 32-bit half holds four rows; after the shift and mask their bits
+// sit at 0, 8, 16, 24, and the multiply by 2^24 + 2^17 + 2^10 + 2^3 moves
+// them to bits 24..27 (the other partial products land below bit 24 at
+// distinct places, so nothing carries into those bits).
+__device__ inline uint32_t column_rows(uint64_t w, int c) {
+    const uint32_t lo = ((uint32_t)w >> c) & 0x01010101u;
+    const uint32_t hi = ((uint32_t)(w >> 32) >> c) & 0x01010101u;
+    return ((lo * 0x01020408u) >> 24) | (((hi * 0x01020408u) >> 24) << 4);
 }
 
 // Softmax state of the wavefront's 8 rows (lane-local partial sums; the
@@ -240,47 +259,42 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
     wave_lds_sync();
 
     // gather step: tile t0 + lane/8, inner-tile column lane%8; the loads of
-    // the next step are issued before this step's work
+    // the next step are issued before this step's work.  They are
+    // unconditional (a lane past the row, or a full tile's word, reads the
+    // row summary instead) and their values are replaced and clamped where
+    // they are used, and the loop is unrolled by two so that the next
+    // step's registers are never copied: a load made conditional, a value
+    // changed where it is loaded, or a copy of the register makes the
+    // compiler wait for the load right there (a full round trip per step).
     const int ic = lane & 7;
-    auto fetch = [&](int t0, int &J, uint64_t &w) __attribute__((always_inline)) {
+    const int32_t *any32 = a.info;
+    const uint64_t *any64 = reinterpret_cast<const uint64_t *>(a.info);
+    auto fetch = [&](int t0, int32_t &jr, uint64_t &wr) __attribute__((always_inline)) {
         const int tile = t0 + (lane >> 3);
-        J = 0;
-        w = 0;
-        if (tile < nT) {
-            if (tile < nF) {
-                J = a.fci[f0 + tile];
-                w = ~0ull;
-            } else {
-                const int p = p0 + tile - nF;
-                J = a.pci[p];
-                w = a.bm[(size_t)p * 64 + ir * 8 + ic];
-            }
-        }
-        J = (int)min((unsigned)J, (unsigned)nmax);  // never outside K / V
+        const bool full = tile < nF, part = tile >= nF && tile < nT;
+        const int32_t *jp = full ? a.fci + f0 + tile
+                                 : part ? a.pci + p0 + (tile - nF) : any32;
+        const uint64_t *wp =
+            part ? a.bm + (size_t)(p0 + tile - nF) * 64 + ir * 8 + ic : any64;
+        jr = *jp;
+        wr = *wp;
     };
     uint32_t head = 0, tail = 0;  // ring positions (uniform)
-    int J_cur, J_nxt = 0;
-    uint64_t w_cur, w_nxt = 0;
-    fetch(0, J_cur, w_cur);
-    for (int t0 = 0; t0 < nT; t0 += 8) {
-        if (t0 + 8 < nT) fetch(t0 + 8, J_nxt, w_nxt);
-        const uint64_t x = transpose8x8(w_cur);  // byte c: rows seeing key 8ic+c
-        const uint32_t nzb = nonzero_byte_mask(x);
-        const int cnt = __popc(nzb);
-        int incl = cnt;  // inclusive prefix over lanes
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(incl, d);
-            if (lane >= d) incl += y;
-        }
-        const int total = __shfl(incl, 63);
-        uint32_t pos = tail + (uint32_t)(incl - cnt);
+    auto step = [&](int t0, const int32_t jr, const uint64_t wr, int32_t &jn,
+                    uint64_t &wn) __attribute__((always_inline)) {
+        fetch(t0 + 8, jn, wn);  // past the row: the row summary, unused
+        const int tile = t0 + (lane >> 3);
+        const int J = (int)min((unsigned)jr, (unsigned)nmax);  // never outside K, V
+        const uint64_t w = tile >= nT ? 0ull : tile < nF ? ~0ull : wr;
+        const uint32_t nzb = live_columns(w);
+        int total;
+        uint32_t pos = tail + (uint32_t)wave_prefix16(__popc(nzb), total);
         uint32_t m = nzb;
         while (m) {
             const int cb = __builtin_ctz(m);
             m &= m - 1;
-            const uint32_t rbits = (uint32_t)(x >> (8 * cb)) & 0xFFu;
-            ring[pos & (CAP - 1)] = (rbits << 24) | (uint32_t)(64 * J_cur + 8 * ic + cb);
+            const uint32_t rbits = column_rows(w, cb);
+            ring[pos & (CAP - 1)] = (rbits << 24) | (uint32_t)(64 * J + 8 * ic + cb);
             ++pos;
         }
         tail += (uint32_t)total;
@@ -289,8 +303,14 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
             rw_chunk<D, TIn>(st, ring, head, 64, qbuf, pbuf, Kh, Vh, a.c);
             head += 64;
         }
-        J_cur = J_nxt;
-        w_cur = w_nxt;
+    };
+    int32_t ja = 0, jb = 0;
+    uint64_t wa = 0, wb = 0;
+    fetch(0, ja, wa);
+    for (int t0 = 0; t0 < nT; t0 += 16) {
+        step(t0, ja, wa, jb, wb);
+        if (t0 + 8 >= nT) break;
+        step(t0 + 8, jb, wb, ja, wa);
     }
     if (tail != head)
         rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qbuf, pbuf, Kh, Vh, a.c);
