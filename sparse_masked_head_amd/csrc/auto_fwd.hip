@@ -17,12 +17,17 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TO
     __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
     const int oi = blockIdx.x / a.U;
     const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
+    // the block-wise path's Q rows, requested before the row summary so that
+    // they arrive during its round trip (under the row-wise choice the
+    // row-wise path reads the same rows again, from the caches)
+    typename Frag<TIn>::type qf[D / 32];
+    load_q_frags<D>(a, sl.I, sl.bh, qf);
     // the row summary carries the statistics the choice reads (both paths
     // need the summary)
     const RowInfo ri = load_row_info(a, sl.row);
     if (device_choice<D>(a, ri) == 2) {
         const TileBufs<D> bufs{{k0, k1}, {v0, v1}};
-        blockwise_row<D, TIn, TOut>(a, bufs, sl.I, sl.bh, ri);
+        blockwise_row<D, TIn, TOut>(a, bufs, sl.I, sl.bh, ri, qf);
     } else {
         // each wavefront's slice is one of the tile buffers
         const int w = threadIdx.x >> 6;

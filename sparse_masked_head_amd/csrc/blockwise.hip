@@ -13,7 +13,9 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TI
     // heavy rows first across all heads (slot_of)
     const int oi = blockIdx.x / a.U;
     const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
-    blockwise_row<D, TIn, TOut>(a, bufs, sl.I, sl.bh, load_row_info(a, sl.row));
+    typename Frag<TIn>::type qf[D / 32];
+    load_q_frags<D>(a, sl.I, sl.bh, qf);  // before the row summary's round trip
+    blockwise_row<D, TIn, TOut>(a, bufs, sl.I, sl.bh, load_row_info(a, sl.row), qf);
 }
 
 template <int D, typename TIn, typename TOut>

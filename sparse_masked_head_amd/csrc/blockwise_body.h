@@ -386,14 +386,32 @@ template <int D> struct TileBufs {
     char *k[2], *v[2];
 };
 
+// This lane's Q rows as the B operand of S^T = K Q^T for outer-tile row I
+// of head bh: query 64I + 16w + l%16, d = 32s + 8(l/16) + 0..7 (a query
+// past S, in a tile cut by S, reads query S-1 and is not stored).  Needs
+// only the slot, not the row summary, so a kernel issues these loads before
+// it reads the summary and they overlap its round trip.
+template <int D, typename TIn, typename TOut>
+__device__ __attribute__((always_inline)) inline void load_q_frags(
+    const FwdArgs<TIn, TOut> &a, int I, int bh,
+    typename Frag<TIn>::type (&qf)[D / 32]) {
+    using frag = typename Frag<TIn>::type;
+    const int t = threadIdx.x, l = t & 63;
+    const int qi = 64 * I + 16 * (t >> 6) + (l & 15);
+    const TIn *qrow = a.Q + (size_t)bh * a.S * D + (size_t)min(qi, a.S - 1) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+        qf[s] = *reinterpret_cast<const frag *>(qrow + 32 * s + 8 * (l >> 4));
+}
+
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void blockwise_row(
     const FwdArgs<TIn, TOut> &a, const TileBufs<D> &bufs, int I, int bh,
-    const RowInfo &ri) {
+    const RowInfo &ri, const typename Frag<TIn>::type (&qf)[D / 32]) {
     using frag = typename Frag<TIn>::type;
     using L = Lds<D>;
     const size_t head = (size_t)bh * a.S * D;
-    const TIn *Qh = a.Q + head, *Kh = a.K + head, *Vh = a.V + head;
+    const TIn *Kh = a.K + head, *Vh = a.V + head;
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int lq = l & 15, g = l >> 4;
@@ -411,16 +429,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     tl.nT = ri.nF + ri.nP;
     const int nT = tl.nT, nF = tl.nF;
 
-    // this lane's Q rows as the B operand: query r, d = 32s + 8g + 0..7
-    // (a query past S, in a tile cut by S, reads query S-1 and is not stored)
     const int qi = 64 * I + r;
-    frag qf[D / 32];
-    {
-        const TIn *qrow = Qh + (size_t)min(qi, a.S - 1) * D;
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-            qf[s] = *reinterpret_cast<const frag *>(qrow + 32 * s + 8 * g);
-    }
 
     RowState<D> rs;
 #pragma unroll

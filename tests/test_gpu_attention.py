@@ -156,7 +156,7 @@ def sample_rows(S, mask, rng, n=48):
 
 
 @pytest.mark.parametrize("kernel", ["auto", "blockwise", "rowwise"])
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7])
 def test_workloads_sampled(cid, kernel, config_mask):
     dev = need_gpu()
     cfg, mask, host, devt, enc, st = workload(cid, dev, config_mask)
