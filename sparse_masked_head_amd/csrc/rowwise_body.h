@@ -28,6 +28,8 @@
 // Probabilities stay in fp32 here.
 #pragma once
 
+#include <type_traits>
+
 #include "fwd_common.h"
 
 namespace smh {
@@ -161,7 +163,7 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
     // hold more registers and measured slower: fewer wavefronts per SIMD)
     constexpr int BATCH = 4;
     const TIn *vcol = Vh + lane * E;
-    TIn vv[2][BATCH][E];
+    TIn vv[3][BATCH][E];
     // The loads are unconditional (an entry past the chunk reads key 0) and
     // keep the raw values; the products convert them and use 0 for entries
     // past the chunk.  A load under a condition, converted in place, ends up
@@ -188,25 +190,12 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
     auto val = [&](int ei, TIn x) __attribute__((always_inline)) {
         return ei < n ? (float)x : 0.f;
     };
-    load(0, 0);
-    for (int b0 = 0; b0 < n; b0 += 2 * BATCH) {
-        if (b0 + BATCH < n) load(1, b0 + BATCH);
+    // products of batch b0 (its values in slot sl, a compile-time constant)
+    auto products = [&](auto slc, int b0) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const f4_t pa = *reinterpret_cast<const f4_t *>(pbuf + (b0 + u) * R);
-            const f4_t pb = *reinterpret_cast<const f4_t *>(pbuf + (b0 + u) * R + 4);
-            const float pr[R] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    st.o[r][e] = fmaf(pr[r], val(b0 + u, vv[0][u][e]), st.o[r][e]);
-        }
-        if (b0 + BATCH >= n) break;
-        if (b0 + 2 * BATCH < n) load(0, b0 + 2 * BATCH);
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int ei = b0 + BATCH + u;
+            const int ei = b0 + u;
             const f4_t pa = *reinterpret_cast<const f4_t *>(pbuf + ei * R);
             const f4_t pb = *reinterpret_cast<const f4_t *>(pbuf + ei * R + 4);
             const float pr[R] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
@@ -214,8 +203,29 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    st.o[r][e] = fmaf(pr[r], val(ei, vv[1][u][e]), st.o[r][e]);
+                    st.o[r][e] = fmaf(pr[r], val(ei, vv[sl][u][e]), st.o[r][e]);
         }
+    };
+    // three slots: the loads of batch b + 2 are issued before the products
+    // of batch b, so two batches' loads are in flight behind the one in use
+    // (with one, every batch waited for most of a memory round trip)
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    // (the loads are unconditional, past the chunk too, where they read key
+    // 0: a load under a condition makes the compiler wait for every load
+    // in flight where the paths join)
+    load(0, 0);
+    load(1, BATCH);
+    for (int b0 = 0; b0 < n; b0 += 3 * BATCH) {
+        load(2, b0 + 2 * BATCH);
+        products(C0(), b0);
+        if (b0 + BATCH >= n) break;
+        load(0, b0 + 3 * BATCH);
+        products(C1(), b0 + BATCH);
+        if (b0 + 2 * BATCH >= n) break;
+        load(1, b0 + 4 * BATCH);
+        products(C2(), b0 + 2 * BATCH);
     }
 }
 
