@@ -22,6 +22,15 @@ MASKS = [("random", {"p": 0.001}), ("random", {"p": 0.01}),
 SIZES = [256, 512, 1024, 2048, 4096]
 HEADS = [1, 8, 64]
 DIMS = [64, 128]
+# long sequences: fewer heads, and no dense mask (its row-wise time alone
+# would dominate the sweep)
+MASKS_LONG = [("random", {"p": 0.001}), ("random", {"p": 0.01}),
+              ("far_random", {"p": 0.02}), ("long_random", {}),
+              ("window", {"w": 64}), ("causal", {})]
+SIZES_LONG = [8192, 16384]
+HEADS_LONG = [1, 8, 32]
+# the decision rule of select_model: row-wise when t_row < ROW_MARGIN * t_blk
+ROW_MARGIN = 0.9
 
 
 def _time(fn, reps):
@@ -45,35 +54,39 @@ def sweep(out_path, quick=False):
     dev = torch.device("cuda:0")
     points = []
     sizes = SIZES[:3] if quick else SIZES
+    grid = [(fam, kw, S, HEADS) for fam, kw in MASKS for S in sizes]
+    if not quick:
+        grid += [(fam, kw, S, HEADS_LONG) for fam, kw in MASKS_LONG
+                 for S in SIZES_LONG]
     t0 = time.time()
-    for fam, kw in MASKS:
-        for S in sizes:
-            if fam == "bigbird" and S < 1024:
-                continue    # needs enough 64-wide blocks for 3 random picks
-            mask = mask_family(fam, S, seed=S, **kw)
-            m = torch.from_numpy(mask).to(dev)
-            enc = smh.encode_mask(m)
-            st = smh.mask_stats_get(enc)
-            for d in DIMS:
-                for BH in HEADS:
-                    if BH * S * d * 2 * 4 > (1 << 31):
-                        continue
-                    q = torch.randn(1, BH, S, d, device=dev).half()
-                    k = torch.randn_like(q)
-                    v = torch.randn_like(q)
-                    o = torch.empty_like(q)
-                    reps = 20 if S * BH < 65536 else 5
-                    t = {}
-                    for kern in ("rowwise", "blockwise"):
-                        t[kern] = _time(lambda: smh.sparse_mha_fwd(
-                            q, k, v, enc, kernel=kern, out=o), reps)
-                    points.append(dict(family=fam, kw=kw, S=S, d=d, BH=BH,
-                                       stats=st, t_row_us=t["rowwise"],
-                                       t_blk_us=t["blockwise"]))
-                    print(f"{fam:8s} {str(kw):14s} S={S:5d} d={d:3d} "
-                          f"BH={BH:3d} row {t['rowwise']:9.1f} us  blk "
-                          f"{t['blockwise']:9.1f} us  [{time.time()-t0:.0f}s]",
-                          flush=True)
+    for fam, kw, S, heads in grid:
+        if fam == "bigbird" and S < 1024:
+            continue    # needs enough 64-wide blocks for 3 random picks
+        mask = mask_family(fam, S, seed=S, **kw)
+        m = torch.from_numpy(mask).to(dev)
+        del mask
+        enc = smh.encode_mask(m)
+        st = smh.mask_stats_get(enc)
+        for d in DIMS:
+            for BH in heads:
+                if BH * S * d * 2 * 4 > (1 << 31):
+                    continue
+                q = torch.randn(1, BH, S, d, device=dev).half()
+                k = torch.randn_like(q)
+                v = torch.randn_like(q)
+                o = torch.empty_like(q)
+                reps = 20 if S * BH < 65536 else 5
+                t = {}
+                for kern in ("rowwise", "blockwise"):
+                    t[kern] = _time(lambda: smh.sparse_mha_fwd(
+                        q, k, v, enc, kernel=kern, out=o), reps)
+                points.append(dict(family=fam, kw=kw, S=S, d=d, BH=BH,
+                                   stats=st, t_row_us=t["rowwise"],
+                                   t_blk_us=t["blockwise"]))
+                print(f"{fam:8s} {str(kw):14s} S={S:5d} d={d:3d} "
+                      f"BH={BH:3d} row {t['rowwise']:9.1f} us  blk "
+                      f"{t['blockwise']:9.1f} us  [{time.time()-t0:.0f}s]",
+                      flush=True)
     with open(out_path, "w") as f:
         json.dump(points, f)
     return points
@@ -121,8 +134,9 @@ def fit(points):
         for p in pts:
             tr, tb = model(c, p)
             best = min(p["t_row_us"], p["t_blk_us"])
-            got = p["t_row_us"] if tr < tb else p["t_blk_us"]
-            agree += (tr < tb) == (p["t_row_us"] < p["t_blk_us"])
+            row = tr < ROW_MARGIN * tb
+            got = p["t_row_us"] if row else p["t_blk_us"]
+            agree += row == (p["t_row_us"] < p["t_blk_us"])
             regret += got - best
             best_sum += best
         out[d] = dict(coef=c.tolist(), rms_log=float(np.sqrt(np.mean(

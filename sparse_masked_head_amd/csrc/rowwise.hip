@@ -7,8 +7,8 @@ namespace smh {
 namespace {
 
 template <int D, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void rowwise_fwd(FwdArgs<TIn, TOut> a,
-                                                   long long n_groups) {
+__global__ __launch_bounds__(256, D == 64 ? 4 : 3) void rowwise_fwd(
+    FwdArgs<TIn, TOut> a, long long n_groups) {
     __shared__ __attribute__((aligned(16))) char lds[4 * RowLds<D>::BYTES];
     const int w = threadIdx.x >> 6;
     const long long gw = (long long)blockIdx.x * 4 + w;

@@ -17,15 +17,14 @@
 //     that some row sees (all of them for a full tile), and for each such
 //     key the set of rows seeing it is appended to a ring of pending
 //     entries (rows << 24 | key) in LDS (a wave prefix sum places them);
-//   * chunks of 64 entries, lane = entry: the lane's K row against the 8
-//     query rows (v_dot2, fp32 accumulation; pairs outside the mask -inf),
-//     online softmax per row with 64-lane DPP max reductions (a row with no
-//     key in the chunk is skipped), probabilities through LDS, then P V with
-//     lane = output column over the chunk's keys, 8 keys per batch with
-//     the next batch's V loads in flight.
+//   * chunks of 64 entries on the matrix cores (rw_chunk): the K rows and
+//     V columns of the chunk's keys are gathered straight into MFMA
+//     operands, S^T = K Q^T and O^T += V^T P^T with the 8 query rows as 8
+//     of the 16 MFMA columns, online softmax per row across the 4 lanes
+//     that share it, P rounded to the input type as in the block-wise
+//     kernel.
 // A wavefront thus touches K and V only for keys some of its rows see, in
 // full 64-key chunks, however the keys are spread over the tiles.
-// Probabilities stay in fp32 here.
 #pragma once
 
 #include <type_traits>
@@ -36,14 +35,12 @@ namespace smh {
 
 constexpr int kRowsPerWave = 8;
 
-// LDS of one wavefront: the 8 query rows, the ring of pending entries and
-// the probabilities of one chunk [64 entries][8 rows].
+// LDS of one wavefront: the 8 query rows and the ring of pending entries.
 template <int D> struct RowLds {
     static constexpr int CAP = 1024;  // > 63 pending + 8 full tiles (512)
     static constexpr int Q_BYTES = kRowsPerWave * D * 2;
     static constexpr int RING_BYTES = CAP * 4;
-    static constexpr int P_BYTES = 64 * kRowsPerWave * 4;
-    static constexpr int BYTES = Q_BYTES + RING_BYTES + P_BYTES;
+    static constexpr int BYTES = Q_BYTES + RING_BYTES;
 };
 
 // The columns of an inner tile that some of its rows see: bit c set iff
@@ -83,149 +80,111 @@ __device__ inline uint32_t column_rows(uint64_t w, int c) {
     return ((lo * 0x01020408u) >> 24) | (((hi * 0x01020408u) >> 24) << 4);
 }
 
-// Softmax state of the wavefront's 8 rows (lane-local partial sums; the
-// output columns of this lane).
+// Softmax state of the wavefront's rows on the matrix cores: lane l holds
+// row l % 16 (rows 8..15 are padding) and of its O^T the outputs d = 16dt
+// + 4(l/16) + i; the running max, its exponent offset (m * c, or 0 while
+// m is -inf) and the lane's part of the row sum.
 template <int D> struct RwState {
-    static constexpr int E = D / 64;  // output columns per lane
-    float m[kRowsPerWave], lp[kRowsPerWave], o[kRowsPerWave][E];
+    f4_t acc[D / 16];
+    float m, mc, l;
 };
 
-// One chunk: entries ring[head .. head+n) (n <= 64), lane = entry.
+// One chunk: entries ring[head .. head+n) (n <= 64; head is a multiple of
+// 64, so the ring reads below are aligned and never wrap).  With lane l =
+// (row lq = l % 16, group g = l / 16) and the 64 entries as four 16-key
+// blocks st:
+//   S^T = K Q^T with v_mfma_f32_16x16x32: A = the K rows of block st's
+//     entries (lane: entry 16st + lq, d = 32s + 8g .. +7, straight from
+//     global memory), B = the 8 query rows (zero rows 8..15) in registers;
+//     lane l gets row lq's scores against entries 16st + 4g + i, which
+//     start at -inf where the entry is past the chunk or its row set lacks
+//     row lq;
+//   online softmax per row across the 4 lanes sharing it (lazy rescale as
+//     in the block-wise kernel), P rounded to the input type;
+//   O^T += V^T P^T: B = P^T straight from the score registers (k-slot
+//     order: entries 32u + 4g + j, then 32u + 16 + 4g + j), A = V^T with
+//     the same slot order, each lane gathering its column 16dt + lq of
+//     those 8 entries' V rows.
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void rw_chunk(
     RwState<D> &st, const uint32_t *ring, uint32_t head, int n,
-    const uint32_t *qbuf, float *pbuf, const TIn *__restrict__ Kh,
+    const typename Frag<TIn>::type (&qf)[D / 32], const TIn *__restrict__ Kh,
     const TIn *__restrict__ Vh, float c) {
-    constexpr int R = kRowsPerWave;
-    constexpr int E = RwState<D>::E;
+    using F = Frag<TIn>;
+    using frag = typename F::type;
     constexpr int CAP = RowLds<D>::CAP;
-    const int lane = threadIdx.x & 63;
-    const uint32_t ent = lane < n ? ring[(head + lane) & (CAP - 1)] : 0u;
-    const uint32_t rb = ent >> 24;
-    const int key = (int)(ent & 0xFFFFFFu);
+    const int lane = threadIdx.x & 63, lq = lane & 15, g = lane >> 4;
+    u4_t ent[4];      // entries 16st + 4g + i
+    uint32_t ka[4];   // entry 16st + lq (the K row this lane supplies)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        ent[b] = *reinterpret_cast<const u4_t *>(ring + ((head + 16 * b + 4 * g) & (CAP - 1)));
+        ka[b] = ring[(head + 16 * b + lq) & (CAP - 1)];
+    }
+    auto key_of = [&](int ei, uint32_t e) __attribute__((always_inline)) {
+        return ei < n ? (int)(e & 0xFFFFFFu) : 0;  // past the chunk: any row
+    };
 
-    float s[R];
+    f4_t sc[4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = 0.f;
-    if (rb) {
-        const u4_t *krow = reinterpret_cast<const u4_t *>(Kh + (size_t)key * D);
-        constexpr int H = D / 8 > 8 ? 8 : D / 8;  // 16-byte pieces per half row
+    for (int b = 0; b < 4; ++b) {
+        f4_t c0;
 #pragma unroll
-        for (int h0 = 0; h0 < D / 8; h0 += H) {
-            u4_t kc[H];
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = 16 * b + 4 * g + i < n && ((ent[b][i] >> (24 + lq)) & 1u);
+            c0[i] = ok ? 0.f : -INFINITY;  // lq >= 8: bit 24 + lq is past the row set
+        }
+        const frag *krow = reinterpret_cast<const frag *>(
+            Kh + (size_t)key_of(16 * b + lq, ka[b]) * D);
+        sc[b] = F::mfma(krow[g], qf[0], c0);
 #pragma unroll
-            for (int cc = 0; cc < H; ++cc) kc[cc] = krow[h0 + cc];
+        for (int s2 = 1; s2 < D / 32; ++s2) sc[b] = F::mfma(krow[4 * s2 + g], qf[s2], sc[b]);
+    }
+
+    float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                // one query row at a time: keeps its LDS reads from all
-                // being scheduled (and held in registers) at once
-                __builtin_amdgcn_sched_barrier(0);
-                float acc = s[r];
+    for (int b = 0; b < 4; ++b)
+        mx = fmaxf(fmaxf(mx, fmaxf(sc[b][0], sc[b][1])), fmaxf(sc[b][2], sc[b][3]));
+    mx = max_xor32(max_xor16(mx));
+    // (mx - m) * c is NaN (no move) when both are -inf, +inf when only m is
+    const bool grow = (mx - st.m) * c > 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((st.m - mx) * c) : 1.f;
+        st.m = grow ? mx : st.m;
+        st.mc = grow ? mx * c : st.mc;
+        st.l *= alpha;
 #pragma unroll
-                for (int cc = 0; cc < H; ++cc) {
-                    const u4_t qc = *reinterpret_cast<const u4_t *>(
-                        qbuf + r * (D / 2) + 4 * (h0 + cc));
-                    acc = dot2<TIn>(qc[0], kc[cc][0], acc);
-                    acc = dot2<TIn>(qc[1], kc[cc][1], acc);
-                    acc = dot2<TIn>(qc[2], kc[cc][2], acc);
-                    acc = dot2<TIn>(qc[3], kc[cc][3], acc);
-                }
-                s[r] = acc;
+        for (int i = 0; i < D / 16; ++i) st.acc[i] *= alpha;
+    }
+    frag pf[2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pf[b >> 1][(b & 1) * 4 + i] =
+                (TIn)__builtin_amdgcn_exp2f(fmaf(sc[b][i], c, -st.mc));
+    float lsum = st.l;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        uint32_t pw[4];
+        __builtin_memcpy(pw, &pf[u], 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
+    }
+    st.l = lsum;
+
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            frag va;
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl) {
+                const int b = 2 * u + (sl >> 2), i = sl & 3;
+                va[sl] = Vh[(size_t)key_of(16 * b + 4 * g + i, ent[b][i]) * D + 16 * dt + lq];
             }
+            st.acc[dt] = F::mfma(va, pf[u], st.acc[dt]);
         }
-    }
-    float p[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        p[r] = 0.f;
-        // a row with no key in this chunk keeps its state unchanged
-        if (!__builtin_amdgcn_ballot_w64((rb >> r) & 1)) continue;
-        const float sr = (rb >> r) & 1 ? s[r] : -INFINITY;
-        const float mx = wave_max(sr);
-        const float m_new = fmaxf(st.m[r], mx);
-        const float alpha = __builtin_amdgcn_exp2f((st.m[r] - m_new) * c);
-        st.m[r] = m_new;
-        p[r] = __builtin_amdgcn_exp2f(fmaf(sr, c, -m_new * c));
-        st.lp[r] = st.lp[r] * alpha + p[r];
-#pragma unroll
-        for (int e = 0; e < E; ++e) st.o[r][e] *= alpha;
-    }
-    wave_lds_sync();  // the previous chunk's readers of pbuf are done
-    {
-        f4_t *dst = reinterpret_cast<f4_t *>(pbuf + lane * R);
-        dst[0] = f4_t{p[0], p[1], p[2], p[3]};
-        dst[1] = f4_t{p[4], p[5], p[6], p[7]};
-    }
-    wave_lds_sync();
-
-    // P V: lane = output columns lane*E .. +E-1, 4 entries per batch, the
-    // next batch's V loads issued before this batch's products (batches of 8
-    // hold more registers and measured slower: fewer wavefronts per SIMD)
-    constexpr int BATCH = 4;
-    const TIn *vcol = Vh + lane * E;
-    TIn vv[3][BATCH][E];
-    // The loads are unconditional (an entry past the chunk reads key 0) and
-    // keep the raw values; the products convert them and use 0 for entries
-    // past the chunk.  A load under a condition, converted in place, ends up
-    // in a branch of its own with a wait for it, and the batch's loads
-    // would run one after another.
-    auto load = [&](int slot, int b0) __attribute__((always_inline)) {
-        // a batch's loads stay where they are issued (hoisted together with
-        // later batches' they would hold too many registers)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int ei = b0 + u;
-            // the same entry in every lane: a scalar, so the load's address
-            // is a scalar base plus the lane's column offset
-            const uint32_t ent = __builtin_amdgcn_readfirstlane(ring[(head + ei) & (CAP - 1)]);
-            const int k = ei < n ? (int)(ent & 0xFFFFFFu) : 0;
-            typedef __attribute__((address_space(1))) const TIn gbl_t;
-            gbl_t *vk = (gbl_t *)uniform_ptr(Vh + (size_t)k * D);
-#pragma unroll
-            for (int e = 0; e < E; ++e) vv[slot][u][e] = vk[lane * E + e];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto val = [&](int ei, TIn x) __attribute__((always_inline)) {
-        return ei < n ? (float)x : 0.f;
-    };
-    // products of batch b0 (its values in slot sl, a compile-time constant)
-    auto products = [&](auto slc, int b0) __attribute__((always_inline)) {
-        constexpr int sl = decltype(slc)::value;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int ei = b0 + u;
-            const f4_t pa = *reinterpret_cast<const f4_t *>(pbuf + ei * R);
-            const f4_t pb = *reinterpret_cast<const f4_t *>(pbuf + ei * R + 4);
-            const float pr[R] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    st.o[r][e] = fmaf(pr[r], val(ei, vv[sl][u][e]), st.o[r][e]);
-        }
-    };
-    // three slots: the loads of batch b + 2 are issued before the products
-    // of batch b, so two batches' loads are in flight behind the one in use
-    // (with one, every batch waited for most of a memory round trip)
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    using C2 = std::integral_constant<int, 2>;
-    // (the loads are unconditional, past the chunk too, where they read key
-    // 0: a load under a condition makes the compiler wait for every load
-    // in flight where the paths join)
-    load(0, 0);
-    load(1, BATCH);
-    for (int b0 = 0; b0 < n; b0 += 3 * BATCH) {
-        load(2, b0 + 2 * BATCH);
-        products(C0(), b0);
-        if (b0 + BATCH >= n) break;
-        load(0, b0 + 3 * BATCH);
-        products(C1(), b0 + BATCH);
-        if (b0 + 2 * BATCH >= n) break;
-        load(1, b0 + 4 * BATCH);
-        products(C2(), b0 + 2 * BATCH);
     }
 }
 
@@ -237,11 +196,9 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
     const FwdArgs<TIn, TOut> &a, char *slice, int I, int ir, int bh,
     const RowInfo &ri) {
     constexpr int R = kRowsPerWave;
-    constexpr int E = RwState<D>::E;
     constexpr int CAP = RowLds<D>::CAP;
     uint32_t *qbuf = reinterpret_cast<uint32_t *>(slice);  // [R][D/2]
     uint32_t *ring = reinterpret_cast<uint32_t *>(slice + RowLds<D>::Q_BYTES);
-    float *pbuf = reinterpret_cast<float *>(slice + RowLds<D>::Q_BYTES + RowLds<D>::RING_BYTES);
     const int lane = threadIdx.x & 63;
     const int row0 = 64 * I + 8 * ir;
     const size_t head_off = (size_t)bh * a.S * D;
@@ -260,13 +217,23 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
 
     RwState<D> st;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        st.m[r] = -INFINITY;
-        st.lp[r] = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) st.o[r][e] = 0.f;
-    }
+    for (int i = 0; i < D / 16; ++i) st.acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.mc = 0.f;
+    st.l = 0.f;
     wave_lds_sync();
+    // the query rows as the B operand of S^T = K Q^T: lane l holds row l % 16
+    // (zero for rows 8..15), d = 32s + 8(l/16) .. +7
+    using frag = typename Frag<TIn>::type;
+    const int lq = lane & 15, g = lane >> 4;
+    frag qf[D / 32];
+#pragma unroll
+    for (int s2 = 0; s2 < D / 32; ++s2) {
+        const frag *qrow = reinterpret_cast<const frag *>(
+            reinterpret_cast<const TIn *>(qbuf) + (lq & (R - 1)) * D);
+        const frag q = qrow[4 * s2 + g];
+        qf[s2] = lq < R ? q : frag{};
+    }
 
     // gather step: tile t0 + lane/8, inner-tile column lane%8; the loads of
     // the next step are issued before this step's work.  They are
@@ -310,7 +277,7 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
         tail += (uint32_t)total;
         wave_lds_sync();
         while (tail - head >= 64) {
-            rw_chunk<D, TIn>(st, ring, head, 64, qbuf, pbuf, Kh, Vh, a.c);
+            rw_chunk<D, TIn>(st, ring, head, 64, qf, Kh, Vh, a.c);
             head += 64;
         }
     };
@@ -323,17 +290,15 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
         step(t0 + 8, jb, wb, ja, wa);
     }
     if (tail != head)
-        rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qbuf, pbuf, Kh, Vh, a.c);
+        rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qf, Kh, Vh, a.c);
 
+    // total l of each row over its 4 lanes; rows 8..15 are not stored
+    const float lt = sum_xor32(sum_xor16(st.l));
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (lq < R && row0 + lq < a.S) {
+        TOut *orow = a.O + head_off + (size_t)(row0 + lq) * D + 4 * g;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const float lt = wave_sum(st.lp[r]);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        TOut *orow = a.O + head_off + (size_t)(row0 + r) * D + lane * E;
-        if (row0 + r < a.S) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) store1<TOut>(orow + e, st.o[r][e] * inv);
-        }
+        for (int dt = 0; dt < D / 16; ++dt) store4<TOut>(orow + 16 * dt, st.acc[dt] * inv);
     }
     wave_lds_sync();  // the slice may be reused by the next group
 }

@@ -64,10 +64,10 @@ struct SelectCoef {
 SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                                    double *t_blk) {
     // fitted on MI355X; fp16 and bf16 share coefficients
-    const SelectCoef k64 = {5.4605, 1.8829e-3, 3.1919e-4, 0.87456,
-                            2.2136e-4, 2.6365e-3, 0.66979, 4.8045};
-    const SelectCoef k128 = {4.1144, 4.1525e-3, 1.6700e-4, 1.3979,
-                             4.0450e-4, 5.4630e-3, 0.48558, 7.7900};
+    const SelectCoef k64 = {5.3194, 1.6425e-3, 1.7245e-4, 0.71518,
+                            1.2889e-4, 1.2573e-3, 0.39789, 1.5769};
+    const SelectCoef k128 = {4.3252, 3.3637e-3, 9.6461e-5, 1.1192,
+                             1.7288e-4, 2.5497e-3, 0.57893, 2.8967};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
     const double heads = (double)in.heads;
@@ -96,11 +96,19 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
     *t_row = k.launch_us + (w_row > crit_row ? w_row : crit_row);
 }
 
+// Row-wise is taken when its predicted time is below this fraction of the
+// block-wise one.  The model underestimates the row-wise kernel by up to
+// 1.7x on long masks whose every stored tile is partial at a few percent
+// density (causal AND Bernoulli(0.02) at S = 8192-16384), where the plain
+// comparison lost 6-7% of the sweep's total time to wrong picks; with the
+// margin 0.3% (d = 64) and 0.02% (d = 128).  Fitted with the coefficients.
+constexpr double kRowMargin = 0.9;
+
 // 1 = row-wise, 2 = block-wise (the smh_kernel values).
 SMH_HD inline int select_model(const SelectInput &in) {
     double tr, tb;
     select_costs_us(in, &tr, &tb);
-    return tr < tb ? 1 : 2;
+    return tr < kRowMargin * tb ? 1 : 2;
 }
 #pragma clang fp contract(on)
 
