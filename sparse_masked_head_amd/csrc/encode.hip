@@ -523,6 +523,66 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     }
 }
 
+// The scan of at most 64 rows (lane = row), in wavefront 0 alone: the
+// outputs of scan_body without segment offsets, with wavefront shuffles
+// in place of workgroup barriers (one memory round trip, then only stores).
+__device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
+                           smh_mask_enc enc) {
+    const int lane = threadIdx.x & 63;
+    const int C = plan.per_row;
+    unsigned long long rc = 0;
+    long long nnz = 0;
+    uint64_t an = 0;
+    if (lane < R) {
+#pragma unroll 8
+        for (int c = 0; c < C; ++c) {  // independent loads: they pipeline
+            rc += sg.cnt[lane * C + c];
+            nnz += (long long)sg.nnz[lane * C + c];
+            an |= sg.any[lane * C + c];
+        }
+    }
+    const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull), cnt = f + p;
+    unsigned long long incl = rc;  // inclusive prefix over rows
+    for (int d = 1; d < 64; d <<= 1) {
+        const unsigned long long y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    const unsigned long long run = incl - rc, tot = __shfl(incl, 63);
+    long long nz = nnz, empty = lane < R ? 64 - __popcll(an) : 0;
+    int mx = lane < R ? cnt : 0;
+    for (int o = 32; o > 0; o >>= 1) {
+        nz += __shfl_xor(nz, o);
+        empty += __shfl_xor(empty, o);
+        mx = max(mx, __shfl_xor(mx, o));
+    }
+    // schedule rank: rows with more stored tiles, then rows before with as many
+    int rank = 0;
+    for (int J2 = 0; J2 < R; ++J2) {  // (a scalar read of lane J2 per row)
+        const int c2 = __builtin_amdgcn_readlane(cnt, J2);
+        rank += (c2 > cnt) || (c2 == cnt && J2 < lane);
+    }
+    if (lane < R) {
+        enc.full_row_ptr[lane] = (int32_t)(run >> 32);
+        enc.part_row_ptr[lane] = (int32_t)(run & 0xFFFFFFFFull);
+        int4 *ri = reinterpret_cast<int4 *>(enc.row_info + 16 * (size_t)lane);
+        ri[0] = make_int4((int)(run >> 32), f, (int)(run & 0xFFFFFFFFull), p);
+        for (int k = cnt; k < 4; ++k) enc.row_info[16 * (size_t)lane + 4 + k] = -1;
+        ri[2] = make_int4((int)(uint32_t)((unsigned long long)nz & 0xFFFFFFFFull),
+                          (int)(nz >> 32), (int)(tot >> 32), (int)(tot & 0xFFFFFFFFull));
+        ri[3] = make_int4(mx, 0, 0, 0);
+        enc.row_order[rank] = lane;
+    }
+    if (lane == 0) {
+        enc.full_row_ptr[R] = (int32_t)(tot >> 32);
+        enc.part_row_ptr[R] = (int32_t)(tot & 0xFFFFFFFFull);
+        enc.stats[0] = nz;
+        enc.stats[1] = (int64_t)(tot >> 32);
+        enc.stats[2] = (int64_t)(tot & 0xFFFFFFFFull);
+        enc.stats[3] = empty - (long long)G * (64LL * n - S);  // rows past S do not exist
+        enc.stats[4] = mx;
+    }
+}
+
 __global__ __launch_bounds__(256) void enc_scan(int S, int n, int R, int G,
                                                 SegPlan plan, Seg sg,
                                                 smh_mask_enc enc) {
@@ -542,7 +602,11 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
     const int t = threadIdx.x, s = blockIdx.x;
     if constexpr (kSelf) {
         if (s == plan.total) {
-            scan_body<kFusedRows, kFusedBins>(S, n, R, G, plan, sg, enc, false);
+            if (R <= 64) {
+                if (threadIdx.x < 64) scan_small(S, n, R, G, plan, sg, enc);
+            } else {
+                scan_body<kFusedRows, kFusedBins>(S, n, R, G, plan, sg, enc, false);
+            }
             return;
         }
     }
