@@ -236,11 +236,11 @@ __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mas
         if (c == 0) rows_any[r0] = a;
     }
     __syncthreads();
-    uint64_t any64 = 0;  // bit 8k + r: query row 8k + r of the strip
-    if (t == 0)
-        for (int r = 0; r < 8; ++r)
-            for (int k = 0; k < 8; ++k)
-                any64 |= (uint64_t)((rows_any[r] >> k) & 1u) << (8 * k + r);
+    // bit 8k + r: query row 8k + r of the strip (one ballot in wavefront 0,
+    // lane 8k + r reading bit k of rows_any[r]; strip_classify reads it there)
+    uint64_t any64 = 0;
+    if (w == 0)
+        any64 = __builtin_amdgcn_ballot_w64(((rows_any[lane & 7] >> (lane >> 3)) & 1u) != 0);
     strip_classify(s, nwin, w0, n, sg, lw, wsum, tkind, any64);
 }
 
