@@ -199,3 +199,56 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libsmh.so"))
     with pytest.raises(ImportError):
         L.lib()
+
+
+def test_calibration_model_is_the_library_model():
+    """The Python restatement the coefficients are fitted with
+    (sparse_masked_head_amd.calibrate.model) computes the same times as the
+    library's cost model (smh_select_costs), and the library picks row-wise
+    exactly when t_row < ROW_MARGIN * t_blk, the rule the fit scores: a
+    fit is then a fit of the model the library runs."""
+    import numpy as np
+    from sparse_masked_head_amd import calibrate as cal
+    text = open(os.path.join(ROOT, "sparse_masked_head_amd", "csrc",
+                             "select_model.h")).read()
+    coef = {}
+    for d in (64, 128):
+        body = re.search(r"k%d\s*=\s*\{([^}]*)\}" % d, text).group(1)
+        coef[d] = np.array([float(x) for x in body.split(",")])
+        assert len(coef[d]) == 8
+    margin = float(re.search(r"kRowMargin\s*=\s*([0-9.]+)", text).group(1))
+    assert margin == cal.ROW_MARGIN
+    rng = np.random.default_rng(5)
+    picks = set()
+    for _ in range(300):
+        S = int(rng.choice([256, 512, 1024, 4096, 16384]))
+        n = S // 64
+        tiles = int(rng.integers(1, n * n + 1))
+        if rng.random() < 0.5:   # dense-ish: any mix of full and partial
+            n_full = int(rng.integers(0, tiles + 1))
+            n_part = tiles - n_full
+            nnz = 4096 * n_full + int(rng.integers(n_part, 4095 * n_part + 1))
+        else:                    # very sparse: partial tiles, 0.1-1% dense
+            n_full, n_part = 0, tiles
+            nnz = max(n_part, int(n_part * 4096 * rng.uniform(0.001, 0.01)))
+        max_row = int(rng.integers(-(-tiles // n), min(n, tiles) + 1))
+        B, H, d = int(rng.integers(1, 9)), int(rng.integers(1, 65)), int(rng.choice([64, 128]))
+        st = L.MaskStats(nnz=nnz, S=S, n_full=n_full, n_partial=n_part,
+                         n_empty_rows=0, max_row_tiles=max_row, mask_b=1,
+                         mask_h=1)
+        a, b = ctypes.c_double(), ctypes.c_double()
+        assert L.lib().smh_select_costs(ctypes.byref(st), B, H, d, L.SMH_F16,
+                                        ctypes.byref(a), ctypes.byref(b)) == 0
+        p = dict(S=S, BH=B * H, stats=dict(nnz=nnz, n_full=n_full,
+                                           n_partial=n_part,
+                                           max_row_tiles=max_row))
+        tr, tb = cal.model(coef[d], p)
+        assert a.value == pytest.approx(tr, rel=1e-9)
+        assert b.value == pytest.approx(tb, rel=1e-9)
+        out = ctypes.c_int()
+        assert L.lib().smh_select_kernel(ctypes.byref(st), B, H, d, L.SMH_F16,
+                                         ctypes.byref(out)) == 0
+        want = L.SMH_ROWWISE if a.value < margin * b.value else L.SMH_BLOCKWISE
+        assert out.value == want
+        picks.add(out.value)
+    assert picks == {L.SMH_ROWWISE, L.SMH_BLOCKWISE}   # both sides exercised
