@@ -56,6 +56,13 @@ __device__ inline uint32_t live_columns(uint64_t w) {
 // and the wavefront's total: the count's four bits as ballots, v_mbcnt
 // counting the lanes below this one in each (no cross-lane data moves).
 __device__ inline int wave_prefix16(int cnt, int &total) {
+    // counts of 0 or 1 only (the common case for a sparse mask): one ballot
+    const uint64_t any = __builtin_amdgcn_ballot_w64(cnt != 0);
+    if (__builtin_amdgcn_ballot_w64(cnt > 1) == 0) {
+        total = __popcll(any);
+        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(any >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)any, 0u));
+    }
     int excl = 0, tot = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
