@@ -188,41 +188,6 @@ template <> __device__ inline void store4<__bf16>(__bf16 *p, f4_t x) {
     *reinterpret_cast<b4 *>(p) = y;
 }
 
-template <typename T> __device__ inline void store1(T *p, float x) { *p = (T)x; }
-
-// DPP move of x within the wavefront (`ctrl` = row_shr / row_bcast code);
-// lanes whose source does not exist, or whose row is outside `rows`,
-// receive `fill`.
-template <int ctrl, int rows>
-__device__ inline float dpp(float x, float fill) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(
-        __float_as_int(fill), __float_as_int(x), ctrl, rows, 0xF, false));
-}
-
-// Max / sum over the 64 lanes, returned uniformly: an inclusive scan
-// within each row of 16 (row_shr 1, 2, 4, 8), then across rows
-// (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3), so lane
-// 63 holds the result; read it as a scalar.
-__device__ inline float wave_max(float x) {
-    const float f = -INFINITY;
-    x = fmaxf(x, dpp<0x111, 0xF>(x, f));
-    x = fmaxf(x, dpp<0x112, 0xF>(x, f));
-    x = fmaxf(x, dpp<0x114, 0xF>(x, f));
-    x = fmaxf(x, dpp<0x118, 0xF>(x, f));
-    x = fmaxf(x, dpp<0x142, 0xA>(x, f));
-    x = fmaxf(x, dpp<0x143, 0xC>(x, f));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-__device__ inline float wave_sum(float x) {
-    x += dpp<0x111, 0xF>(x, 0.f);
-    x += dpp<0x112, 0xF>(x, 0.f);
-    x += dpp<0x114, 0xF>(x, 0.f);
-    x += dpp<0x118, 0xF>(x, 0.f);
-    x += dpp<0x142, 0xA>(x, 0.f);
-    x += dpp<0x143, 0xC>(x, 0.f);
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
 // Max / sum of x over lanes l and l^16 (then l^32) with the gfx950 row
 // swaps: swapping odd rows of one copy with even rows of the other leaves
 // the two partners' values side by side in every lane.
