@@ -56,3 +56,24 @@ def test_bias_and_residual_add():
     base = out_proj(o, w)
     np.testing.assert_allclose(out_proj(o, w, b), base + b, atol=1e-13)
     np.testing.assert_allclose(out_proj(o, w, None, r), base + r, atol=1e-13)
+
+
+def test_abs_products_elementwise_fsum():
+    """abs_products (the scale of the fp32 accumulation error that sets the
+    per-element GPU bar) is sum_k |x_k| |w_k| per output element: checked
+    against an element-by-element math.fsum on signed data, so a dropped
+    absolute value (which lets terms cancel) or a transposed weight fails."""
+    from oracle.out_proj import abs_products
+    B, H, S, d, D = 2, 3, 4, 5, 7
+    o, w = rand((B, H, S, d), 21), rand((D, H * d), 22)
+    assert (o < 0).any() and (w < 0).any()
+    got = abs_products(o, w)
+    assert got.shape == (B, S, D)
+    for bb in range(B):
+        for s in range(S):
+            for n in range(D):
+                want = math.fsum(abs(o[bb, h, s, k]) * abs(w[n, h * d + k])
+                                 for h in range(H) for k in range(d))
+                assert abs(got[bb, s, n] - want) <= 1e-12 * want
+    # bounded below by the magnitude of the signed sum
+    assert (got >= np.abs(out_proj(o, w)) - 1e-12).all()

@@ -72,6 +72,30 @@ def test_block_map_by_hand():
     assert np.array_equal(m, want)
 
 
+def test_threshold16_values_by_definition():
+    """floor(p * 65536) with p rounded to float32 first.  Values derived by
+    hand from the float32 neighbours of p (a multiplication by 2^16 is
+    exact, so only the rounding of p and the floor matter):
+      0.02  -> float32 0.0199999995529651641845703125,
+               * 65536 = 1310.71997..., floor 1310 (rounding would give 1311)
+      0.8   -> float32 0.800000011920928955078125, * 65536 = 52428.80078,
+               floor 52428
+      0.001 -> float32 0.001000000047497451305389404296875,
+               * 65536 = 65.536003..., floor 65
+      0.5   -> exact, 32768;  1.0 -> 65536;  0.0 -> 0
+      2^-16 -> exact, 1;  just below 2^-16 (float32 0x377FFFFF) -> 0"""
+    assert threshold16(0.02) == 1310
+    assert threshold16(0.8) == 52428
+    assert threshold16(0.001) == 65
+    assert threshold16(0.5) == 32768
+    assert threshold16(1.0) == 65536
+    assert threshold16(0.0) == 0
+    assert threshold16(2.0 ** -16) == 1
+    below = float(np.frombuffer(np.uint32(0x377FFFFF).tobytes(), np.float32)[0])
+    assert below < 2.0 ** -16
+    assert threshold16(below) == 0
+
+
 def test_random_fractions_and_limits():
     S = 1024
     m = pattern_mask(S, random_p=0.02, seed=9)
