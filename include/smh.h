@@ -234,7 +234,13 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
                             int32_t d, smh_dtype dt, double *t_rowwise_us,
                             double *t_blockwise_us);
 
-/* Masked attention forward: for every b < B, h < H and query row i,
+/* Masked attention forward ([EXP] Technical summary > Problem statement: a
+ * mask decides which (query, key) pairs take part in softmax(Q K^T) V, and
+ * a masked pair must not contribute; Methodology > 1. Unified MHA module:
+ * the row-wise and block-wise kernels read only the two-level encoding,
+ * skip absent outer tiles and mask partial ones bit by bit from their
+ * inner-tile bitmaps, so the result is exact).  For every b < B, h < H and
+ * query row i,
  *   O[b,h,i,:] = sum_j w_j V[b,h,j,:] / sum_j w_j over valid keys j of row i
  *   in the mask of (b, h),
  *   w_j = exp(scale * <Q[b,h,i,:], K[b,h,j,:]> - max), and O = 0 for a row
@@ -254,10 +260,10 @@ smh_status smh_select_costs(const smh_mask_stats *st, int32_t B, int32_t H,
  *          st NULL the same model is evaluated on the device from the
  *          statistics the encoder wrote, inside one fused launch that then
  *          runs the chosen algorithm, so no host synchronisation is needed.
- * Arithmetic: fp32 scores, softmax statistics and accumulators.  The
- * block-wise kernel rounds the probabilities to in_dt for its matrix-core
- * probability-times-V product (the row sums use the rounded values); the
- * row-wise kernel keeps them in fp32.  Q, K and V must be finite: a
+ * Arithmetic: fp32 scores, softmax statistics and accumulators.  Both
+ * kernels round the probabilities to in_dt for their matrix-core
+ * probability-times-V product, and the row sums use the rounded values.
+ * Q, K and V must be finite: a
  * masked key's V row is multiplied by a zero probability.  Asynchronous on
  * `stream`. */
 smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,

@@ -52,7 +52,7 @@ template <typename TIn, typename TOut> struct FwdArgs {
     const int32_t *frp, *fci, *prp, *pci;
     const uint64_t *bm;
     const int32_t *row_order;
-    const int32_t *info;  // row_info [R][8]
+    const int32_t *info;  // row_info [R][16]
     const int64_t *stats;
 };
 

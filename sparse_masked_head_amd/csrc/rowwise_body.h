@@ -116,7 +116,7 @@ template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void rw_chunk(
     RwState<D> &st, const uint32_t *ring, uint32_t head, int n,
     const typename Frag<TIn>::type (&qf)[D / 32], const TIn *__restrict__ Kh,
-    const TIn *__restrict__ Vh, float c) {
+    const TIn *__restrict__ Vh, float c, int S) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     constexpr int CAP = RowLds<D>::CAP;
@@ -128,8 +128,11 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
         ent[b] = *reinterpret_cast<const u4_t *>(ring + ((head + 16 * b + 4 * g) & (CAP - 1)));
         ka[b] = ring[(head + 16 * b + lq) & (CAP - 1)];
     }
+    // The key of entry ei, clamped into the head's S rows: an encoding that
+    // is not this library's (bits set past S in a tile cut by S) then gives
+    // wrong numbers, never a read outside K and V.  Past the chunk: any row.
     auto key_of = [&](int ei, uint32_t e) __attribute__((always_inline)) {
-        return ei < n ? (int)(e & 0xFFFFFFu) : 0;  // past the chunk: any row
+        return ei < n ? min((int)(e & 0xFFFFFFu), S - 1) : 0;
     };
 
     f4_t sc[4];
@@ -138,8 +141,11 @@ __device__ __attribute__((always_inline)) inline void rw_chunk(
         f4_t c0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = 16 * b + 4 * g + i < n && ((ent[b][i] >> (24 + lq)) & 1u);
-            c0[i] = ok ? 0.f : -INFINITY;  // lq >= 8: bit 24 + lq is past the row set
+            // rows lq >= 8 are padding: no entry's row set holds them (and
+            // the shift below stays under 32)
+            const bool ok = 16 * b + 4 * g + i < n && lq < 8 &&
+                            ((ent[b][i] >> (24 + (lq & 7))) & 1u);
+            c0[i] = ok ? 0.f : -INFINITY;
         }
         const frag *krow = reinterpret_cast<const frag *>(
             Kh + (size_t)key_of(16 * b + lq, ka[b]) * D);
@@ -284,7 +290,7 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
         tail += (uint32_t)total;
         wave_lds_sync();
         while (tail - head >= 64) {
-            rw_chunk<D, TIn>(st, ring, head, 64, qf, Kh, Vh, a.c);
+            rw_chunk<D, TIn>(st, ring, head, 64, qf, Kh, Vh, a.c, a.S);
             head += 64;
         }
     };
@@ -297,7 +303,7 @@ __device__ __attribute__((always_inline)) inline void rowwise_group(
         step(t0 + 8, jb, wb, ja, wa);
     }
     if (tail != head)
-        rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qf, Kh, Vh, a.c);
+        rw_chunk<D, TIn>(st, ring, head, (int)(tail - head), qf, Kh, Vh, a.c, a.S);
 
     // total l of each row over its 4 lanes; rows 8..15 are not stored
     const float lt = sum_xor32(sum_xor16(st.l));
