@@ -3,8 +3,8 @@
 
 One step is one pass of the whole path over one batch of synthetic input
 already resident in device memory:
-    encode the [S, S] mask (GPU, 2 launches)  ->  attention forward in one
-    launch that picks the row-wise or block-wise algorithm with the cost
+    encode the [S, S] mask (GPU, 2 or 3 launches)  ->  attention forward in
+    one launch that picks the row-wise or block-wise algorithm with the cost
     model evaluated on the device from the encoding's statistics.
 No host synchronisation inside a step, so steps are captured into a HIP
 graph and replayed (--eager launches every step from the host instead).
@@ -13,10 +13,16 @@ events around graphs of back-to-back launches of that part alone.
 The headline value is effective TFLOP/s: 4*d FLOPs per valid (query, key)
 pair, summed over every (batch, head), divided by the step time.
 
-Default workload: BERT-base-shaped sliding window (B=8, H=12, S=512, d=64,
-fp16, |i-j| <= 64).  --seq-len changes S (any length: the last tiles are
-cut), --mask-stack batch gives each sequence its own mask (the pattern cut
-to a per-sequence length), encoded as one stack.  Prints one JSON line.
+Default workload (the headline): the long-sequence unstructured mask
+(B=1, H=32, S=16384, d=128, bf16 in, fp32 out, causal AND (|i-j| <= 1024
+OR Bernoulli(0.02))).  With the default options the line also carries
+`per_mask`: the same measurements on each of the five workloads (warm: the
+inputs stay in the caches between launches; cold: launches rotate through
+copies of the inputs, more than 1 GiB in all where memory allows, twice
+the 256 MB last-level cache).  --seq-len changes S (any length: the last
+tiles are cut), --mask-stack batch gives each sequence its own mask (the
+pattern cut to a per-sequence length), encoded as one stack.  Prints one
+JSON line.
 """
 import argparse
 import json
@@ -38,10 +44,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload id 1..7 (default 2; 6 = the row-wise "
-                         "kernel's regime, a 0.1%% random mask; 7 = "
-                         "workload 5's far tiles alone)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload id 1..7 (default 5, the 16k mask; 6 = "
+                         "the row-wise kernel's regime, a 0.1%% random "
+                         "mask; 7 = workload 5's far tiles alone)")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "rowwise", "blockwise"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -77,6 +83,13 @@ def parse():
                     help="out_proj: the step also runs the fused output "
                          "projection (attention output x W^T + bias + "
                          "residual, D = H*d) on the attention output")
+    ap.add_argument("--per-mask", default="auto",
+                    choices=["auto", "on", "off"],
+                    help="also measure workloads 1-5 (per_mask); auto = on "
+                         "for the default headline options")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timings (rotated input "
+                         "copies)")
     ap.add_argument("--out-dtype", default="auto",
                     choices=["auto", "in", "f32"],
                     help="output type; auto = input type for fp16, f32 for "
@@ -259,6 +272,198 @@ def workload(args):
     return cfg, mask
 
 
+COLD_BYTES = 1 << 30     # rotation target: twice the 256 MB last-level cache, x2
+COLD_MAX_COPIES = 1024
+
+
+def roofline_of(flops, nbytes, t_s, dtype):
+    """Roofline entry of a kernel doing `flops` effective FLOPs and moving
+    `nbytes` algorithmic bytes in `t_s` seconds: the bound is the one its
+    arithmetic intensity puts it under."""
+    if flops / nbytes < RIDGE:
+        r = {"bound": "hbm", "achieved": nbytes / t_s / 1e9,
+             "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": flops / t_s / 1e12,
+             "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["algorithmic_flops"] = flops
+    r["algorithmic_bytes"] = nbytes
+    return r
+
+
+class Timer:
+    """Average duration of one call of a function's kernels: `reps` calls
+    back to back captured in one graph (or launched eagerly), bracketed by
+    events on their stream."""
+
+    def __init__(self, stream, eager):
+        self.stream, self.eager = stream, eager
+
+    def us(self, fn, reps=20):
+        import torch
+        calls = fn if isinstance(fn, list) else [fn]
+        if len(calls) > 1:
+            reps = max(reps, len(calls))
+        seq = [calls[i % len(calls)] for i in range(reps)]
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        if self.eager:
+            for f in calls:
+                f()
+            torch.cuda.synchronize()
+            a.record(self.stream)
+            for f in seq:
+                f()
+            b.record(self.stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in seq:
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):          # the median of three replays
+            a.record(self.stream)
+            g.replay()
+            b.record(self.stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / reps)
+        return sorted(ts)[1]
+
+
+class Workload:
+    """Device tensors of one workload and the calls a step makes."""
+
+    def __init__(self, args, cfg, mask, dev, copies=1):
+        import torch
+        import sparse_masked_head_amd as smh
+        from workloads import make_qkv
+        self.cfg, self.mask, self.args = cfg, mask, args
+        self.smh = smh
+        qkv = make_qkv(cfg.B, cfg.H, cfg.S, cfg.d, cfg.dtype, seed=cfg.cid)
+        self.qkv_host = qkv
+        q, k, v = (x.to(dev) for x in qkv)
+        self.in_dtype = q.dtype
+        self.out_dt = {"auto": torch.float32 if cfg.dtype == "bf16"
+                       else q.dtype, "in": q.dtype,
+                       "f32": torch.float32}[args.out_dtype]
+        self.mb, self.mh = (1, 1) if mask.ndim == 2 else mask.shape[:2]
+        self.pattern = None
+        mask_d = None
+        if args.mask_source == "pattern":
+            from workloads import pattern_of
+            pat = dict(pattern_of(cfg))
+            if pat.get("blocks") is not None:
+                pat["blocks"] = torch.from_numpy(pat["blocks"]).to(dev)
+            self.pattern = pat
+        else:
+            mask_d = torch.from_numpy(mask).to(dev)
+        ws_bytes = smh.encode_workspace_bytes(cfg.S, self.mb, self.mh)
+        self.sets = []
+        for c in range(copies):
+            qc, kc, vc = (q, k, v) if c == 0 else (x.clone() for x in (q, k, v))
+            mc = mask_d if (c == 0 or mask_d is None) else mask_d.clone()
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            out = torch.empty(q.shape, dtype=self.out_dt, device=dev)
+            self.sets.append({"q": qc, "k": kc, "v": vc, "mask": mc,
+                              "ws": ws, "out": out})
+        self.dev = dev
+        for c in range(copies):
+            self.sets[c]["enc"] = self.encode(c)
+        torch.cuda.synchronize()
+        self.stats = smh.mask_stats_get(self.sets[0]["enc"])
+        self.kernel = args.kernel if args.kernel != "auto" else \
+            smh.select_kernel(self.stats, cfg.B, cfg.H, cfg.d, q.dtype)
+        per = sum(t.numel() * t.element_size() for t in
+                  (self.sets[0][x] for x in ("q", "k", "v", "out", "ws")))
+        if mask_d is not None:
+            per += mask_d.numel() * mask_d.element_size()
+        self.copy_bytes = per
+
+    def encode(self, c=0):
+        st = self.sets[c]
+        if self.pattern is not None:
+            return self.smh.encode_pattern(self.cfg.S, device=self.dev,
+                                           workspace=st["ws"], **self.pattern)
+        return self.smh.encode_mask(st["mask"], workspace=st["ws"])
+
+    def fwd(self, c=0):
+        st = self.sets[c]
+        self.smh.sparse_mha_fwd(st["q"], st["k"], st["v"], st["enc"],
+                                kernel=self.args.kernel,
+                                out_dtype=self.out_dt, out=st["out"])
+
+    def step(self, c=0):
+        st = self.sets[c]
+        st["enc"] = self.encode(c)
+        self.fwd(c)
+
+    # algorithmic work of one step
+    def work(self):
+        cfg, st = self.cfg, self.stats
+        users = users_per_mask(self.mask, cfg.B, cfg.H)
+        flops = 4.0 * cfg.d * users * st["nnz"]
+        tiles = st["n_full"] + st["n_partial"]
+        tile_flops = 4.0 * cfg.d * 4096.0 * users * tiles
+        rows = self.mb * self.mh * cfg.n_ot
+        enc_b = encoding_bytes(st, rows)
+        eb_out = self.sets[0]["out"].element_size()
+        attn_bytes = cfg.B * cfg.H * cfg.S * cfg.d * (3 * 2 + eb_out) + enc_b
+        mask_bytes = 0 if self.pattern is not None else self.mask.size
+        return flops, tile_flops, attn_bytes, mask_bytes + enc_b
+
+
+def measure(args, cfg, mask, dev, timer, cold):
+    """Warm (and cold) kernel timings of one workload: a dict for
+    per_mask, and the Workload (for the headline's own timed steps)."""
+    import torch
+    w = Workload(args, cfg, mask, dev)
+    flops, tile_flops, attn_bytes, enc_bytes = w.work()
+    enc_us = timer.us(lambda: w.encode(0))
+    fwd_us = timer.us(lambda: w.fwd(0))
+    step_us = timer.us(lambda: w.step(0))
+    dt = cfg.dtype
+    e = {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "d": cfg.d,
+         "dtype": dt, "out_dtype": str(w.out_dt).replace("torch.", ""),
+         "mask": cfg.desc, "kernel": w.kernel, "mask_stats": w.stats,
+         "encode_ms": enc_us / 1e3, "fwd_ms": fwd_us / 1e3,
+         "step_ms": step_us / 1e3,
+         "fwd_tflops": flops / fwd_us / 1e6,
+         "fwd_pct_mfma_peak": 100.0 * flops / fwd_us / 1e6 /
+         MFMA_PEAK_TFLOPS[dt],
+         "step_tflops": flops / step_us / 1e6,
+         "tile_mfma_frac": tile_flops / fwd_us / 1e6 / MFMA_PEAK_TFLOPS[dt],
+         "roofline": roofline_of(flops, attn_bytes, fwd_us * 1e-6, dt),
+         "encoder": {"us": enc_us, "algorithmic_bytes": enc_bytes,
+                     "achieved": enc_bytes / enc_us / 1e3, "unit": "GB/s",
+                     "peak": HBM_PEAK_GBS,
+                     "frac": enc_bytes / enc_us / 1e3 / HBM_PEAK_GBS}}
+    e["roofline"]["kernel"] = "auto_fwd" if args.kernel == "auto" \
+        else f"{w.kernel}_fwd"
+    pred_row, pred_blk = w.smh.select_costs(w.stats, cfg.B, cfg.H, cfg.d,
+                                            w.in_dtype)
+    e["selector_pred_us"] = {"rowwise": pred_row, "blockwise": pred_blk}
+    if cold:
+        n = max(2, min(COLD_MAX_COPIES, -(-COLD_BYTES // w.copy_bytes)))
+        del w
+        torch.cuda.empty_cache()
+        wc = Workload(args, cfg, mask, dev, copies=n)
+        ce = timer.us([lambda c=c: wc.encode(c) for c in range(n)])
+        cf = timer.us([lambda c=c: wc.fwd(c) for c in range(n)])
+        cs = timer.us([lambda c=c: wc.step(c) for c in range(n)])
+        e["cold"] = {"encode_ms": ce / 1e3, "fwd_ms": cf / 1e3,
+                     "step_ms": cs / 1e3, "copies": n,
+                     "rotation_bytes": n * wc.copy_bytes,
+                     "fwd_tflops": flops / cf / 1e6,
+                     "roofline": roofline_of(flops, attn_bytes, cf * 1e-6, dt)}
+        del wc
+        torch.cuda.empty_cache()
+    return e
+
+
 def main():
     args = parse()
     if args.copy_reference:
@@ -274,47 +479,22 @@ def main():
         sys.exit(2)
     import torch
     import sparse_masked_head_amd as smh
-    from workloads import make_qkv
+    from workloads import get_config, make_mask
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg, mask = workload(args)
-    qkv = make_qkv(cfg.B, cfg.H, cfg.S, cfg.d, cfg.dtype, seed=cfg.cid)
-    q, k, v = (x.to(dev) for x in qkv)
-    mask_d = torch.from_numpy(mask).to(dev) \
-        if args.mask_source == "dense" else None
-    out_dt = {"auto": torch.float32 if cfg.dtype == "bf16" else q.dtype,
-              "in": q.dtype, "f32": torch.float32}[args.out_dtype]
-    mb, mh = (1, 1) if mask.ndim == 2 else mask.shape[:2]
-    ws = torch.empty(smh.encode_workspace_bytes(cfg.S, mb, mh),
-                     dtype=torch.uint8, device=dev)
-    out = torch.empty(q.shape, dtype=out_dt, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    # the selector's statistics and choice, read once for the report (the
-    # timed steps decide on the device from the same statistics)
-    if args.mask_source == "pattern":
-        from workloads import pattern_of
-        pat = dict(pattern_of(cfg))
-        if pat.get("blocks") is not None:
-            pat["blocks"] = torch.from_numpy(pat["blocks"]).to(dev)
-
-        def encode():
-            return smh.encode_pattern(cfg.S, device=dev, workspace=ws, **pat)
-    else:
-        def encode():
-            return smh.encode_mask(mask_d, workspace=ws)
-
-    enc0 = encode()
-    st = smh.mask_stats_get(enc0)
-    which = args.kernel if args.kernel != "auto" else smh.select_kernel(
-        st, cfg.B, cfg.H, cfg.d, q.dtype)
+    timer = Timer(stream, args.eager)
+    cfg, mask = workload(args)
+    w = Workload(args, cfg, mask, dev)
+    q = w.sets[0]["q"]
+    st = w.stats
 
     proj = None
     if args.epilogue == "out_proj":
-        if out_dt != q.dtype:
+        if w.out_dt != q.dtype:
             raise SystemExit("--epilogue out_proj needs the attention output "
                              "in the input type (--out-dtype in)")
         D = cfg.H * cfg.d
@@ -326,25 +506,17 @@ def main():
         proj = (pw, pb, pr, pout)
 
     def step():
-        enc = encode()
-        smh.sparse_mha_fwd(q, k, v, enc, kernel=args.kernel,
-                           out_dtype=out_dt, out=out)
+        w.step(0)
         if proj is not None:
-            smh.out_proj(out, proj[0], proj[1], proj[2], out=proj[3])
-
-    def encode_only():
-        encode()
-
-    def fwd_only():
-        smh.sparse_mha_fwd(q, k, v, enc0, kernel=args.kernel,
-                           out_dtype=out_dt, out=out)
+            smh.out_proj(w.sets[0]["out"], proj[0], proj[1], proj[2],
+                         out=proj[3])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # A step enqueues three kernels and needs no host synchronisation, so
-    # it is captured once into a HIP graph and replayed (launch-bound
+    # A step enqueues its kernels and needs no host synchronisation, so it
+    # is captured once into a HIP graph and replayed (launch-bound
     # otherwise at small sizes).  `per_graph` steps per replay.
     per_graph = 1 if args.eager else max(1, min(10, args.steps))
     if args.steps % per_graph:
@@ -369,119 +541,99 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
+    del graph
 
-    def kernel_us(fn, reps=20):
-        """Average duration of one launch of fn's kernels: `reps` launches
-        back to back in one graph, bracketed by events on their stream."""
-        if args.eager:
-            fn()
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / reps
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / reps
-
-    enc_ms = kernel_us(encode_only) / 1e3
-    fwd_ms = kernel_us(fwd_only) / 1e3
+    enc_ms = timer.us(lambda: w.encode(0)) / 1e3
+    fwd_ms = timer.us(lambda: w.fwd(0)) / 1e3
     epi = None
     if proj is not None:
-        def proj_only():
-            smh.out_proj(out, proj[0], proj[1], proj[2], out=proj[3])
-        p_us = kernel_us(proj_only)
+        p_us = timer.us(lambda: smh.out_proj(w.sets[0]["out"], proj[0],
+                                             proj[1], proj[2], out=proj[3]))
         M, K, D = cfg.B * cfg.S, cfg.H * cfg.d, proj[0].shape[0]
         p_flops = 2.0 * M * K * D
         p_bytes = 2.0 * (M * K + D * K + D + 2 * M * D)
-        p_roof = ({"bound": "hbm", "achieved": p_bytes / p_us / 1e3,
-                   "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-                  if p_flops / p_bytes < RIDGE else
-                  {"bound": "mfma", "achieved": p_flops / p_us / 1e6,
-                   "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s"})
-        p_roof["frac"] = p_roof["achieved"] / p_roof["peak"]
         epi = {"kernel": "out_proj", "us": p_us, "M": M, "K": K, "N": int(D),
-               "tflops": p_flops / p_us / 1e6, "algorithmic_flops": p_flops,
-               "algorithmic_bytes": p_bytes, "roofline": p_roof}
+               "tflops": p_flops / p_us / 1e6,
+               "roofline": roofline_of(p_flops, p_bytes, p_us * 1e-6,
+                                       cfg.dtype)}
 
-    nnz = st["nnz"]              # total over the masks of a stack
-    BH = cfg.B * cfg.H
-    flops = 4.0 * cfg.d * users_per_mask(mask, cfg.B, cfg.H) * nnz
+    flops, tile_flops, attn_bytes, enc_bytes = w.work()
     value = flops / step_s / 1e12
-    eb_in = 2
-    eb_out = out.element_size()
-    rows = mb * mh * cfg.n_ot
-    attn_bytes = BH * cfg.S * cfg.d * (3 * eb_in + eb_out) + \
-        encoding_bytes(st, rows)
-    ai = flops / attn_bytes
     fwd_s = fwd_ms / 1e3
-    if ai < RIDGE:
-        roof = {"bound": "hbm", "achieved": attn_bytes / fwd_s / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": flops / fwd_s / 1e12,
-                "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "auto_fwd" if args.kernel == "auto" else f"{which}_fwd"
-    roof["algorithmic_bytes"] = attn_bytes
-    roof["algorithmic_flops"] = flops
+    roof = roofline_of(flops, attn_bytes, fwd_s, cfg.dtype)
+    roof["kernel"] = "auto_fwd" if args.kernel == "auto" else f"{w.kernel}_fwd"
     roof["traffic"] = stored_traffic(roof["kernel"], cfg.name)
     pred_row, pred_blk = smh.select_costs(st, cfg.B, cfg.H, cfg.d, q.dtype)
-    # encoder: the mask bytes it reads (none from a pattern) and the
-    # encoding it writes, against HBM peak
-    enc_bytes = (0 if args.mask_source == "pattern" else mask.size) + \
-        encoding_bytes(st, rows)
     encoder = {"us": enc_ms * 1e3, "algorithmic_bytes": enc_bytes,
                "achieved": enc_bytes / (enc_ms * 1e-3) / 1e9, "unit": "GB/s",
                "peak": HBM_PEAK_GBS}
     encoder["frac"] = encoder["achieved"] / HBM_PEAK_GBS
+    qkv_host = w.qkv_host
+    del w, proj
+    torch.cuda.empty_cache()
+
+    per_mask = None
+    default_opts = (args.seq_len == 0 and args.mask_stack == "shared" and
+                    args.mask_source == "dense" and args.kernel == "auto" and
+                    args.epilogue == "none" and args.out_dtype == "auto")
+    if args.per_mask == "on" or (args.per_mask == "auto" and default_opts and
+                                 args.config == 5):
+        per_mask = []
+        for cid in (1, 2, 3, 4, 5):
+            c = get_config(cid)
+            m = mask if c.name == cfg.name and args.seq_len == 0 else \
+                make_mask(c)
+            per_mask.append(measure(args, c, m, dev, timer,
+                                    not args.no_cold))
+            print(f"bench.py: per_mask {c.name} done", file=sys.stderr,
+                  flush=True)
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(cfg, mask, qkv, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, mask, qkv_host, args.cpu_seconds)
 
     line = {
         "metric": "effective TFLOP/s on valid QK pairs (4*d FLOPs per valid "
-                  "(query,key) pair) + % of MI355X dense MFMA peak",
+                  "(query,key) pair) + % of MI355X dense MFMA peak, per mask",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": step_s * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, seeded mask)",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S,
-                   "d": cfg.d, "mask": cfg.desc, "mask_stack": [mb, mh],
-                   "out_dtype": str(out_dt).replace("torch.", ""),
+                   "d": cfg.d, "mask": cfg.desc,
+                   "mask_stack": [int(x) for x in (mask.shape[:2]
+                                                   if mask.ndim == 4
+                                                   else (1, 1))],
+                   "out_dtype": w_out_dtype(args, cfg),
                    "launch": "eager" if args.eager else
                    f"hip graph, {per_graph} steps per replay",
                    "parallelism": "single GPU"},
         "pct_mfma_peak": 100.0 * value / MFMA_PEAK_TFLOPS[cfg.dtype],
-        "kernel": which,
+        "kernel": smh.select_kernel(st, cfg.B, cfg.H, cfg.d, q.dtype)
+        if args.kernel == "auto" else args.kernel,
         "encode_ms": enc_ms, "fwd_ms": fwd_ms,
         "fwd_tflops": flops / fwd_s / 1e12,
         "fwd_pct_mfma_peak": 100.0 * flops / fwd_s / 1e12 /
+        MFMA_PEAK_TFLOPS[cfg.dtype],
+        "tile_mfma_frac": tile_flops / fwd_s / 1e12 /
         MFMA_PEAK_TFLOPS[cfg.dtype],
         "selector_pred_us": {"rowwise": pred_row, "blockwise": pred_blk},
         "mask_stats": st,
         "roofline": roof,
         "encoder": encoder,
         "epilogue": epi,
+        "per_mask": per_mask,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def w_out_dtype(args, cfg):
+    if args.out_dtype == "f32" or (args.out_dtype == "auto" and
+                                   cfg.dtype == "bf16"):
+        return "float32"
+    return "float16" if cfg.dtype == "f16" else "bfloat16"
 
 
 if __name__ == "__main__":

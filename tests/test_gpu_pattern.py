@@ -42,11 +42,14 @@ def test_workload_patterns_bit_exact(cid):
     check(cfg.S, dev, pattern_of(cfg))
 
 
-def test_long_random_pattern_bit_exact():
+@pytest.mark.parametrize("S", [4096, 16384])
+def test_long_random_pattern_bit_exact(S):
     """The long-sequence family (causal, band 1024, 2% elsewhere) at
-    S = 4096 (the 16k mask takes the oracle minutes)."""
+    S = 4096 and at the 16k workload's own length (the oracle builds the
+    268 MB dense mask in about 15 s)."""
     dev = need_gpu()
-    check(4096, dev, dict(causal=True, window=1024, random_p=0.02, seed=5))
+    print(f"long_random pattern S={S}", flush=True)
+    check(S, dev, dict(causal=True, window=1024, random_p=0.02, seed=5))
 
 
 @pytest.mark.parametrize("S,pat", [
