@@ -14,7 +14,8 @@
  * Conventions shared by every entry point
  *   - Device buffers are owned by the caller.  The library never allocates,
  *     frees or synchronises device memory, except smh_mask_stats_get, which
- *     synchronises `stream`.
+ *     synchronises `stream`.  (smh_encode_masks_noalloc uses a fixed device
+ *     array of the library's code object as scratch.)
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Device work is enqueued on it and the call returns at once.
  *   - Every argument is validated on the host before anything is enqueued;
@@ -22,7 +23,8 @@
  *   - No C++ exception crosses this interface.  A failed kernel launch is
  *     reported as SMH_EHIP.
  *   - The library keeps no mutable global state besides cached device
- *     properties; calls are thread-safe.  Calls that share a workspace or an
+ *     properties and the static encoder scratch of
+ *     smh_encode_masks_noalloc (see there); calls are thread-safe.  Calls that share a workspace or an
  *     output buffer must be ordered by the caller (same stream or events).
  */
 #ifndef SMH_H_
@@ -175,6 +177,41 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
                             int32_t mask_h, int32_t S, void *workspace,
                             size_t ws_bytes, smh_mask_enc *enc_out,
                             void *stream);
+
+/* Size of the static encoder scratch of smh_encode_masks_noalloc: 40 MiB,
+ * enough for one mask of S = 16384 (32.5 MiB) or any stack with as many
+ * outer tiles.  Every device the library runs on holds one copy of it in
+ * the library's code object until the process ends. */
+#define SMH_STATIC_SCRATCH_BYTES ((size_t)40 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * encoder of smh_encode_masks without a workspace argument.  The encoding
+ * is written to the caller's `enc_buf`; the encoder's internal scratch is
+ * the library's static device array (SMH_STATIC_SCRATCH_BYTES per device,
+ * its address looked up once per device on the first call there).  The
+ * call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Same launches, result and layout as smh_encode_masks.
+ *   enc_bytes (in/out): with enc_buf == NULL the call only stores the
+ *       number of bytes the encoding needs in *enc_bytes and returns
+ *       SMH_OK (nothing enqueued, no device touched).  Otherwise *enc_bytes
+ *       is the capacity of enc_buf (SMH_ENOSPACE when smaller than that
+ *       number).
+ *   enc_buf: device memory, 256-byte aligned, on the current device; it
+ *       holds the encoding afterwards and must outlive every use of
+ *       *enc_out.
+ *   masks, mask_b, mask_h, S, enc_out, stream: as for smh_encode_masks;
+ *       the stream must belong to the current device.
+ * SMH_EUNSUPPORTED when the scratch the stack needs exceeds
+ * SMH_STATIC_SCRATCH_BYTES (about ceil(S/64)^2 * masks * 520 bytes).
+ * Every call on a device shares that device's scratch (no call needs it
+ * cleared, and each call's result depends only on its own inputs): calls
+ * that may overlap on one device (different streams, different host
+ * threads) race and must be ordered by the caller. */
+smh_status smh_encode_masks_noalloc(const uint8_t *masks, int32_t mask_b,
+                                    int32_t mask_h, int32_t S, void *enc_buf,
+                                    size_t *enc_bytes, smh_mask_enc *enc_out,
+                                    void *stream);
 
 /* A mask described by its pattern instead of stored ([EXP] storage-format
  * items: the encoding is built without the dense S x S mask).  Element

@@ -21,7 +21,8 @@ from ._lib import (SMH_AUTO, SMH_BF16, SMH_BLOCKWISE, SMH_F16, SMH_F32,
                    SMH_MAX_S, SMH_OK, SMH_ROWWISE, MaskEnc, MaskStats,
                    Pattern, SmhError, check, lib, status_string)
 
-__all__ = ["encode_mask", "encode_pattern", "encode_workspace_bytes",
+__all__ = ["encode_mask", "encode_masks_noalloc", "encode_pattern",
+           "encode_workspace_bytes",
            "mask_stats_get",
            "select_kernel", "select_costs", "sparse_mha_fwd", "out_proj",
            "version",
@@ -123,6 +124,43 @@ def encode_mask(mask, workspace=None):
         ctypes.byref(enc), _stream(mask.device))
     check(st, "smh_encode_masks")
     return MaskEncoding(workspace, enc, S, mb, mh)
+
+
+def encode_masks_noalloc(mask, out=None):
+    """encode_mask through smh_encode_masks_noalloc: the library allocates
+    nothing (its encoder scratch is a static device array) and the
+    encoding goes to `out` (a device uint8 tensor of at least
+    encode_noalloc_bytes(...) bytes; allocated here when None)."""
+    if mask.dtype not in (torch.bool, torch.uint8) or not mask.is_cuda:
+        raise TypeError("mask must be a bool or uint8 device tensor")
+    if mask.dim() not in (2, 4) or mask.shape[-1] != mask.shape[-2]:
+        raise ValueError("mask must be [S, S] or [mask_b, mask_h, S, S]")
+    mask = mask.contiguous()
+    if mask.data_ptr() % 16:
+        mask = mask.clone()
+    S = int(mask.shape[-1])
+    mb, mh = (1, 1) if mask.dim() == 2 else (int(mask.shape[0]),
+                                              int(mask.shape[1]))
+    need = encode_noalloc_bytes(S, mb, mh)
+    if out is None:
+        out = torch.empty(max(need, 1), dtype=torch.uint8, device=mask.device)
+    cap = ctypes.c_size_t(out.numel())
+    enc = MaskEnc()
+    check(lib().smh_encode_masks_noalloc(
+        ctypes.c_void_p(mask.data_ptr()), mb, mh, S,
+        ctypes.c_void_p(out.data_ptr()), ctypes.byref(cap),
+        ctypes.byref(enc), _stream(mask.device)), "smh_encode_masks_noalloc")
+    return MaskEncoding(out, enc, S, mb, mh)
+
+
+def encode_noalloc_bytes(S, mask_b=1, mask_h=1):
+    """Bytes of the encoding buffer smh_encode_masks_noalloc writes (its
+    size query: nothing is enqueued)."""
+    n = ctypes.c_size_t(0)
+    check(lib().smh_encode_masks_noalloc(None, int(mask_b), int(mask_h),
+                                         int(S), None, ctypes.byref(n), None,
+                                         None), "smh_encode_masks_noalloc")
+    return int(n.value)
 
 
 def encode_pattern(S, causal=False, window=-1, global_rows=0, global_cols=0,

@@ -10,10 +10,12 @@ SMH_F16, SMH_BF16, SMH_F32 = range(3)
 SMH_AUTO, SMH_ROWWISE, SMH_BLOCKWISE = range(3)
 SMH_MAX_S = 131072
 SMH_MAX_ENC_ROWS = 8192
+SMH_STATIC_SCRATCH_BYTES = 40 << 20
 
 # every exported name of include/smh.h
 EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_masks_workspace_bytes",
-           "smh_encode_mask", "smh_encode_masks", "smh_encode_pattern",
+           "smh_encode_mask", "smh_encode_masks", "smh_encode_masks_noalloc",
+           "smh_encode_pattern",
            "smh_mask_stats_get",
            "smh_select_kernel", "smh_select_costs", "smh_sparse_mha_fwd",
            "smh_out_proj",
@@ -81,6 +83,10 @@ def lib():
         L.smh_encode_masks.argtypes = [p, i32, i32, i32, p, sz,
                                        ctypes.POINTER(MaskEnc), p]
         L.smh_encode_masks.restype = ctypes.c_int
+        L.smh_encode_masks_noalloc.argtypes = [p, i32, i32, i32, p,
+                                               ctypes.POINTER(sz),
+                                               ctypes.POINTER(MaskEnc), p]
+        L.smh_encode_masks_noalloc.restype = ctypes.c_int
         L.smh_encode_pattern.argtypes = [ctypes.POINTER(Pattern), i32, p, sz,
                                          ctypes.POINTER(MaskEnc), p]
         L.smh_encode_pattern.restype = ctypes.c_int

@@ -123,7 +123,8 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
         char *ws = (char *)workspace;
         smh_mask_enc e;
         fill_enc(e, ws, L, S, mask_b, mask_h);
-        if (launch_encode(masks, S, ws, L, e, (hipStream_t)stream) !=
+        if (launch_encode(masks, S, L, e, ws + enc_output_bytes(L),
+                          (hipStream_t)stream) !=
             hipSuccess)
             return SMH_EHIP;
         *enc_out = e;
@@ -152,7 +153,43 @@ smh_status smh_encode_pattern(const smh_pattern *pat, int32_t S,
         char *ws = (char *)workspace;
         smh_mask_enc e;
         fill_enc(e, ws, L, S, 1, 1);
-        if (launch_encode_pattern(*pat, S, ws, L, e, (hipStream_t)stream) !=
+        if (launch_encode_pattern(*pat, S, L, e, ws + enc_output_bytes(L),
+                                  (hipStream_t)stream) !=
+            hipSuccess)
+            return SMH_EHIP;
+        *enc_out = e;
+        return SMH_OK;
+    } catch (...) {
+        return SMH_EHIP;
+    }
+}
+
+smh_status smh_encode_masks_noalloc(const uint8_t *masks, int32_t mask_b,
+                                    int32_t mask_h, int32_t S, void *enc_buf,
+                                    size_t *enc_bytes, smh_mask_enc *enc_out,
+                                    void *stream) {
+    try {
+        if (stack_rows(mask_b, mask_h, S) < 0 || !enc_bytes) return SMH_EINVAL;
+        const int64_t G = (int64_t)mask_b * mask_h;
+        const EncLayout L = enc_layout(S, G);
+        const size_t need = enc_output_bytes(L);
+        if (!enc_buf) {  // size query: nothing enqueued, no device touched
+            *enc_bytes = need;
+            return SMH_OK;
+        }
+        if (!enc_out) return SMH_EINVAL;
+        if (S > 0 && (!masks || !aligned(masks, 16))) return SMH_EINVAL;
+        if (!aligned(enc_buf, 256)) return SMH_EINVAL;
+        if (*enc_bytes < need) return SMH_ENOSPACE;
+        if (enc_scratch_bytes(L) > SMH_STATIC_SCRATCH_BYTES) return SMH_EUNSUPPORTED;
+        if (S > 0 && overlaps(masks, (size_t)G * S * S, enc_buf, need))
+            return SMH_EINVAL;
+        char *scratch = nullptr;
+        if (static_scratch(&scratch) != hipSuccess) return SMH_EHIP;
+        char *ws = (char *)enc_buf;
+        smh_mask_enc e;
+        fill_enc(e, ws, L, S, mask_b, mask_h);
+        if (launch_encode(masks, S, L, e, scratch, (hipStream_t)stream) !=
             hipSuccess)
             return SMH_EHIP;
         *enc_out = e;

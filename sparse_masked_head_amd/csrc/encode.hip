@@ -28,6 +28,7 @@
 // the mask: the result is deterministic and equals appending tiles row by
 // row, column by column.
 #include <math.h>
+#include <mutex>
 
 #include "smh_internal.h"
 
@@ -674,8 +675,8 @@ namespace {
 // The launches of an encode: strip pass (`strip` enqueues it on the
 // segments), then the scan and placement.
 template <typename StripLaunch>
-hipError_t encode_launches(StripLaunch strip, int32_t S, char *ws,
-                           const EncLayout &L, const smh_mask_enc &enc,
+hipError_t encode_launches(StripLaunch strip, int32_t S, const EncLayout &L,
+                           const smh_mask_enc &enc, char *scratch,
                            hipStream_t stream) {
     if (S == 0) {
         hipLaunchKernelGGL(enc_empty, dim3(1), dim3(64), 0, stream, enc);
@@ -687,14 +688,15 @@ hipError_t encode_launches(StripLaunch strip, int32_t S, char *ws,
     if (plan.total <= 0 || plan.win > kMaxSegWin || plan.per_row > 64 ||
         n > kMaxN || R > kScanRows || (int64_t)G * n != L.rows)
         return hipErrorInvalidValue;
-    Seg sg;
-    sg.cnt = (uint64_t *)(ws + L.seg_cnt);
-    sg.off = (uint64_t *)(ws + L.seg_off);
-    sg.nnz = (uint64_t *)(ws + L.seg_nnz);
-    sg.any = (uint64_t *)(ws + L.seg_any);
-    sg.fcol = (int32_t *)(ws + L.seg_fcol);
-    sg.pcol = (int32_t *)(ws + L.seg_pcol);
-    sg.words = (uint64_t *)(ws + L.seg_words);
+    Seg sg;  // the scratch arrays keep their workspace offsets past seg_cnt
+    char *sc = scratch - L.seg_cnt;
+    sg.cnt = (uint64_t *)(sc + L.seg_cnt);
+    sg.off = (uint64_t *)(sc + L.seg_off);
+    sg.nnz = (uint64_t *)(sc + L.seg_nnz);
+    sg.any = (uint64_t *)(sc + L.seg_any);
+    sg.fcol = (int32_t *)(sc + L.seg_fcol);
+    sg.pcol = (int32_t *)(sc + L.seg_pcol);
+    sg.words = (uint64_t *)(sc + L.seg_words);
     sg.cap = (int)L.seg_cap;
     strip(n, plan, sg);
     if (plan.total <= kFusedMaxSegs && R <= kFusedRows) {
@@ -711,8 +713,8 @@ hipError_t encode_launches(StripLaunch strip, int32_t S, char *ws,
 
 }  // namespace
 
-hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
-                         const EncLayout &L, const smh_mask_enc &enc,
+hipError_t launch_encode(const uint8_t *mask, int32_t S, const EncLayout &L,
+                         const smh_mask_enc &enc, char *scratch,
                          hipStream_t stream) {
     auto strip = [&](int n, SegPlan plan, Seg sg) {
         if (S % 64 == 0)
@@ -725,12 +727,12 @@ hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
             hipLaunchKernelGGL(enc_strip<kDwords>, dim3(plan.total), dim3(256), 0,
                                stream, mask, S, n, plan, sg);
     };
-    return encode_launches(strip, S, ws, L, enc, stream);
+    return encode_launches(strip, S, L, enc, scratch, stream);
 }
 
-hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S, char *ws,
+hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S,
                                  const EncLayout &L, const smh_mask_enc &enc,
-                                 hipStream_t stream) {
+                                 char *scratch, hipStream_t stream) {
     Pattern p;
     p.causal = pat.causal != 0;
     p.window = pat.window;
@@ -744,7 +746,33 @@ hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S, char *ws,
         hipLaunchKernelGGL(enc_pattern_strip, dim3(plan.total), dim3(256), 0,
                            stream, p, S, n, plan, sg);
     };
-    return encode_launches(strip, S, ws, L, enc, stream);
+    return encode_launches(strip, S, L, enc, scratch, stream);
+}
+
+// The encoder scratch of smh_encode_masks_noalloc: a fixed array in the
+// code object, one copy per device, for callers that cannot allocate.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// kernels and copies get the address static_scratch() looked up.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[SMH_STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(char **ptr) {
+    static std::mutex mu;
+    static char *addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return hipErrorInvalidValue;
+        addr[dev] = static_cast<char *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace smh

@@ -92,17 +92,28 @@ inline EncLayout enc_layout(int32_t S, int64_t G) {
     return L;
 }
 
+// The encoding proper is the workspace's first enc_output_bytes; the
+// encoder's scratch (the per-segment arrays, from seg_cnt on) follows.
+inline size_t enc_output_bytes(const EncLayout &L) { return L.seg_cnt; }
+inline size_t enc_scratch_bytes(const EncLayout &L) { return L.total - L.seg_cnt; }
+
 // Encoder of a stack of G = enc.mask_b * enc.mask_h masks [G][S][S]: two or
-// three launches on `stream` (strip pass, [scan,] placement).
-hipError_t launch_encode(const uint8_t *mask, int32_t S, char *ws,
-                         const EncLayout &L, const smh_mask_enc &enc,
+// three launches on `stream` (strip pass, [scan,] placement).  The encoding
+// goes where `enc` points; `scratch` (enc_scratch_bytes(L) bytes, 256-byte
+// aligned, no preparation needed) holds the per-segment arrays.
+hipError_t launch_encode(const uint8_t *mask, int32_t S, const EncLayout &L,
+                         const smh_mask_enc &enc, char *scratch,
                          hipStream_t stream);
 
 // Encoder of the mask a pattern describes (one mask, enc.mask_b = mask_h =
 // 1): the pattern strip pass, then the same scan and placement.
-hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S, char *ws,
+hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S,
                                  const EncLayout &L, const smh_mask_enc &enc,
-                                 hipStream_t stream);
+                                 char *scratch, hipStream_t stream);
+
+// Device address of the library's static encoder scratch on the current
+// device (SMH_STATIC_SCRATCH_BYTES bytes; looked up once per device).
+hipError_t static_scratch(char **ptr);
 
 // Block-wise kernel launcher.  in_dt: 0 f16, 1 bf16; out_dt: 0/1/2 (f32).
 hipError_t launch_blockwise(const void *q, const void *k, const void *v,
