@@ -147,3 +147,39 @@ def encode_stack(masks, encode=None):
     for key in ("nnz", "n_full", "n_partial", "n_empty_rows"):
         out[key] = sum(int(e[key]) for e in parts)
     return out
+
+
+def row_entries(mask, theta):
+    """Row-wise entries of the sparse outer tiles of one [S, S] mask.
+
+    The abstract's row-wise kernel reads a storage format of its own ("row-
+    wise or block-wise kernels with unique storage formats", arXiv record
+    of "Accelerating Sparse Transformer Inference on GPU", abstract); the
+    pages do not print it.  Reading taken here: for outer-tile row I and
+    group q of 16 query rows (rows 64I + 16q .. 64I + 16q + 15), every key
+    j of a *sparse* tile of row I (a tile with some but at most ``theta``
+    valid elements) that some row of the group attends to, in ascending j,
+    as the pair (j, rows) with bit k of rows set iff row 64I + 16q + k
+    attends to j.  Written from the dense mask (numpy over the tiles of a
+    row); rows and columns past S are not valid.
+
+    Returns {(I, q): [(j, rows), ...]} for every I < ceil(S/64), q < 4
+    (empty lists included)."""
+    m = np.asarray(mask, dtype=bool)
+    S = m.shape[0]
+    n = (S + OT - 1) // OT
+    pad = np.zeros((n * OT, n * OT), dtype=bool)
+    pad[:S, :S] = m
+    weight = (1 << np.arange(16, dtype=np.int64))        # bit k = row k
+    out = {}
+    for I in range(n):
+        strip = pad[OT * I:OT * I + OT].reshape(OT, n, OT)  # [row, J, col]
+        cnt = strip.sum(axis=(0, 2))
+        sparse = np.nonzero((cnt > 0) & (cnt < OT * OT) & (cnt <= theta))[0]
+        for q in range(4):
+            rows = np.einsum("kjc,k->jc", strip[16 * q:16 * q + 16, sparse]
+                             .astype(np.int64), weight)     # [tile, col]
+            keys = (OT * sparse[:, None] + np.arange(OT)[None, :])
+            live = rows != 0
+            out[(I, q)] = list(zip(keys[live].tolist(), rows[live].tolist()))
+    return out

@@ -320,3 +320,99 @@ def test_stack_sections_decode(mb, mh, S):
         same(encode_stack(masks, encode=encode_py), enc)
     if mb * mh == 1:
         same(enc, encode_c(masks[0, 0]))
+
+
+# ---- row-wise entries of sparse tiles (oracle.encode.row_entries) ----
+
+def test_row_entries_by_hand():
+    """Hand-built tiles: one element, a whole column, a whole row, the
+    threshold (theta valid elements in, theta + 1 out), full and dense
+    tiles (no entries), a ragged S."""
+    from oracle.encode import row_entries
+    S = 256
+    m = np.zeros((S, S), bool)
+    m[70, 130] = True                 # tile (1, 2): one element
+    m[128:192, 200] = True            # tile (2, 3): a whole column
+    m[5, 64:128] = True               # tile (0, 1): a whole row
+    m[192:256, 0:64] = True           # tile (3, 0): full, no entries
+    m[200, 70] = True                 # tile (3, 1): one element
+    e = row_entries(m, theta=64)
+    assert e[(1, 0)] == [(130, 1 << 6)]
+    assert all(not e[(1, q)] for q in (1, 2, 3))
+    for q in range(4):                # the column: one entry per group
+        assert e[(2, q)] == [(200, 0xFFFF)]
+    assert e[(0, 0)] == [(j, 1 << 5) for j in range(64, 128)]
+    assert e[(3, 0)] == [(70, 1 << 8)]
+    # the 64-element row and column tiles have 64 <= theta elements; with
+    # theta = 63 they are dense and leave no entries
+    e2 = row_entries(m, theta=63)
+    assert not e2[(0, 0)] and all(not e2[(2, q)] for q in range(4))
+    assert e2[(1, 0)] == [(130, 1 << 6)]
+    # ragged S: elements past S do not exist, so every tile but (0, 0)
+    # (full) is cut, hence partial, hence sparse under theta = 4095
+    r = row_entries(np.ones((100, 100), bool), theta=4095)
+    for q in range(4):                # row 0: tile (0, 1), keys 64 .. 99
+        assert r[(0, q)] == [(j, 0xFFFF) for j in range(64, 100)]
+    assert r[(1, 0)] == [(j, 0xFFFF) for j in range(100)]
+    assert r[(1, 1)] == [(j, 0xFFFF) for j in range(100)]
+    assert r[(1, 2)] == [(j, 0xF) for j in range(100)]   # rows 96 .. 99
+    assert not r[(1, 3)]
+
+
+def test_row_entries_reconstruct_sparse_tiles():
+    """Decoding the entries gives back exactly the valid pairs of the
+    sparse tiles (and nothing of the other tiles); keys ascend."""
+    from oracle.encode import row_entries
+    rng = np.random.default_rng(5)
+    S, theta = 320, 256
+    m = rng.random((S, S)) < 0.03
+    m |= np.abs(np.arange(S)[:, None] - np.arange(S)[None, :]) <= 20
+    e = row_entries(m, theta)
+    back = np.zeros_like(m)
+    for (I, q), lst in e.items():
+        keys = [j for j, _ in lst]
+        assert keys == sorted(set(keys))
+        for j, rows in lst:
+            assert rows
+            for k in range(16):
+                if rows >> k & 1:
+                    back[64 * I + 16 * q + k, j] = True
+    n = S // 64
+    sparse = np.zeros_like(m)
+    for I in range(n):
+        for J in range(n):
+            t = m[64 * I:64 * I + 64, 64 * J:64 * J + 64]
+            if 0 < t.sum() <= theta:
+                sparse[64 * I:64 * I + 64, 64 * J:64 * J + 64] = t
+    assert sparse.any() and np.array_equal(back, sparse)
+
+
+def test_row_entries_brute_force():
+    """Against an element-by-element loop over tiles, groups, columns and
+    rows, on a small random mask with sparse, dense and full tiles."""
+    from oracle.encode import row_entries
+    rng = np.random.default_rng(8)
+    S, theta = 200, 256
+    m = rng.random((S, S)) < rng.choice([0.005, 0.03, 0.5], (S, 1))
+    m[0:64, 0:64] = True
+    e = row_entries(m, theta)
+    n = -(-S // 64)
+    for I in range(n):
+        for q in range(4):
+            want = []
+            for J in range(n):
+                cnt = sum(1 for r in range(64) for c in range(64)
+                          if 64 * I + r < S and 64 * J + c < S and
+                          m[64 * I + r, 64 * J + c])
+                if cnt == 0 or cnt == 4096 or cnt > theta:
+                    continue
+                for c in range(64):
+                    j = 64 * J + c
+                    rows = 0
+                    for k in range(16):
+                        i = 64 * I + 16 * q + k
+                        if i < S and j < S and m[i, j]:
+                            rows |= 1 << k
+                    if rows:
+                        want.append((j, rows))
+            assert e[(I, q)] == want, (I, q)
