@@ -49,7 +49,8 @@ def parse():
                          "the row-wise kernel's regime, a 0.1%% random "
                          "mask; 7 = workload 5's far tiles alone)")
     ap.add_argument("--kernel", default="auto",
-                    choices=["auto", "rowwise", "blockwise"])
+                    choices=["auto", "rowwise", "blockwise",
+                             "blockwise_dense"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 disables)")
     ap.add_argument("--eager", action="store_true",

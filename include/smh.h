@@ -50,7 +50,12 @@ typedef enum { SMH_F16 = 0, SMH_BF16 = 1, SMH_F32 = 2 } smh_dtype;
 typedef enum {
     SMH_AUTO = 0,       /* let smh_select_kernel decide (needs host stats) */
     SMH_ROWWISE = 1,    /* row-wise kernel ([EXP] row-wise kernel item)     */
-    SMH_BLOCKWISE = 2   /* block-wise kernel ([EXP] block-wise kernel item) */
+    SMH_BLOCKWISE = 2,  /* block-wise kernel ([EXP] block-wise kernel item)
+                           with per-tile dispatch: sparse partial tiles (at
+                           most SMH_SPARSE_TILE_MAX valid elements) on its
+                           gather path when S <= 65536                      */
+    SMH_BLOCKWISE_DENSE = 3  /* block-wise kernel, every stored tile on the
+                                matrix-core tile path                        */
 } smh_kernel;
 
 /* Largest sequence length accepted (the encoding workspace of one mask
@@ -62,6 +67,11 @@ typedef enum {
 /* Outer tile edge and inner tile edge, in elements. */
 #define SMH_OT 64
 #define SMH_IT 8
+/* A partial outer tile with at most this many valid elements (1/16 of its
+ * 4096) is "sparse": the block-wise kernel computes it on its gather path
+ * (each wavefront gathers the keys its 16 query rows see) instead of as a
+ * dense 64 x 64 tile, when the mask's length allows (S <= 65536). */
+#define SMH_SPARSE_TILE_MAX 256
 
 /* The two-level encoding of a stack of S x S masks ([EXP] storage-format
  * items).  A host struct of device pointers into the caller's workspace; it
@@ -87,20 +97,36 @@ typedef enum {
  *       inner tile (ir, ic), covering tile rows 8ir..8ir+7 and columns
  *       8ic..8ic+7; bit 8*r+c of it is element (8ir+r, 8ic+c).
  *   Outer tiles with no valid element appear in neither list.
- *   stats[5] (device int64), summed over the stack: nnz, n_full,
- *       n_partial, n_empty_rows (query rows with no valid key), and
- *       max_row_tiles (stored tiles in the fullest outer-tile row).
+ *   stats[8] (device int64), summed over the stack: nnz, n_full,
+ *       n_partial, n_empty_rows (query rows with no valid key),
+ *       max_row_tiles (stored tiles in the fullest outer-tile row), n_sparse
+ *       (partial tiles with at most SMH_SPARSE_TILE_MAX valid elements),
+ *       sparse_nnz (their valid elements) and row_entries (the row-wise
+ *       entries of those tiles, the sum of row_ent_cnt).
+ *   part_pop[n_partial] (device int32): valid elements of each partial tile
+ *       (the population count of its 64 words), in part_col_idx order.
+ *   row_ent, row_ent_cnt (device uint32, int32): the row-wise format of
+ *       the sparse partial tiles ([ABS]: the row-wise kernel reads a format
+ *       of its own), built when S <= 65536 (else every count is 0).  For
+ *       encoding row r (outer-tile row I) and group q < 4 of 16 query rows
+ *       (rows 64I + 16q .. +15): the keys j of the row's sparse tiles that
+ *       some query of the group attends to, ascending, each entry
+ *       rows << 16 | j with bit 16 + k set iff query 64I + 16q + k attends
+ *       to j; entry i < row_ent_cnt[4r + q] at
+ *       row_ent[256 * part_row_ptr[r] + 64 * q * np + i], np = the row's
+ *       partial-tile count.
  *   row_order[R] (device int32): the encoding's rows sorted by their number
  *       of stored tiles, most first, ties by ascending row (a schedule).
  *   row_info[R][16] (device int32): a summary of each row that a kernel
  *       reads in one load: [0] full_row_ptr[r], [1] its full-tile count,
  *       [2] part_row_ptr[r], [3] its partial-tile count, [4..7] the columns
  *       of the row's first four stored tiles in list order (full tiles,
- *       then partial tiles), -1 past the row's last tile, [8..12] the
- *       encoding's nnz (low, high 32 bits), n_full, n_partial and
- *       max_row_tiles, [13..15] 0.
- * Capacities reserved in the workspace: col_idx arrays R * n_ot, bitmaps
- * R * n_ot * 64 words. */
+ *       then partial tiles), -1 past the row's last tile, [8..15] the
+ *       encoding's nnz (low, high 32 bits), n_full, n_partial,
+ *       max_row_tiles, n_sparse and row_entries (low, high 32 bits).
+ * Capacities reserved in the workspace: col_idx and part_pop arrays
+ * R * n_ot, bitmaps R * n_ot * 64 words, row_ent R * n_ot * 256 entries
+ * (S <= 65536). */
 typedef struct {
     int32_t S;
     int32_t n_ot;
@@ -114,6 +140,9 @@ typedef struct {
     int64_t *stats;
     int32_t *row_order;
     int32_t *row_info;
+    int32_t *part_pop;
+    uint32_t *row_ent;
+    int32_t *row_ent_cnt;
 } smh_mask_enc;
 
 /* Host copy of the encoding statistics (totals over the masks of the
@@ -127,6 +156,9 @@ typedef struct {
     int32_t max_row_tiles; /* stored tiles in the fullest outer-tile row */
     int32_t mask_b;       /* the stack's shape, as in smh_mask_enc */
     int32_t mask_h;
+    int32_t n_sparse;     /* partial tiles of at most SMH_SPARSE_TILE_MAX valid elements */
+    int64_t sparse_nnz;   /* valid pairs in those tiles */
+    int64_t row_entries;  /* their row-wise entries (0 when S > 65536) */
 } smh_mask_stats;
 
 /* Bytes of device workspace smh_encode_mask needs for sequence length S
@@ -178,11 +210,11 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
                             size_t ws_bytes, smh_mask_enc *enc_out,
                             void *stream);
 
-/* Size of the static encoder scratch of smh_encode_masks_noalloc: 40 MiB,
- * enough for one mask of S = 16384 (32.5 MiB) or any stack with as many
+/* Size of the static encoder scratch of smh_encode_masks_noalloc: 100 MiB,
+ * enough for one mask of S = 16384 (96.8 MiB) or any stack with as many
  * outer tiles.  Every device the library runs on holds one copy of it in
  * the library's code object until the process ends. */
-#define SMH_STATIC_SCRATCH_BYTES ((size_t)40 << 20)
+#define SMH_STATIC_SCRATCH_BYTES ((size_t)100 << 20)
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
@@ -203,7 +235,8 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
  *   masks, mask_b, mask_h, S, enc_out, stream: as for smh_encode_masks;
  *       the stream must belong to the current device.
  * SMH_EUNSUPPORTED when the scratch the stack needs exceeds
- * SMH_STATIC_SCRATCH_BYTES (about ceil(S/64)^2 * masks * 520 bytes).
+ * SMH_STATIC_SCRATCH_BYTES (about ceil(S/64)^2 * masks * 1544 bytes for
+ * S <= 65536, which build the row-wise entries, 520 bytes above).
  * Every call on a device shares that device's scratch (no call needs it
  * cleared, and each call's result depends only on its own inputs): calls
  * that may overlap on one device (different streams, different host

@@ -17,7 +17,8 @@ import ctypes
 
 import torch
 
-from ._lib import (SMH_AUTO, SMH_BF16, SMH_BLOCKWISE, SMH_F16, SMH_F32,
+from ._lib import (SMH_AUTO, SMH_BF16, SMH_BLOCKWISE, SMH_BLOCKWISE_DENSE,
+                   SMH_F16, SMH_F32,
                    SMH_MAX_S, SMH_OK, SMH_ROWWISE, MaskEnc, MaskStats,
                    Pattern, SmhError, check, lib, status_string)
 
@@ -29,7 +30,7 @@ __all__ = ["encode_mask", "encode_masks_noalloc", "encode_pattern",
            "MaskEncoding", "SmhError", "KERNELS"]
 
 KERNELS = {"auto": SMH_AUTO, "rowwise": SMH_ROWWISE,
-           "blockwise": SMH_BLOCKWISE}
+           "blockwise": SMH_BLOCKWISE, "blockwise_dense": SMH_BLOCKWISE_DENSE}
 _KNAME = {v: k for k, v in KERNELS.items()}
 _DT = {torch.float16: SMH_F16, torch.bfloat16: SMH_BF16,
        torch.float32: SMH_F32}
@@ -91,7 +92,10 @@ class MaskEncoding:
             part_bitmaps=view(e.part_bitmaps, st["n_partial"] * 64,
                               torch.int64, 8).view(-1, 64),
             row_order=view(e.row_order, n, torch.int32, 4),
-            row_info=view(e.row_info, 16 * n, torch.int32, 4).view(-1, 16))
+            row_info=view(e.row_info, 16 * n, torch.int32, 4).view(-1, 16),
+            part_pop=view(e.part_pop, st["n_partial"], torch.int32, 4),
+            row_ent_cnt=view(e.row_ent_cnt, 4 * n, torch.int32, 4).view(-1, 4),
+            row_ent=view(e.row_ent, 256 * st["n_partial"], torch.int32, 4))
 
 
 def encode_mask(mask, workspace=None):
@@ -212,8 +216,11 @@ def mask_stats_get(enc):
 def _stats_struct(st):
     s = MaskStats()
     for k, _ in MaskStats._fields_:
-        # a dict without the stack shape describes one mask
-        setattr(s, k, int(st.get(k, 1) if k in ("mask_b", "mask_h") else st[k]))
+        # a dict without the stack shape describes one mask, one without the
+        # sparse-tile counts a mask with no sparse tile
+        dflt = {"mask_b": 1, "mask_h": 1, "n_sparse": 0, "sparse_nnz": 0,
+                "row_entries": 0}
+        setattr(s, k, int(st[k] if k in st else dflt[k]))
     return s
 
 

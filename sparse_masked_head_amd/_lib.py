@@ -7,10 +7,11 @@ LIB_PATH = os.path.join(HERE, "libsmh.so")
 
 SMH_OK, SMH_EINVAL, SMH_EUNSUPPORTED, SMH_ENOSPACE, SMH_EHIP = range(5)
 SMH_F16, SMH_BF16, SMH_F32 = range(3)
-SMH_AUTO, SMH_ROWWISE, SMH_BLOCKWISE = range(3)
+SMH_AUTO, SMH_ROWWISE, SMH_BLOCKWISE, SMH_BLOCKWISE_DENSE = range(4)
 SMH_MAX_S = 131072
 SMH_MAX_ENC_ROWS = 8192
-SMH_STATIC_SCRATCH_BYTES = 40 << 20
+SMH_STATIC_SCRATCH_BYTES = 100 << 20
+SMH_SPARSE_TILE_MAX = 256
 
 # every exported name of include/smh.h
 EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_masks_workspace_bytes",
@@ -32,7 +33,10 @@ class MaskEnc(ctypes.Structure):
                 ("part_bitmaps", ctypes.c_void_p),
                 ("stats", ctypes.c_void_p),
                 ("row_order", ctypes.c_void_p),
-                ("row_info", ctypes.c_void_p)]
+                ("row_info", ctypes.c_void_p),
+                ("part_pop", ctypes.c_void_p),
+                ("row_ent", ctypes.c_void_p),
+                ("row_ent_cnt", ctypes.c_void_p)]
 
 
 class Pattern(ctypes.Structure):
@@ -48,7 +52,9 @@ class MaskStats(ctypes.Structure):
                 ("n_full", ctypes.c_int32), ("n_partial", ctypes.c_int32),
                 ("n_empty_rows", ctypes.c_int32),
                 ("max_row_tiles", ctypes.c_int32),
-                ("mask_b", ctypes.c_int32), ("mask_h", ctypes.c_int32)]
+                ("mask_b", ctypes.c_int32), ("mask_h", ctypes.c_int32),
+                ("n_sparse", ctypes.c_int32), ("sparse_nnz", ctypes.c_int64),
+                ("row_entries", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

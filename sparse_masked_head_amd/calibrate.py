@@ -6,7 +6,9 @@ the coefficients of the kernel-choice cost model (csrc/select_model.h).
 
 Each point times the forced row-wise and block-wise kernels with HIP events
 over back-to-back launches (inputs resident, mask encoded once) and records
-the encoding statistics the model sees.
+the encoding statistics the model sees.  The block-wise kernel is timed as
+SMH_AUTO runs it: with the per-tile dispatch of sparse partial tiles to its
+gather path.
 """
 import argparse
 import json
@@ -30,7 +32,7 @@ MASKS_LONG = [("random", {"p": 0.001}), ("random", {"p": 0.01}),
 SIZES_LONG = [8192, 16384]
 HEADS_LONG = [1, 8, 32]
 # the decision rule of select_model: row-wise when t_row < ROW_MARGIN * t_blk
-ROW_MARGIN = 0.9
+ROW_MARGIN = 1.0
 
 
 def _time(fn, reps):
@@ -94,12 +96,20 @@ def sweep(out_path, quick=False):
 
 def model(coef, p):
     """Python restatement of select_costs_us for fitting (same formula)."""
-    launch, bt, bp, bs, rg, rk, rsg, rsk = coef
+    launch, bt, bp, bs, rg, rk, rsg, rsk, be, bsp, bes, launch_r = coef
     st = p["stats"]
-    n = p["S"] // 64
+    n = -(-p["S"] // 64)
     tiles = st["n_full"] + st["n_partial"]
-    w_blk = p["BH"] * (tiles * bt + st["n_partial"] * bp)
-    t_blk = launch + max(w_blk, st["max_row_tiles"] * bs)
+    ents = st.get("row_entries", 0)
+    nsp = st.get("n_sparse", 0) if ents > 0 else 0
+    w_blk = p["BH"] * ((tiles - nsp) * bt + (st["n_partial"] - nsp) * bp +
+                       ents * be + nsp * bsp)
+    # heaviest row: its tiles split like the mask's, the sparse ones costing
+    # their entries per wavefront (4 wavefronts, one group of 16 rows each)
+    f = nsp / tiles if tiles else 0.0
+    ept = ents / (4.0 * nsp) if nsp else 0.0
+    crit = st["max_row_tiles"] * ((1.0 - f) * bs + f * ept * bes)
+    t_blk = launch + max(w_blk, crit)
     live = 64.0 * st["n_full"]
     if st["n_partial"] > 0:
         rho = (st["nnz"] - 4096.0 * st["n_full"]) / (4096.0 * st["n_partial"])
@@ -109,7 +119,7 @@ def model(coef, p):
     w_row = p["BH"] * (tiles * rg + 8.0 * chunks * rk)
     live_max = live / tiles * st["max_row_tiles"] if tiles else 0.0
     s_row = st["max_row_tiles"] / 8.0 * rsg + (live_max / 64.0 + 1.0) * rsk
-    t_row = launch + max(w_row, s_row)
+    t_row = launch_r + max(w_row, s_row)
     return t_row, t_blk
 
 
@@ -127,7 +137,7 @@ def fit(points):
                 r.append(np.log(tr / p["t_row_us"]))
                 r.append(np.log(tb / p["t_blk_us"]))
             return np.array(r)
-        c0 = np.array([4.0, 1e-3, 2e-4, 0.5, 1e-4, 1e-3, 1.0, 1.0])
+        c0 = np.array([4.0, 1e-3, 2e-4, 0.5, 1e-4, 1e-3, 1.0, 1.0, 5e-5, 1e-4, 0.02, 4.0])
         res = least_squares(resid, c0, x_scale=c0)
         c = np.abs(res.x)
         agree = regret = best_sum = 0
@@ -142,7 +152,7 @@ def fit(points):
         out[d] = dict(coef=c.tolist(), rms_log=float(np.sqrt(np.mean(
             res.fun ** 2))), agree=agree, n=len(pts),
             regret=regret / best_sum)
-        print(f"d={d}: coef {np.array2string(c, precision=4)}  rms log "
+        print(f"d={d}: coef {', '.join('%.5g' % x for x in c)}  rms log "
               f"{out[d]['rms_log']:.3f}  choice agrees {agree}/{len(pts)}  "
               f"time lost to wrong picks {100 * regret / best_sum:.2f}%")
     return out

@@ -37,7 +37,12 @@ smh_status check_stats(const smh_mask_stats *st) {
     const int64_t n = ((int64_t)st->S + SMH_OT - 1) / SMH_OT;
     const int64_t G = (int64_t)st->mask_b * st->mask_h;
     if (st->n_full < 0 || st->n_partial < 0 || st->nnz < 0 ||
-        st->max_row_tiles < 0 || st->n_empty_rows < 0)
+        st->max_row_tiles < 0 || st->n_empty_rows < 0 || st->n_sparse < 0 ||
+        st->sparse_nnz < 0)
+        return SMH_EINVAL;
+    if (st->n_sparse > st->n_partial || st->row_entries < 0 ||
+        st->sparse_nnz > (int64_t)st->n_sparse * SMH_SPARSE_TILE_MAX ||
+        st->row_entries > st->sparse_nnz)
         return SMH_EINVAL;
     if ((int64_t)st->n_full + st->n_partial > rows * n ||
         st->nnz > G * st->S * st->S || st->max_row_tiles > n)
@@ -72,6 +77,9 @@ void fill_enc(smh_mask_enc &e, char *ws, const EncLayout &L, int32_t S,
     e.stats = (int64_t *)(ws + L.stats);
     e.row_order = (int32_t *)(ws + L.row_order);
     e.row_info = (int32_t *)(ws + L.row_info);
+    e.part_pop = (int32_t *)(ws + L.part_pop);
+    e.row_ent = (uint32_t *)(ws + L.row_ent);
+    e.row_ent_cnt = (int32_t *)(ws + L.row_ent_cnt);
 }
 
 // (batch, head) pairs that share each mask of the stack.
@@ -211,7 +219,7 @@ smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
     try {
         if (!enc || !out || !enc->stats) return SMH_EINVAL;
         if (stack_rows(enc->mask_b, enc->mask_h, enc->S) < 0) return SMH_EINVAL;
-        int64_t h[5];
+        int64_t h[8];
         hipStream_t s = (hipStream_t)stream;
         if (hipMemcpyAsync(h, enc->stats, sizeof(h), hipMemcpyDeviceToHost,
                            s) != hipSuccess)
@@ -225,6 +233,9 @@ smh_status smh_mask_stats_get(const smh_mask_enc *enc, smh_mask_stats *out,
         out->max_row_tiles = (int32_t)h[4];
         out->mask_b = enc->mask_b;
         out->mask_h = enc->mask_h;
+        out->n_sparse = (int32_t)h[5];
+        out->sparse_nnz = h[6];
+        out->row_entries = h[7];
         return SMH_OK;
     } catch (...) {
         return SMH_EHIP;
@@ -265,7 +276,8 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
         if (in_dt != SMH_F16 && in_dt != SMH_BF16) return SMH_EUNSUPPORTED;
         if (out_dt != in_dt && out_dt != SMH_F32) return SMH_EUNSUPPORTED;
         if (!isfinite(scale) || scale < 0.f) return SMH_EINVAL;
-        if (which != SMH_AUTO && which != SMH_ROWWISE && which != SMH_BLOCKWISE)
+        if (which != SMH_AUTO && which != SMH_ROWWISE && which != SMH_BLOCKWISE &&
+            which != SMH_BLOCKWISE_DENSE)
             return SMH_EINVAL;
         const int64_t BH = (int64_t)B * H;
         if (BH > 0 && !broadcasts(enc->mask_b, enc->mask_h, B, H)) return SMH_EINVAL;
@@ -288,7 +300,7 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
             return SMH_EINVAL;
         if (!enc->full_row_ptr || !enc->full_col_idx || !enc->part_row_ptr ||
             !enc->part_col_idx || !enc->part_bitmaps || !enc->row_order ||
-            !enc->row_info)
+            !enc->row_info || !enc->part_pop || !enc->row_ent || !enc->row_ent_cnt)
             return SMH_EINVAL;
         const size_t in_b = n_el * 2;
         const size_t out_b = n_el * (out_dt == SMH_F32 ? 4 : 2);
@@ -309,7 +321,7 @@ smh_status smh_sparse_mha_fwd(const void *q, const void *k, const void *v,
                                    *enc, hs);
             else
                 e = launch_blockwise(q, k, v, o, B, H, S, d, in_dt, out_dt, sc,
-                                     *enc, hs);
+                                     *enc, which != SMH_BLOCKWISE_DENSE, hs);
         }
         return e == hipSuccess ? SMH_OK : SMH_EHIP;
     } catch (...) {

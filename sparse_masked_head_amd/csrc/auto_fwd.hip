@@ -15,6 +15,7 @@ template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TOut> a) {
     __shared__ __attribute__((aligned(16))) char k0[Lds<D>::KBUF], k1[Lds<D>::KBUF];
     __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
+    __shared__ HybLds hl;
     const int oi = blockIdx.x / a.U;
     const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
     // the block-wise path's Q rows, requested before the row summary so that
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TO
     const RowInfo ri = load_row_info(a, sl.row);
     if (device_choice<D>(a, ri) == 2) {
         const TileBufs<D> bufs{{k0, k1}, {v0, v1}};
-        blockwise_row<D, TIn, TOut>(a, bufs, sl.I, sl.bh, ri, qf);
+        blockwise_row<D, TIn, TOut>(a, bufs, sl.row, sl.I, sl.bh, ri, qf, hl);
     } else {
         // each wavefront's slice is one of the tile buffers
         const int w = threadIdx.x >> 6;
@@ -44,6 +45,7 @@ hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
     static_assert(RowLds<D>::BYTES <= Lds<D>::KBUF, "LDS slices");
     auto kern = auto_fwd<D, TIn, TOut>;
     FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, B, H, S, scale, enc);
+    a.hybrid = hybrid_allowed(S, enc.n_ot);
     const long long slots = (long long)a.R * a.U;  // = n * B * H
     a.use_order = slots > resident_workgroups(kern, 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(256), 0, stream, a);

@@ -279,17 +279,20 @@ template <int D> __device__ inline VOff<D> v_offsets(int lq, int g) {
     return o;
 }
 
-// Softmax of one tile's scores (masked ones already -inf) and
-// O^T += V^T P^T.  c = scale * log2(e) > 0.
-template <int D, typename TIn>
+// Softmax of the scores of NST 16-key sub-tiles (masked ones already -inf;
+// NST = 4 for an outer tile, 2 for a gathered chunk of 32 keys) and
+// O^T += V^T P^T with V's rows in a tile-buffer layout.  c = scale *
+// log2(e) > 0.  kWaitV: wait for this wave's outstanding loads (the V rows
+// it staged itself) before the first V read.
+template <int D, typename TIn, int NST = 4, bool kWaitV = false>
 __device__ __attribute__((always_inline)) inline void softmax_pv(
-    RowState<D> &rs, f4_t (&sc)[4], const char *vb, float c, const VOff<D> &vo) {
+    RowState<D> &rs, f4_t (&sc)[NST], const char *vb, float c, const VOff<D> &vo) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     using L = Lds<D>;
     float mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < NST; ++st) {
         mx = fmaxf(fmaxf(mx, sc[st][0]), sc[st][1]);
         mx = fmaxf(fmaxf(mx, sc[st][2]), sc[st][3]);
     }
@@ -312,16 +315,17 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
     const float mc = rs.mc;
 
     // P^T as B operand: keys 32u + 4g + j (j < 4), 32u + 16 + 4g + j - 4
-    frag pf[2];
+    constexpr int NU = NST / 2;
+    frag pf[NU];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             pf[st >> 1][(st & 1) * 4 + i] =
                 (TIn)__builtin_amdgcn_exp2f(fmaf(sc[st][i], c, -mc));
     float lsum = rs.l;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
         uint32_t pw[4];
         __builtin_memcpy(pw, &pf[u], 16);
 #pragma unroll
@@ -335,10 +339,11 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
     // and lane i receives V[key0 .. key0+3][d0 + i]; key0 = 32u + 4g for
     // slots 0..3 and 32u + 16 + 4g for slots 4..7.  vo holds the lane's
     // (q, a) offsets in the swizzled buffer.
+    if (kWaitV) wait_loads();
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NU; ++u) {
             const char *p0 = vb + vo.x[dt] + 32 * u * L::CPR * 16;
             const char *p1 = p0 + 16 * L::CPR * 16;
             const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -359,22 +364,95 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
 // of the first four tiles come with the row summary; the tile loop reads
 // each later column one step before it needs it (a column read in the step
 // that uses it would put a memory round trip in front of every tile load).
+// With `dl` set (a row split by split_partials), the partial tiles the
+// loop visits are the dense ones of the LDS list instead of the row's
+// whole partial list.
 struct TileList {
     const int32_t *fci, *pci;
     const uint64_t *bm;
+    const uint32_t *dl;  // LDS: column << 16 | index in the row's partial list
     int f0, nF, p0, nT, nmax, S;
     __device__ int clamp(int J) const { return (int)min((unsigned)J, (unsigned)nmax); }
-    __device__ const int32_t *col_ptr(int idx) const {
-        return idx < nF ? fci + f0 + idx : pci + p0 + idx - nF;
+    // column of stored tile idx (full tiles first); a load from memory
+    // (or LDS) that the caller issues a step before it needs the value
+    __device__ int col_of(int idx) const {
+        if (idx < nF) return fci[f0 + idx];
+        return dl ? (int)(dl[idx - nF] >> 16) : pci[p0 + idx - nF];
     }
     // last in-bounds 16-byte chunk offset (bytes) of tile J (S cuts the last tile)
     template <int D> __device__ uint32_t lim(int J) const {
         return 2u * (uint32_t)(min(64, S - 64 * J) * D - 8);
     }
     __device__ const uint64_t *words(int idx) const {
-        return idx < nF ? nullptr : bm + (size_t)(p0 + idx - nF) * 64;
+        if (idx < nF) return nullptr;
+        const int k = dl ? (int)(dl[idx - nF] & 0xFFFFu) : idx - nF;
+        return bm + (size_t)(p0 + k) * 64;
     }
 };
+
+// Most outer tiles per side for which the block-wise algorithm splits rows
+// into dense and sparse partial tiles (S <= 65536: keys fit 16 bits).
+constexpr int kHybMaxN = 1024;
+
+// LDS of the split: the row's partial tiles, dense ones first, each
+// column << 16 | index in the row's partial list, and per-wavefront counts.
+struct HybLds {
+    uint32_t list[kHybMaxN];
+    int wcnt[16];
+};
+
+// The split of an outer-tile row's partial tiles (whole workgroup, two
+// barriers): list[0 .. nD) the dense ones (more than SMH_SPARSE_TILE_MAX
+// valid elements), list[nD .. nP) the sparse ones, each in ascending column
+// order.  Returns nD.  Requires nP <= kHybMaxN.
+template <typename TIn, typename TOut>
+__device__ inline int split_partials(const FwdArgs<TIn, TOut> &a, const RowInfo &ri,
+                                     HybLds &hl) {
+    constexpr int kPer = kHybMaxN / 256;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int nP = ri.nP, nk = (nP + 255) >> 8;
+    int popv[kPer], colv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {  // every load in flight at once
+        const int idx = 256 * k + t;
+        const bool v = k < nk && idx < nP;
+        popv[k] = v ? a.pop[ri.p0 + idx] : SMH_SPARSE_TILE_MAX + 1;
+        colv[k] = v ? a.pci[ri.p0 + idx] : 0;
+    }
+    uint64_t dmask[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const bool dense = 256 * k + t < nP && popv[k] > SMH_SPARSE_TILE_MAX;
+        dmask[k] = __builtin_amdgcn_ballot_w64(dense);
+        if (lane == 0) hl.wcnt[4 * k + w] = __popcll(dmask[k]);
+    }
+    __syncthreads();
+    int nD = 0, before[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        before[k] = nD;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int x = hl.wcnt[4 * k + q];
+            before[k] += q < w ? x : 0;
+            nD += x;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int idx = 256 * k + t;
+        if (idx < nP) {
+            const int drank = before[k] +
+                (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(dmask[k] >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)dmask[k], 0u));
+            const bool dense = (dmask[k] >> lane) & 1ull;
+            const int at = dense ? drank : nD + idx - drank;
+            hl.list[at] = ((uint32_t)colv[k] << 16) | (uint32_t)idx;
+        }
+    }
+    __syncthreads();
+    return nD;
+}
 
 // Workgroup work: encoding row `row` (outer-tile row I of its mask, summary
 // ri) of head bh.
@@ -404,10 +482,127 @@ __device__ __attribute__((always_inline)) inline void load_q_frags(
         qf[s] = *reinterpret_cast<const frag *>(qrow + 32 * s + 8 * (l >> 4));
 }
 
+// ---- gather path of sparse partial tiles (per wavefront, no barrier) ----
+//
+// The row-wise side of the per-tile dispatch: a partial tile with few valid
+// elements would cost a dense tile's work on the matrix cores, so each
+// wavefront instead streams the row-wise entries of its 16 query rows (the
+// keys some of them see in the row's sparse tiles, with their row sets;
+// built once per mask by the encoder) and computes them in chunks of 32
+// keys with the same MFMA layout and online-softmax state as the tile path.
+// Pipeline, at chunk c: the entries of chunk c + 2 are requested (one
+// register: lane l holds entry l % 32); chunk c + 1's K rows go into one of
+// two register sets and its V rows (global_load_lds) into one of two V
+// slots, chunk-swizzled like a tile buffer so that the tile path's V^T
+// reads serve, its keys and row sets taken from its entry register with
+// ds_bpermute; then chunk c is computed.  The V slots of chunks c and c + 1
+// lie in different LDS objects (the K tile buffers, the V tile buffers),
+// so the V^T reads of one do not wait for the loads landing in the other.
+// Loads past the list re-read its last entry (or key 0), so every wait
+// counts the same loads.
+
+// One chunk in registers: K rows as A operands (entries 16st + lq, st =
+// 0, 1; d = 32s + 8g .. +7) and the lane's score slots that are valid (bit
+// 4st + i: entry 16st + 4g + i is in the chunk and its row set holds the
+// lane's query row).
+template <int D, typename TIn> struct ChunkK {
+    typename Frag<TIn>::type k[2][D / 32];
+    uint32_t ok;
+};
+
+template <int D, typename TIn>
+__device__ __attribute__((always_inline)) inline void gather_stream(
+    RowState<D> &rs, char *vslot0, char *vslot1, const uint32_t *__restrict__ ents,
+    int ne, const typename Frag<TIn>::type (&qf)[D / 32], const TIn *__restrict__ Kh,
+    const TIn *__restrict__ Vh, float c, int S, const VOff<D> &vo) {
+    using F = Frag<TIn>;
+    using L = Lds<D>;
+    const int lane = threadIdx.x & 63, lq = lane & 15, g = lane >> 4;
+    constexpr int RPI = 1024 / (2 * D);  // V rows per 1 KB load instruction
+    constexpr int NV = 32 / RPI;         // V instructions per chunk
+    constexpr int NK = 2 * (D / 32);     // K loads per chunk
+    const int nch = (ne + 31) >> 5;
+    // the key of entry ei of a chunk of n entries, clamped into the head's
+    // rows; past the chunk: key 0
+    auto key_of = [&](int ei, int n, uint32_t e) __attribute__((always_inline)) {
+        return ei < n ? min((int)(e & 0xFFFFu), S - 1) : 0;
+    };
+    auto load_e = [&](int ci) __attribute__((always_inline)) {
+        return ents[min(32 * ci + (lane & 31), ne - 1)];
+    };
+    auto issue = [&](int ci, uint32_t e, char *vs, ChunkK<D, TIn> &ck)
+        __attribute__((always_inline)) {
+        // entry idx of the chunk, from lane idx of the entry register
+        auto ent = [&](int idx) __attribute__((always_inline)) {
+            return (uint32_t)__builtin_amdgcn_ds_bpermute(idx << 2, (int)e);
+        };
+        const int n = min(32, ne - 32 * ci);
+        uint32_t ok = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int rr = RPI * i + lane / L::CPR, cp = lane % L::CPR;
+            const int key = key_of(rr, n, ent(rr));
+            __builtin_amdgcn_global_load_lds(
+                (gbl_void_t *)(Vh + (size_t)key * D + 8 * (cp ^ L::sw(rr))),
+                (lds_void_t *)(vs + 1024 * i), 16, 0, 0);
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const typename F::type *krow = reinterpret_cast<const typename F::type *>(
+                Kh + (size_t)key_of(16 * st + lq, n, ent(16 * st + lq)) * D);
+#pragma unroll
+            for (int s2 = 0; s2 < D / 32; ++s2) ck.k[st][s2] = krow[4 * s2 + g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t e2 = ent(16 * st + 4 * g + i);
+                ok |= (uint32_t)(16 * st + 4 * g + i < n && ((e2 >> (16 + lq)) & 1u))
+                      << (4 * st + i);
+            }
+        }
+        ck.ok = ok;
+    };
+    auto compute = [&](const char *vs, const ChunkK<D, TIn> &ck)
+        __attribute__((always_inline)) {
+        f4_t sc[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            f4_t c0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c0[i] = (ck.ok >> (4 * st + i)) & 1u ? 0.f : -INFINITY;
+            sc[st] = F::mfma(ck.k[st][0], qf[0], c0);
+#pragma unroll
+            for (int s2 = 1; s2 < D / 32; ++s2) sc[st] = F::mfma(ck.k[st][s2], qf[s2], sc[st]);
+        }
+        softmax_pv<D, TIn, 2>(rs, sc, vs, c, vo);
+    };
+    if (nch == 0) return;
+    ChunkK<D, TIn> ka, kb;
+    uint32_t ea = load_e(0), eb = load_e(1);
+    issue(0, ea, vslot0, ka);
+    // chunk ci: registers `cur`, V slot vc; chunk ci + 1: entries in `en`,
+    // goes to `nxt` and vn; the entries of ci + 2 replace those of ci in
+    // `ef`.  Loads issued after chunk ci's: the entries of ci + 2 (one) and
+    // chunk ci + 1's (NV + NK).
+    auto iter = [&](int ci, uint32_t &ef, const uint32_t en, char *vc, char *vn,
+                    ChunkK<D, TIn> &cur, ChunkK<D, TIn> &nxt) __attribute__((always_inline)) {
+        ef = load_e(ci + 2);
+        issue(ci + 1, en, vn, nxt);
+        wait_loads_but<NV + NK + 1>();
+        asm volatile("" ::: "memory");
+        compute(vc, cur);
+    };
+    for (int ci = 0; ci < nch; ci += 2) {
+        iter(ci, ea, eb, vslot0, vslot1, ka, kb);
+        if (ci + 1 >= nch) break;
+        iter(ci + 1, eb, ea, vslot1, vslot0, kb, ka);
+    }
+    wait_loads();  // the loads past the list land before the slots are left
+}
+
 template <int D, typename TIn, typename TOut>
 __device__ __attribute__((always_inline)) inline void blockwise_row(
-    const FwdArgs<TIn, TOut> &a, const TileBufs<D> &bufs, int I, int bh,
-    const RowInfo &ri, const typename Frag<TIn>::type (&qf)[D / 32]) {
+    const FwdArgs<TIn, TOut> &a, const TileBufs<D> &bufs, int row, int I, int bh,
+    const RowInfo &ri, const typename Frag<TIn>::type (&qf)[D / 32], HybLds &hl) {
     using frag = typename Frag<TIn>::type;
     using L = Lds<D>;
     const size_t head = (size_t)bh * a.S * D;
@@ -426,8 +621,23 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     tl.f0 = ri.f0;
     tl.nF = ri.nF;
     tl.p0 = ri.p0;
-    tl.nT = ri.nF + ri.nP;
+    tl.dl = nullptr;
+    // per-tile dispatch: with sparse partial tiles in the encoding, the row's
+    // partial tiles are split; the dense ones stay on the tile path below,
+    // the sparse ones go to the gather path after it
+    const bool hyb = a.hybrid && ri.stats[5] > 0 && ri.nP > 0;
+    int nD = ri.nP;
+    if (hyb) {
+        nD = split_partials(a, ri, hl);
+        tl.dl = hl.list;
+    }
+    tl.nT = ri.nF + nD;
     const int nT = tl.nT, nF = tl.nF;
+    // columns of the first four tiles the tile path visits (-1 past them)
+    int cc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        cc[k] = !hyb || k < nF ? ri.c[k] : k < nT ? (int)(hl.list[k - nF] >> 16) : -1;
 
     const int qi = 64 * I + r;
 
@@ -482,9 +692,9 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
         // summary and go unused), so the loads are one fixed sequence and a
         // constant count waits for exactly those of tiles 0 and 1.  Tiles
         // go through the softmax in the loop's order (same results).
-        const int c0 = tl.clamp(ri.c[0]);
-        const int c1 = nT > 1 ? tl.clamp(ri.c[1]) : c0;
-        const int c2 = nT > 2 ? tl.clamp(ri.c[2]) : c0;
+        const int c0 = tl.clamp(cc[0]);
+        const int c1 = nT > 1 ? tl.clamp(cc[1]) : c0;
+        const int c2 = nT > 2 ? tl.clamp(cc[2]) : c0;
         const uint8_t *any_src = reinterpret_cast<const uint8_t *>(a.info);
         auto mask_src = [&](int idx) __attribute__((always_inline)) {
             return idx < nT && idx >= nF
@@ -528,10 +738,10 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     } else {
         // columns of the K tile (jk, tile it+2) and V tile (jv, tile it+1) that
         // tile step it loads
-        int jv = tl.clamp(ri.c[1]), jk = tl.clamp(ri.c[2]);
+        int jv = tl.clamp(cc[1]), jk = tl.clamp(cc[2]);
         if (nT > 0) {
-            load_k(bufs.k[0], mk0, 0, tl.clamp(ri.c[0]));
-            load_v(bufs.v[0], tl.clamp(ri.c[0]));
+            load_k(bufs.k[0], mk0, 0, tl.clamp(cc[0]));
+            load_v(bufs.v[0], tl.clamp(cc[0]));
             if (nT > 1) load_k(bufs.k[1], mk1, 1, jv);
         }
         wait_loads();
@@ -550,8 +760,8 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
             constexpr int cb = decltype(cbc)::value, nb = cb ^ 1;
             // column of tile it+3 (tile step it+1 loads its K); from memory past
             // the four of the row summary
-            int jn_raw = ri.c[3];
-            if (it + 3 < nT && it + 3 >= 4) jn_raw = *tl.col_ptr(it + 3);
+            int jn_raw = cc[3];
+            if (it + 3 < nT && it + 3 >= 4) jn_raw = tl.col_of(it + 3);
             // K(it+2) replaces K(it) (read in the previous step); V(it+1)
             // replaces V(it-1) (read in the previous step)
             if (it + 2 < nT) load_k(bufs.k[cb], mk0, it + 2, jk);
@@ -571,6 +781,19 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
             step(it + 1, std::integral_constant<int, 1>(), s_b, s_a, m_b, m_a);
         }
 
+    }
+
+    if (hyb && nD < ri.nP) {
+        // every wave is done with the tile buffers; each takes one as its
+        // slice for the gather path, over its group's row-wise entries
+        if (nT > 0) __syncthreads();
+        // V slot 0 of waves 0-3 in the K buffers, slot 1 in the V buffers
+        constexpr int VSL = 32 * D * 2;
+        char *vs0 = (w < 2 ? bufs.k[0] : bufs.k[1]) + VSL * (w & 1);
+        char *vs1 = (w < 2 ? bufs.v[0] : bufs.v[1]) + VSL * (w & 1);
+        const uint32_t *ents = a.rent + 256 * (size_t)ri.p0 + 64 * (size_t)w * ri.nP;
+        const int ne = a.rcnt[4 * (size_t)row + w];
+        gather_stream<D, TIn>(rs, vs0, vs1, ents, ne, qf, Kh, Vh, a.c, a.S, vo);
     }
 
     // epilogue: total l over the 4 lanes of this query

@@ -30,6 +30,7 @@
 #include <math.h>
 #include <mutex>
 
+#include "bits.h"
 #include "smh_internal.h"
 
 namespace smh {
@@ -137,11 +138,78 @@ constexpr int kFusedRows = 1024, kFusedBins = 0;
 constexpr int kFusedMaxSegs = 2048;
 
 struct Seg {  // per-segment scratch (EncLayout)
-    uint64_t *cnt, *off, *nnz, *any;
-    int32_t *fcol, *pcol;
+    uint64_t *cnt, *off, *nnz, *any, *sp;
+    int32_t *fcol, *pcol, *pop;
     uint64_t *words;
+    int32_t *ecnt;  // [segment][group]: row-wise entries of its sparse tiles
+    uint32_t *ent;  // [segment][group][64 * cap], or null: no row-wise format
     int cap;  // tiles of room per segment
 };
+
+// Sparse partial tiles (count << kSpShift | valid pairs) of a segment or a
+// sum of segments: the pairs stay below 2^40 and the count below 2^24.
+constexpr int kSpShift = 40;
+constexpr uint64_t kSpLow = (1ull << kSpShift) - 1;
+
+// The row-wise entries of the segment's sparse tiles (tkind bit 18), per
+// group q of 16 query rows (inner-tile rows 2q, 2q + 1): for each key that
+// some row of the group sees, rows << 16 | key, in key order (tiles in
+// column order, then inner-tile column, then column in it).  Lane (ir, ic)
+// of the wavefront holding a tile owns word (ir, ic); the lanes of even ir
+// gather their column block's keys for group ir / 2 from their word and
+// the word below it.  Three passes: entries per (tile, group); their prefix
+// over the segment's tiles (wavefront q, lane = tile); the entries, at the
+// segment's scratch for group q.
+__device__ void strip_entries(int s, int nwin, int w0, Seg sg,
+                              uint64_t (*lw)[64], const int *tkind) {
+    __shared__ int ecnt_t[kMaxSegTiles][4];
+    __shared__ int eoff_t[kMaxSegTiles][4];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int ir = lane >> 3, ic = lane & 7, q = ir >> 1;
+    const bool top = (ir & 1) == 0;
+    const int ntile = kWin * nwin;
+    for (int l = w; l < kMaxSegTiles; l += 4) {
+        int c = 0;
+        if (l < ntile && (tkind[l] & (1 << 18)) && top)
+            c = __popc(live_columns(lw[l][lane] | lw[l][lane + 8]));
+        c += __shfl_xor(c, 1);
+        c += __shfl_xor(c, 2);
+        c += __shfl_xor(c, 4);
+        if (ic == 0 && top) ecnt_t[l][q] = c;
+    }
+    __syncthreads();
+    {
+        const int v = ecnt_t[lane][w];  // wavefront w: group w, lane: tile
+        int incl = v;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        eoff_t[lane][w] = incl - v;
+        if (lane == 63) sg.ecnt[4 * (size_t)s + w] = incl;
+    }
+    __syncthreads();
+    for (int l = w; l < ntile; l += 4) {
+        if (!(tkind[l] & (1 << 18))) continue;  // (uniform in the wavefront)
+        const uint64_t lo = lw[l][lane], hi = lw[l][(lane + 8) & 63];
+        uint32_t live = top ? live_columns(lo | hi) : 0u;
+        const int cnt = __popc(live);
+        int incl = cnt;  // prefix over the 8 lanes of this inner-tile row
+        for (int d = 1; d < 8; d <<= 1) {
+            const int y = __shfl_up(incl, d, 8);
+            if (ic >= d) incl += y;
+        }
+        int pos = eoff_t[l][q] + incl - cnt;
+        const uint32_t key0 = 64u * (uint32_t)(kWin * (w0 + (l >> 3)) + (l & 7)) + 8u * ic;
+        uint32_t *dst = sg.ent + (4 * (size_t)s + q) * (64 * (size_t)sg.cap);
+        while (live) {
+            const int cb = __builtin_ctz(live);
+            live &= live - 1;
+            const uint32_t rows = column_rows(lo, cb) | (column_rows(hi, cb) << 8);
+            dst[pos++] = (rows << 16) | (key0 + (uint32_t)cb);
+        }
+    }
+}
 
 // Shared tail of the strip passes: classify the segment's tiles (wavefront
 // 0, lane = tile), write its columns, counts, valid pairs and covered rows
@@ -151,6 +219,7 @@ struct Seg {  // per-segment scratch (EncLayout)
 __device__ void strip_classify(int s, int nwin, int w0, int n, Seg sg,
                                uint64_t (*lw)[64], int (*wsum)[4], int *tkind,
                                uint64_t any64) {
+    __shared__ int seg_sparse;  // the segment has a sparse partial tile
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     if (w == 0) {
         const int wi = lane >> 3, J = kWin * (w0 + wi) + (lane & 7);
@@ -162,15 +231,27 @@ __device__ void strip_classify(int s, int nwin, int w0, int n, Seg sg,
         const uint64_t mf = __ballot(full), mp = __ballot(part);
         const uint64_t below = (1ull << lane) - 1;
         const int rf = __popcll(mf & below), rp = __popcll(mp & below);
-        tkind[lane] = full ? (1 << 17) | rf : part ? (1 << 16) | rp : 0;
+        tkind[lane] = full ? (1 << 17) | rf
+                    : part ? (1 << 16) | rp | (cnt <= SMH_SPARSE_TILE_MAX ? 1 << 18 : 0)
+                           : 0;
         if (full) sg.fcol[(size_t)s * sg.cap + rf] = J;
-        if (part) sg.pcol[(size_t)s * sg.cap + rp] = J;
-        long long nz = cnt;
-        for (int off = 32; off > 0; off >>= 1) nz += __shfl_xor(nz, off);
+        if (part) {
+            sg.pcol[(size_t)s * sg.cap + rp] = J;
+            sg.pop[(size_t)s * sg.cap + rp] = cnt;
+        }
+        const bool sparse = part && cnt <= SMH_SPARSE_TILE_MAX;
+        long long nz = cnt, spz = sparse ? cnt : 0;
+        for (int off = 32; off > 0; off >>= 1) {
+            nz += __shfl_xor(nz, off);
+            spz += __shfl_xor(spz, off);
+        }
+        const uint64_t ms = __ballot(sparse);
         if (lane == 0) {
+            seg_sparse = ms != 0;
             sg.cnt[s] = ((uint64_t)__popcll(mf) << 32) | (uint64_t)__popcll(mp);
             sg.nnz[s] = (uint64_t)nz;
             sg.any[s] = any64;
+            sg.sp[s] = ((uint64_t)__popcll(ms) << kSpShift) | (uint64_t)spz;
         }
     }
     __syncthreads();
@@ -178,6 +259,12 @@ __device__ void strip_classify(int s, int nwin, int w0, int n, Seg sg,
         const int k = tkind[l];
         if (k & (1 << 16))
             sg.words[((size_t)s * sg.cap + (k & 0xFFFF)) * 64 + lane] = lw[l][lane];
+    }
+    if (sg.ent) {
+        if (seg_sparse)
+            strip_entries(s, nwin, w0, sg, lw, tkind);
+        else if (t < 4)
+            sg.ecnt[4 * (size_t)s + t] = 0;
     }
 }
 
@@ -418,7 +505,7 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     const int rows_per = (R + 255) / 256;
     const int r_lo = min(R, t * rows_per), r_hi = min(R, r_lo + rows_per);
     unsigned long long own = 0;
-    long long nnz = 0, empty = 0;
+    long long nnz = 0, empty = 0, spw = 0, ents = 0;
     int mx = 0;
     for (int I = r_lo; I < r_hi; ++I) {
         unsigned long long rc = 0;
@@ -428,6 +515,11 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
             rc += sg.cnt[I * C + c];
             nnz += (long long)sg.nnz[I * C + c];
             an |= sg.any[I * C + c];
+            spw += (long long)sg.sp[I * C + c];
+            if (sg.ent) {
+                const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[I * C + c];
+                ents += (long long)e.x + e.y + e.z + e.w;
+            }
         }
         const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull);
         rowc[I] = ((uint32_t)f << 16) | (uint32_t)p;
@@ -466,7 +558,11 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     }
     nnz = block_sum(nnz, sh_l);
     empty = block_sum(empty, sh_l);
+    spw = block_sum(spw, sh_l);
+    ents = block_sum(ents, sh_l);
     mx = block_max(mx, sh_i);
+    const int nsp = (int)((uint64_t)spw >> kSpShift);
+    const long long spnz = (long long)((uint64_t)spw & kSpLow);
     auto cnt_of = [&](int J) { return (int)((rowc[J] >> 16) + (rowc[J] & 0xFFFFu)); };
     if constexpr (kBins == 0) {  // (every row's count is in LDS: barriers above)
         for (int J = t; J < R; J += 256) {
@@ -511,6 +607,9 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
         // rows past S do not exist
         enc.stats[3] = empty - (long long)G * (64LL * n - S);
         enc.stats[4] = mx;
+        enc.stats[5] = nsp;
+        enc.stats[6] = spnz;
+        enc.stats[7] = ents;
     }
     // the statistics the kernel choice reads, in every row's summary (one
     // load per workgroup instead of a line that every workgroup waits on);
@@ -520,7 +619,8 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
         ri[0] = make_int4((int)(uint32_t)((unsigned long long)nnz & 0xFFFFFFFFull),
                           (int)(nnz >> 32), (int)(sh_tot >> 32),
                           (int)(sh_tot & 0xFFFFFFFFull));
-        ri[1] = make_int4(mx, 0, 0, 0);
+        ri[1] = make_int4(mx, nsp, (int)(uint32_t)((uint64_t)ents & 0xFFFFFFFFull),
+                          (int)(ents >> 32));
     }
 }
 
@@ -532,7 +632,7 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
     const int lane = threadIdx.x & 63;
     const int C = plan.per_row;
     unsigned long long rc = 0;
-    long long nnz = 0;
+    long long nnz = 0, spw = 0, ents = 0;
     uint64_t an = 0;
     if (lane < R) {
 #pragma unroll 8
@@ -540,6 +640,11 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
             rc += sg.cnt[lane * C + c];
             nnz += (long long)sg.nnz[lane * C + c];
             an |= sg.any[lane * C + c];
+            spw += (long long)sg.sp[lane * C + c];
+            if (sg.ent) {
+                const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[lane * C + c];
+                ents += (long long)e.x + e.y + e.z + e.w;
+            }
         }
     }
     const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull), cnt = f + p;
@@ -554,8 +659,12 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
     for (int o = 32; o > 0; o >>= 1) {
         nz += __shfl_xor(nz, o);
         empty += __shfl_xor(empty, o);
+        spw += __shfl_xor(spw, o);
+        ents += __shfl_xor(ents, o);
         mx = max(mx, __shfl_xor(mx, o));
     }
+    const int nsp = (int)((uint64_t)spw >> kSpShift);
+    const long long spnz = (long long)((uint64_t)spw & kSpLow);
     // schedule rank: rows with more stored tiles, then rows before with as many
     int rank = 0;
     for (int J2 = 0; J2 < R; ++J2) {  // (a scalar read of lane J2 per row)
@@ -570,7 +679,8 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
         for (int k = cnt; k < 4; ++k) enc.row_info[16 * (size_t)lane + 4 + k] = -1;
         ri[2] = make_int4((int)(uint32_t)((unsigned long long)nz & 0xFFFFFFFFull),
                           (int)(nz >> 32), (int)(tot >> 32), (int)(tot & 0xFFFFFFFFull));
-        ri[3] = make_int4(mx, 0, 0, 0);
+        ri[3] = make_int4(mx, nsp, (int)(uint32_t)((uint64_t)ents & 0xFFFFFFFFull),
+                          (int)(ents >> 32));
         enc.row_order[rank] = lane;
     }
     if (lane == 0) {
@@ -581,6 +691,9 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
         enc.stats[2] = (int64_t)(tot & 0xFFFFFFFFull);
         enc.stats[3] = empty - (long long)G * (64LL * n - S);  // rows past S do not exist
         enc.stats[4] = mx;
+        enc.stats[5] = nsp;
+        enc.stats[6] = spnz;
+        enc.stats[7] = ents;
     }
 }
 
@@ -600,6 +713,7 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
                                                  SegPlan plan, Seg sg,
                                                  smh_mask_enc enc) {
     __shared__ unsigned long long sh_u[4];
+    __shared__ size_t ent_dst[4];  // where the segment's entries of group g go
     const int t = threadIdx.x, s = blockIdx.x;
     if constexpr (kSelf) {
         if (s == plan.total) {
@@ -619,9 +733,16 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
     // can go to its row_info
     const int row = s / plan.per_row, s0 = row * plan.per_row;
     const uint64_t rcnt = t < plan.per_row ? sg.cnt[s0 + t] : 0;
+    // row-wise entries of the row's segments per group (lane = segment)
+    const int4 recnt = sg.ent && t < plan.per_row
+                           ? reinterpret_cast<const int4 *>(sg.ecnt)[s0 + t]
+                           : make_int4(0, 0, 0, 0);
     // columns (t < cap) and the first 256 16-byte chunks of the words
     const int colf = t < sg.cap ? sg.fcol[base + t] : 0;
     const int colp = t < sg.cap ? sg.pcol[base + t] : 0;
+    const int popp = t < sg.cap ? sg.pop[base + t] : 0;
+    const int4 ecs = sg.ent ? reinterpret_cast<const int4 *>(sg.ecnt)[s] : make_int4(0, 0, 0, 0);
+    const bool has_ent = (ecs.x | ecs.y | ecs.z | ecs.w) != 0;
     const u4v *src = reinterpret_cast<const u4v *>(sg.words + base * 64);
     const u4v w0 = t < sg.cap * 32 ? src[t] : u4v{0, 0, 0, 0};
     unsigned long long off;
@@ -644,6 +765,38 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
             bp += __shfl_xor(bp, o);
             rf += __shfl_xor(rf, o);
         }
+        if (sg.ent) {
+            // the segment's entries go after those of the row's earlier
+            // segments, in the row's region of group q; the row's first
+            // segment writes the row's counts
+            int rp = (int)(rcnt & 0xFFFFFFFFull);  // the row's partial tiles
+            int e[4] = {recnt.x, recnt.y, recnt.z, recnt.w}, be[4], re[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                be[g] = before ? e[g] : 0;
+                re[g] = e[g];
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                rp += __shfl_xor(rp, o);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    be[g] += __shfl_xor(be[g], o);
+                    re[g] += __shfl_xor(re[g], o);
+                }
+            }
+            if (t < 4) {
+                const size_t p0 = (size_t)(pp - bp);
+                if (has_ent)
+                    ent_dst[t] = 256 * p0 + 64 * (size_t)t * rp +
+                                 (size_t)(t == 0 ? be[0] : t == 1 ? be[1] : t == 2 ? be[2] : be[3]);
+                if (s == s0)
+                    enc.row_ent_cnt[4 * (size_t)row + t] =
+                        t == 0 ? re[0] : t == 1 ? re[1] : t == 2 ? re[2] : re[3];
+            }
+        }
+        else if (s == s0 && t < 4) {
+            enc.row_ent_cnt[4 * (size_t)row + t] = 0;  // no row-wise format
+        }
         int32_t *ri = enc.row_info + 16 * (size_t)row + 4;
         if (t < nf) {
             enc.full_col_idx[pf + t] = colf;
@@ -651,12 +804,23 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
         }
         if (t < np) {
             enc.part_col_idx[pp + t] = colp;
+            enc.part_pop[pp + t] = popp;
             if (rf + bp + t < 4) ri[rf + bp + t] = colp;
         }
     }
     u4v *dst = reinterpret_cast<u4v *>(enc.part_bitmaps + (size_t)pp * 64);
     if (t < np * 32) dst[t] = w0;
     for (int e = t + 256; e < np * 32; e += 256) dst[e] = src[e];
+    if (has_ent) {
+        __syncthreads();  // ent_dst from wavefront 0
+        const int cnts[4] = {ecs.x, ecs.y, ecs.z, ecs.w};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t *es = sg.ent + (4 * (size_t)s + g) * (64 * (size_t)sg.cap);
+            uint32_t *ed = enc.row_ent + ent_dst[g];
+            for (int i = t; i < cnts[g]; i += 256) ed[i] = es[i];
+        }
+    }
 }
 
 // S == 0: an empty encoding.  Row pointers {0}, all statistics zero.
@@ -665,7 +829,7 @@ __global__ void enc_empty(smh_mask_enc enc) {
         enc.full_row_ptr[0] = 0;
         enc.part_row_ptr[0] = 0;
     }
-    if (threadIdx.x < 5) enc.stats[threadIdx.x] = 0;
+    if (threadIdx.x < 8) enc.stats[threadIdx.x] = 0;
 }
 
 }  // namespace
@@ -694,8 +858,12 @@ hipError_t encode_launches(StripLaunch strip, int32_t S, const EncLayout &L,
     sg.off = (uint64_t *)(sc + L.seg_off);
     sg.nnz = (uint64_t *)(sc + L.seg_nnz);
     sg.any = (uint64_t *)(sc + L.seg_any);
+    sg.sp = (uint64_t *)(sc + L.seg_sp);
     sg.fcol = (int32_t *)(sc + L.seg_fcol);
     sg.pcol = (int32_t *)(sc + L.seg_pcol);
+    sg.pop = (int32_t *)(sc + L.seg_pop);
+    sg.ecnt = (int32_t *)(sc + L.seg_ecnt);
+    sg.ent = L.rowfmt ? (uint32_t *)(sc + L.seg_ent) : nullptr;
     sg.words = (uint64_t *)(sc + L.seg_words);
     sg.cap = (int)L.seg_cap;
     strip(n, plan, sg);

@@ -3,6 +3,7 @@
 
 #include <atomic>
 
+#include "bits.h"
 #include "select_model.h"
 #include "smh_internal.h"
 
@@ -54,6 +55,13 @@ template <typename TIn, typename TOut> struct FwdArgs {
     const int32_t *row_order;
     const int32_t *info;  // row_info [R][16]
     const int64_t *stats;
+    const int32_t *pop;   // part_pop: valid elements of each partial tile
+    const uint32_t *rent; // row-wise entries of the sparse tiles (row_ent)
+    const int32_t *rcnt;  // their counts per (row, 16-row group)
+    // 1: the block-wise algorithm computes sparse partial tiles (at most
+    // SMH_SPARSE_TILE_MAX valid elements) on its gather path; set only when
+    // every key fits 16 bits (S <= 65536)
+    int hybrid;
 };
 
 // A row's summary (row_info): where its full and partial lists start, their
@@ -64,7 +72,8 @@ template <typename TIn, typename TOut> struct FwdArgs {
 struct RowInfo {
     int f0, nF, p0, nP;
     int c[4];
-    int64_t stats[5];  // nnz, n_full, n_partial, (unused), max_row_tiles
+    // nnz, n_full, n_partial, (unused), max_row_tiles, n_sparse, row_entries
+    int64_t stats[7];
 };
 template <typename TIn, typename TOut>
 __device__ inline RowInfo load_row_info(const FwdArgs<TIn, TOut> &a, int row) {
@@ -72,7 +81,8 @@ __device__ inline RowInfo load_row_info(const FwdArgs<TIn, TOut> &a, int row) {
     const int4 h = p[0], c = p[1], s = p[2], m = p[3];
     return RowInfo{h.x, h.y, h.z, h.w, {c.x, c.y, c.z, c.w},
                    {(int64_t)(((uint64_t)(uint32_t)s.y << 32) | (uint32_t)s.x),
-                    s.z, s.w, 0, m.x}};
+                    s.z, s.w, 0, m.x, m.y,
+                    (int64_t)(((uint64_t)(uint32_t)m.w << 32) | (uint32_t)m.z)}};
 }
 
 template <typename TIn, typename TOut>
@@ -103,6 +113,10 @@ inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
     a.row_order = enc.row_order;
     a.info = enc.row_info;
     a.stats = enc.stats;
+    a.pop = enc.part_pop;
+    a.rent = enc.row_ent;
+    a.rcnt = enc.row_ent_cnt;
+    a.hybrid = 0;
     return a;
 }
 

@@ -9,6 +9,8 @@ smh_kernel select_kernel(const smh_mask_stats &st, int64_t heads, int d,
     SelectInput in;
     in.nnz = st.nnz;
     in.n_full = st.n_full;
+    in.n_sparse = st.n_sparse;
+    in.entries = st.row_entries;
     in.n_partial = st.n_partial;
     in.max_row_tiles = st.max_row_tiles;
     in.heads = heads;

@@ -10,13 +10,17 @@
 //
 //   block-wise: one workgroup per (head, outer-tile row), one 64 x 64 x d
 //     tile per step.  Work = stored tiles * heads; partial tiles add a
-//     masking cost.  When the launch fits in one wave of workgroups it runs
-//     for the length of its heaviest row instead:
-//       T_blk = c0 + max(W_blk, max_row_tiles * t_tile_serial).
+//     masking cost; sparse partial tiles (gather path) cost per tile and per
+//     row-wise entry instead.  When the launch fits in one wave of
+//     workgroups it runs for the length of its heaviest row instead, whose
+//     tiles are taken to split like the mask's (a fraction f sparse, each
+//     costing its entries per wavefront, ept = entries / (4 n_sparse)):
+//       T_blk = c0 + max(W_blk, max_row_tiles * ((1 - f) t_tile_serial
+//                                                 + f * ept * t_entry_serial)).
 //   row-wise: one wavefront per (head, 8 query rows); it gathers the keys
 //     its rows see from its row's stored tiles, 8 tiles per step, and
 //     processes them in chunks of 64:
-//       T_row = c0 + max(heads * (tiles * t_gather + 8 * chunks * t_chunk),
+//       T_row = c0' + max(heads * (tiles * t_gather + 8 * chunks * t_chunk),
 //                        max_row_tiles / 8 * t_gather_serial
 //                        + (live_max / 64 + 1) * t_chunk_serial),
 //     chunks = live / 64 + rows summed over the groups of one inner-tile
@@ -45,6 +49,7 @@ namespace smh {
 // pairs per mask; rows = outer-tile rows of the encoding (masks * n_ot).
 struct SelectInput {
     int64_t nnz, n_full, n_partial, max_row_tiles;
+    int64_t n_sparse, entries;  // sparse partial tiles, their row-wise entries
     int64_t heads, rows;
     int d, bf16;
 };
@@ -58,22 +63,37 @@ struct SelectCoef {
     double row_chunk_us;       // row-wise: one 64-key chunk, chip busy
     double row_gather_ser_us;  // row-wise: one 8-tile gather step, one wavefront
     double row_chunk_ser_us;   // row-wise: one chunk on one wavefront
+    double blk_entry_us;       // block-wise gather path: one row-wise entry
+    double blk_sparse_us;      // block-wise gather path: one sparse tile
+    double blk_entry_ser_us;   // gather path: one entry on one wavefront
+    double row_launch_us;      // row-wise: fixed cost of a launch
 };
 
 #pragma clang fp contract(off)
 SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                                    double *t_blk) {
     // fitted on MI355X; fp16 and bf16 share coefficients
-    const SelectCoef k64 = {5.3194, 1.6425e-3, 1.7245e-4, 0.71518,
-                            1.2889e-4, 1.2573e-3, 0.39789, 1.5769};
-    const SelectCoef k128 = {4.3252, 3.3637e-3, 9.6461e-5, 1.1192,
-                             1.7288e-4, 2.5497e-3, 0.57893, 2.8967};
+    const SelectCoef k64 = {7.5073, 1.5049e-3, 6.6232e-4, 0.52826,
+                            1.1914e-4, 1.2808e-3, 0.49381, 1.6309,
+                            1.7999e-5, 4.8481e-5, 0.020037, 4.664};
+    const SelectCoef k128 = {7.5705, 2.9049e-3, 1.8364e-3, 0.80593,
+                             1.8268e-4, 2.6629e-3, 0.71439, 3.2687,
+                             3.4328e-5, 1.4663e-4, 0.034548, 2.7347};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
     const double heads = (double)in.heads;
+    // the sparse tiles go to the gather path when the encoding holds their
+    // row-wise entries (a sparse tile has at least one)
+    const double nsp = in.entries > 0 ? (double)in.n_sparse : 0.0;
     const double w_blk =
-        heads * (tiles * k.blk_tile_us + (double)in.n_partial * k.blk_part_us);
-    const double crit_blk = (double)in.max_row_tiles * k.blk_serial_us;
+        heads * ((tiles - nsp) * k.blk_tile_us +
+                 ((double)in.n_partial - nsp) * k.blk_part_us +
+                 (double)in.entries * k.blk_entry_us + nsp * k.blk_sparse_us);
+    const double f = tiles > 0.0 ? nsp / tiles : 0.0;
+    const double ept = nsp > 0.0 ? (double)in.entries / (4.0 * nsp) : 0.0;
+    const double crit_blk =
+        (double)in.max_row_tiles *
+        ((1.0 - f) * k.blk_serial_us + f * ept * k.blk_entry_ser_us);
     *t_blk = k.launch_us + (w_blk > crit_blk ? w_blk : crit_blk);
     double live = 64.0 * (double)in.n_full;
     if (in.n_partial > 0) {
@@ -93,16 +113,14 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
         tiles > 0.0 ? live / tiles * (double)in.max_row_tiles : 0.0;
     const double crit_row = (double)in.max_row_tiles / 8.0 * k.row_gather_ser_us +
                             (live_max / 64.0 + 1.0) * k.row_chunk_ser_us;
-    *t_row = k.launch_us + (w_row > crit_row ? w_row : crit_row);
+    *t_row = k.row_launch_us + (w_row > crit_row ? w_row : crit_row);
 }
 
 // Row-wise is taken when its predicted time is below this fraction of the
-// block-wise one.  The model underestimates the row-wise kernel by up to
-// 1.7x on long masks whose every stored tile is partial at a few percent
-// density (causal AND Bernoulli(0.02) at S = 8192-16384), where the plain
-// comparison lost 6-7% of the sweep's total time to wrong picks; with the
-// margin 0.3% (d = 64) and 0.02% (d = 128).  Fitted with the coefficients.
-constexpr double kRowMargin = 0.9;
+// block-wise one.  With the split critical path and per-kernel launch
+// costs the plain comparison loses 0.14% (d = 64) and 0.26% (d = 128) of
+// the calibration sweep's total time to wrong picks, so no margin is kept.
+constexpr double kRowMargin = 1.0;
 
 // 1 = row-wise, 2 = block-wise (the smh_kernel values).
 SMH_HD inline int select_model(const SelectInput &in) {
@@ -120,6 +138,8 @@ __device__ inline int select_on_device(const int64_t *stats, int64_t heads,
     in.n_full = stats[1];
     in.n_partial = stats[2];
     in.max_row_tiles = stats[4];
+    in.n_sparse = stats[5];
+    in.entries = stats[6];
     in.heads = heads;
     in.rows = rows;
     in.d = d;

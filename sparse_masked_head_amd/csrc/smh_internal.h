@@ -44,17 +44,26 @@ struct EncLayout {
     int64_t rows;  // outer-tile rows of the stack (G * n)
     SegPlan plan;
     size_t full_row_ptr, part_row_ptr, full_col_idx, part_col_idx,
-        part_bitmaps, stats, row_order, row_info;
+        part_bitmaps, stats, row_order, row_info, part_pop, row_ent, row_ent_cnt;
+    bool rowfmt;   // the row-wise format of sparse tiles is built (S <= 65536)
     // per segment: tile counts (full << 32 | partial), exclusive offsets
     // (same packing), valid pairs, covered query rows (bit 8k + r = strip
-    // row 8k + r), and its tiles' columns and partial-tile words (room for
+    // row 8k + r), sparse partial tiles (count << 40 | their valid pairs),
+    // and its tiles' columns, partial-tile populations and words (room for
     // seg_cap tiles each)
-    size_t seg_cnt, seg_off, seg_nnz, seg_any, seg_fcol, seg_pcol, seg_words;
+    size_t seg_cnt, seg_off, seg_nnz, seg_any, seg_sp, seg_fcol, seg_pcol,
+        seg_pop, seg_words;
+    // per segment and 16-row group: row-wise entries of its sparse tiles
+    // (count, then room for 64 per tile)
+    size_t seg_ecnt, seg_ent;
     size_t seg_cap;
     size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Longest sequence whose row-wise entries (16-bit keys) are built.
+constexpr int kRowFmtMaxS = 65536;
 
 // Caller guarantees 0 <= S <= SMH_MAX_S, G >= 1 and G * n <= SMH_MAX_ENC_ROWS.
 inline EncLayout enc_layout(int32_t S, int64_t G) {
@@ -76,18 +85,26 @@ inline EncLayout enc_layout(int32_t S, int64_t G) {
     L.full_col_idx = take(sizeof(int32_t) * cap);
     L.part_col_idx = take(sizeof(int32_t) * cap);
     L.part_bitmaps = take(sizeof(uint64_t) * 64 * cap);
-    L.stats = take(sizeof(int64_t) * 8);  // nnz, n_full, n_partial, empty rows, max row tiles
+    L.stats = take(sizeof(int64_t) * 8);  // nnz, n_full, n_partial, empty rows, max row tiles, n_sparse, sparse_nnz
     L.row_order = take(sizeof(int32_t) * rows);
     L.row_info = take(sizeof(int32_t) * 16 * rows);
+    L.part_pop = take(sizeof(int32_t) * cap);
+    L.rowfmt = S <= kRowFmtMaxS;
+    L.row_ent = take(L.rowfmt ? sizeof(uint32_t) * 256 * cap : 0);
+    L.row_ent_cnt = take(sizeof(int32_t) * 4 * rows);
     const size_t T = (size_t)L.plan.total;
     L.seg_cap = (size_t)L.plan.win * kWin;
     L.seg_cnt = take(sizeof(uint64_t) * T);
     L.seg_off = take(sizeof(uint64_t) * T);
     L.seg_nnz = take(sizeof(uint64_t) * T);
     L.seg_any = take(sizeof(uint64_t) * T);
+    L.seg_sp = take(sizeof(uint64_t) * T);
     L.seg_fcol = take(sizeof(int32_t) * T * L.seg_cap);
     L.seg_pcol = take(sizeof(int32_t) * T * L.seg_cap);
+    L.seg_pop = take(sizeof(int32_t) * T * L.seg_cap);
     L.seg_words = take(sizeof(uint64_t) * 64 * T * L.seg_cap);
+    L.seg_ecnt = take(sizeof(int32_t) * 4 * T);
+    L.seg_ent = take(L.rowfmt ? sizeof(uint32_t) * 256 * T * L.seg_cap : 0);
     L.total = off;
     return L;
 }
@@ -116,10 +133,16 @@ hipError_t launch_encode_pattern(const smh_pattern &pat, int32_t S,
 hipError_t static_scratch(char **ptr);
 
 // Block-wise kernel launcher.  in_dt: 0 f16, 1 bf16; out_dt: 0/1/2 (f32).
+// hybrid: sparse partial tiles (at most SMH_SPARSE_TILE_MAX valid elements)
+// go to the gather path where the mask allows (hybrid_allowed).
 hipError_t launch_blockwise(const void *q, const void *k, const void *v,
                             void *o, int B, int H, int S, int d, int in_dt,
                             int out_dt, float scale, const smh_mask_enc &enc,
-                            hipStream_t stream);
+                            int hybrid, hipStream_t stream);
+
+// The gather path reads the row-wise entries (built for S <= 65536) and
+// splits rows in an LDS list of at most 1024 partial tiles.
+inline bool hybrid_allowed(int S, int n_ot) { return S <= kRowFmtMaxS && n_ot <= 1024; }
 
 // Row-wise kernel launcher, same conventions.
 hipError_t launch_rowwise(const void *q, const void *k, const void *v,

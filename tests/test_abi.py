@@ -215,7 +215,7 @@ def test_calibration_model_is_the_library_model():
     for d in (64, 128):
         body = re.search(r"k%d\s*=\s*\{([^}]*)\}" % d, text).group(1)
         coef[d] = np.array([float(x) for x in body.split(",")])
-        assert len(coef[d]) == 8
+        assert len(coef[d]) == 12
     margin = float(re.search(r"kRowMargin\s*=\s*([0-9.]+)", text).group(1))
     assert margin == cal.ROW_MARGIN
     rng = np.random.default_rng(5)
@@ -233,15 +233,23 @@ def test_calibration_model_is_the_library_model():
             nnz = max(n_part, int(n_part * 4096 * rng.uniform(0.001, 0.01)))
         max_row = int(rng.integers(-(-tiles // n), min(n, tiles) + 1))
         B, H, d = int(rng.integers(1, 9)), int(rng.integers(1, 65)), int(rng.choice([64, 128]))
+        # sparse partial tiles and their row-wise entries (none, some, all)
+        n_sp = int(rng.choice([0, n_part // 2, n_part]))
+        sp_nnz = int(n_sp * rng.integers(1, 257)) if n_sp else 0
+        ents = int(rng.integers(n_sp, sp_nnz + 1)) if n_sp else 0
+        if rng.random() < 0.2:   # S > 65536 keeps no entries
+            ents = 0
         st = L.MaskStats(nnz=nnz, S=S, n_full=n_full, n_partial=n_part,
                          n_empty_rows=0, max_row_tiles=max_row, mask_b=1,
-                         mask_h=1)
+                         mask_h=1, n_sparse=n_sp, sparse_nnz=sp_nnz,
+                         row_entries=ents)
         a, b = ctypes.c_double(), ctypes.c_double()
         assert L.lib().smh_select_costs(ctypes.byref(st), B, H, d, L.SMH_F16,
                                         ctypes.byref(a), ctypes.byref(b)) == 0
         p = dict(S=S, BH=B * H, stats=dict(nnz=nnz, n_full=n_full,
                                            n_partial=n_part,
-                                           max_row_tiles=max_row))
+                                           max_row_tiles=max_row,
+                                           n_sparse=n_sp, row_entries=ents))
         tr, tb = cal.model(coef[d], p)
         assert a.value == pytest.approx(tr, rel=1e-9)
         assert b.value == pytest.approx(tb, rel=1e-9)
@@ -252,3 +260,37 @@ def test_calibration_model_is_the_library_model():
         assert out.value == want
         picks.add(out.value)
     assert picks == {L.SMH_ROWWISE, L.SMH_BLOCKWISE}   # both sides exercised
+
+
+def _header_struct_fields(name):
+    """(field, is_pointer, base type) of `typedef struct { ... } name;` in
+    smh.h, one declaration per field."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    end = text.index("} " + name + ";")
+    body = text[text.rindex("typedef struct {", 0, end) + len("typedef struct {"):end]
+    out = []
+    for decl in body.split(";"):
+        toks = decl.replace("*", " * ").split()
+        if not toks:
+            continue
+        fname = toks[-1]
+        ptr = "*" in toks
+        base = [t for t in toks[:-1] if t not in ("*", "const")][-1]
+        out.append((fname, ptr, base))
+    return out
+
+
+@pytest.mark.parametrize("cname,pyname", [("smh_mask_enc", "MaskEnc"),
+                                          ("smh_mask_stats", "MaskStats"),
+                                          ("smh_pattern", "Pattern")])
+def test_ctypes_structs_match_header(cname, pyname):
+    """The ctypes structures the binding passes by pointer have the header
+    struct's fields in the same order with the same widths (a shorter
+    structure would let the library write past it)."""
+    width = {"int32_t": 4, "int64_t": 8, "uint64_t": 8, "float": 4}
+    fields = _header_struct_fields(cname)
+    cls = getattr(L, pyname)
+    assert [f for f, _, _ in fields] == [f for f, _ in cls._fields_]
+    for (f, ptr, ctype), (_, pytype) in zip(fields, cls._fields_):
+        want = 8 if ptr else width[ctype.split()[-1]]
+        assert ctypes.sizeof(pytype) == want, f

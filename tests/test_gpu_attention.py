@@ -10,7 +10,7 @@ import torch
 
 import sparse_masked_head_amd as smh
 from oracle.attention import attention, attention_rows
-from tests.gpu_util import TDT, TOL, need_gpu
+from tests.gpu_util import TDT, TOL, counted_row_entries, need_gpu
 from workloads import get_config, make_qkv, mask_family
 
 pytestmark = pytest.mark.gpu
@@ -309,7 +309,9 @@ def test_graph_replay_matches_eager():
     torch.cuda.synchronize()
     want_out = out.clone()
     st = smh.mask_stats_get(enc)
-    want_enc = {kk: vv.clone() for kk, vv in enc.arrays(st).items()}
+    want_enc = {kk: vv.clone() for kk, vv in enc.arrays(st).items()
+                if kk != "row_ent"}
+    want_ent = counted_row_entries(enc.arrays(st))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
@@ -323,6 +325,7 @@ def test_graph_replay_matches_eager():
         got = enc.arrays(st)
         for kk in want_enc:
             assert torch.equal(got[kk], want_enc[kk]), (rep, kk)
+        assert np.array_equal(counted_row_entries(got), want_ent), rep
         eager = smh.sparse_mha_fwd(kd, qd, vd, enc, kernel="blockwise")
         torch.cuda.synchronize()
         assert torch.isfinite(eager).all()

@@ -6,8 +6,8 @@ import torch
 
 import sparse_masked_head_amd as smh
 from oracle.encode import encode_c
-from tests.gpu_util import (assert_same_encoding, enc_to_host,
-                            expected_row_order, need_gpu)
+from tests.gpu_util import (assert_same_encoding, assert_same_row_entries,
+                            enc_to_host, expected_row_order, need_gpu)
 from workloads import mask_family
 
 pytestmark = pytest.mark.gpu
@@ -24,6 +24,7 @@ def check(mask_np, dev):
     enc, st, got = gpu_encode(mask_np, dev)
     ref = encode_c(mask_np)
     assert_same_encoding(got, ref)
+    assert_same_row_entries(got, mask_np, mask_np.shape[-1])
     order, mrt = expected_row_order(ref)
     assert got["row_order"].tolist() == order
     assert st["max_row_tiles"] == mrt
@@ -38,6 +39,7 @@ def test_workload_masks_bit_exact(cid, config_mask, config_encoding):
     enc, st, got = gpu_encode(m, dev)
     ref = config_encoding(cid)
     assert_same_encoding(got, ref)
+    assert_same_row_entries(got, m, m.shape[0])
     order, mrt = expected_row_order(ref)
     assert got["row_order"].tolist() == order and st["max_row_tiles"] == mrt
 
@@ -127,6 +129,7 @@ def stack_check(masks, dev):
     got = enc_to_host(enc, st)
     ref = encode_stack(masks)
     assert_same_encoding(got, ref)
+    assert_same_row_entries(got, masks, masks.shape[-1])
     order, mrt = expected_row_order(ref)
     assert got["row_order"].tolist() == order
     assert st["max_row_tiles"] == mrt

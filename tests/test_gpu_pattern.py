@@ -9,8 +9,8 @@ import sparse_masked_head_amd as smh
 from oracle.attention import attention
 from oracle.encode import encode_c
 from oracle.pattern import pattern_mask
-from tests.gpu_util import (TOL, assert_same_encoding, enc_to_host,
-                            expected_row_order, need_gpu)
+from tests.gpu_util import (TOL, assert_same_encoding, assert_same_row_entries,
+                            enc_to_host, expected_row_order, need_gpu)
 from workloads import get_config, make_qkv, pattern_of
 
 pytestmark = pytest.mark.gpu
@@ -27,8 +27,10 @@ def gpu_pattern(S, dev, pat):
 
 def check(S, dev, pat):
     enc, st, got = gpu_pattern(S, dev, pat)
-    ref = encode_c(pattern_mask(S, **pat))
+    dense = pattern_mask(S, **pat)
+    ref = encode_c(dense)
     assert_same_encoding(got, ref)
+    assert_same_row_entries(got, dense, S)
     order, mrt = expected_row_order(ref)
     assert got["row_order"].tolist() == order and st["max_row_tiles"] == mrt
     return enc, st
