@@ -1,7 +1,7 @@
 """The analytical selector picks the faster kernel on every workload.
 
 Both kernels are timed on the full workload (HIP events around a graph of
-back-to-back launches); the choice of smh_select_kernel must be the faster
+back-to-back launches, best of three replays); the choice of smh_select_kernel must be the faster
 one, or the two must lie within 3% of each other (either choice passes)."""
 import pytest
 import torch
@@ -26,11 +26,14 @@ def _time_us(fn, reps):
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / reps
+    best = float("inf")
+    for _ in range(3):   # best of three replays: one stall does not decide
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e3 / reps)
+    return best
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
