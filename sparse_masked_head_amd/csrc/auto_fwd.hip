@@ -16,8 +16,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TO
     __shared__ __attribute__((aligned(16))) char k0[Lds<D>::KBUF], k1[Lds<D>::KBUF];
     __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
     __shared__ HybLds hl;
-    const int oi = blockIdx.x / a.U;
-    const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
+    const Slot sl = slot_at(a, (int)blockIdx.x);
     // the block-wise path's Q rows, requested before the row summary so that
     // they arrive during its round trip (under the row-wise choice the
     // row-wise path reads the same rows again, from the caches)

@@ -11,9 +11,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TI
     __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
     __shared__ HybLds hl;
     const TileBufs<D> bufs{{k0, k1}, {v0, v1}};
-    // heavy rows first across all heads (slot_of)
-    const int oi = blockIdx.x / a.U;
-    const Slot sl = slot_of(a, oi, blockIdx.x - oi * a.U);
+    // heavy rows first, heads in sequence per XCD (slot_at)
+    const Slot sl = slot_at(a, (int)blockIdx.x);
     typename Frag<TIn>::type qf[D / 32];
     load_q_frags<D>(a, sl.I, sl.bh, qf);  // before the row summary's round trip
     blockwise_row<D, TIn, TOut>(a, bufs, sl.row, sl.I, sl.bh, load_row_info(a, sl.row), qf, hl);

@@ -161,14 +161,6 @@ __device__ __attribute__((always_inline)) inline uint32_t mask_bits(
     return (m.mb[0] | (m.mb[1] << 8) | (m.mb[2] << 16) | (m.mb[3] << 24)) >> nib;
 }
 
-// Bit `off` of x as 0 or -1 (v_bfe_i32; written out so that the compiler
-// keeps this one-instruction form instead of a compare and a select).
-template <int off> __device__ __attribute__((always_inline)) inline int bit_mask(int x) {
-    int r;
-    asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(r) : "v"(x), "i"(off));
-    return r;
-}
-
 // Wait for this wave's outstanding global loads (the tile loads into LDS
 // among them), before the barrier that hands their buffers to every wave.
 __device__ __attribute__((always_inline)) inline void wait_loads() {
@@ -182,6 +174,11 @@ __device__ __attribute__((always_inline)) inline void wait_loads() {
 template <int N> __device__ __attribute__((always_inline)) inline void wait_loads_but() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait for this wave's outstanding LDS operations (global loads are not
+// waited for): vmcnt and expcnt at their maxima, lgkmcnt 0.
+__device__ __attribute__((always_inline)) inline void wait_lds() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 // s_barrier without the workgroup fence of __syncthreads (which would also
 // wait for every global load still in flight).
@@ -197,7 +194,14 @@ template <int D> struct RowState {
     f4_t acc[D / 16];
     float m, l;
     float mc;  // m * c, or 0 while m is -inf (the exponent offset)
+    // d = 64: the row sum comes from the matrix cores (P^T times a block of
+    // ones), every element the whole sum of the lane's query; l is unused
+    f4_t lacc;
 };
+// At d = 64 the softmax's vector work outweighs the MFMA work of a tile, so
+// the row sum moves to the matrix cores (two more MFMAs per tile instead of
+// eight v_dot2); at d = 128 the matrix cores are the busier unit.
+template <int D> constexpr bool kSumOnMfma = false;
 
 // S^T = K Q^T for one tile (four 16-key sub-tiles), raw scores.  For a
 // partial tile the accumulators start at 0 for a valid key and -inf for a
@@ -220,41 +224,48 @@ template <int D> __device__ inline KOff<D> k_offsets(int lq, int g) {
     return o;
 }
 
+// The starting accumulators of a partial tile come from a 16-entry table in
+// LDS (entry n: element i is 0 if bit i of n is set, else -inf), one
+// 16-byte read per sub-tile indexed by the lane's four mask bits, instead
+// of two vector operations per score.
+__device__ __attribute__((always_inline)) inline void fill_mask_lut(f4_t *lut) {
+    const int t = threadIdx.x;
+    if (t < 64)
+        reinterpret_cast<float *>(lut)[t] = (t >> 2 >> (t & 3)) & 1 ? 0.f : -INFINITY;
+}
+
 template <int D, typename TIn, bool kPartial>
 __device__ __attribute__((always_inline)) inline void qk_tile_k(
     f4_t (&sc)[4], const typename Frag<TIn>::type (&qf)[D / 32],
-    const char *kb, const KOff<D> &ko, uint32_t mbits) {
+    const char *kb, const KOff<D> &ko, uint32_t mbits, const f4_t *lut) {
     using F = Frag<TIn>;
     using frag = typename F::type;
     const char *ks = kb + ko.base;
-    const int inv = (int)~mbits;
+    // the four sub-tiles' products alternate (slice s of d outer), so that
+    // consecutive MFMAs never wait for each other's results
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        f4_t c0 = f4_t{0.f, 0.f, 0.f, 0.f};
-        if (kPartial)  // all ones where masked -> the bits of -inf
-            c0 = f4_t{__int_as_float(bit_mask<0>(inv >> (8 * st)) & (int)0xFF800000u),
-                      __int_as_float(bit_mask<1>(inv >> (8 * st)) & (int)0xFF800000u),
-                      __int_as_float(bit_mask<2>(inv >> (8 * st)) & (int)0xFF800000u),
-                      __int_as_float(bit_mask<3>(inv >> (8 * st)) & (int)0xFF800000u)};
-        const char *row = ks + 16 * st * Lds<D>::CPR * 16;
-        const frag a0 = *reinterpret_cast<const frag *>(row + ko.x[0]);
-        sc[st] = F::mfma(a0, qf[0], c0);
+    for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-        for (int s = 1; s < D / 32; ++s) {
-            const frag a = *reinterpret_cast<const frag *>(row + ko.x[s]);
-            sc[st] = F::mfma(a, qf[s], sc[st]);
+        for (int st = 0; st < 4; ++st) {
+            const frag a = *reinterpret_cast<const frag *>(
+                ks + 16 * st * Lds<D>::CPR * 16 + ko.x[s]);
+            f4_t c = sc[st];
+            if (s == 0) {
+                c = f4_t{0.f, 0.f, 0.f, 0.f};
+                if (kPartial) c = lut[(mbits >> (8 * st)) & 0xFu];
+            }
+            sc[st] = F::mfma(a, qf[s], c);
         }
-    }
 }
 
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void qk_tile(
     f4_t (&sc)[4], const typename Frag<TIn>::type (&qf)[D / 32],
-    const char *kb, const KOff<D> &ko, bool partial, uint32_t mbits) {
+    const char *kb, const KOff<D> &ko, bool partial, uint32_t mbits, const f4_t *lut) {
     if (partial)
-        qk_tile_k<D, TIn, true>(sc, qf, kb, ko, mbits);
+        qk_tile_k<D, TIn, true>(sc, qf, kb, ko, mbits, lut);
     else
-        qk_tile_k<D, TIn, false>(sc, qf, kb, ko, mbits);
+        qk_tile_k<D, TIn, false>(sc, qf, kb, ko, mbits, lut);
 }
 
 // This lane's byte offsets into a V buffer for the transposing reads of
@@ -281,15 +292,13 @@ template <int D> __device__ inline VOff<D> v_offsets(int lq, int g) {
 
 // Softmax of the scores of NST 16-key sub-tiles (masked ones already -inf;
 // NST = 4 for an outer tile, 2 for a gathered chunk of 32 keys) and
-// O^T += V^T P^T with V's rows in a tile-buffer layout.  c = scale *
-// log2(e) > 0.  kWaitV: wait for this wave's outstanding loads (the V rows
-// it staged itself) before the first V read.
-template <int D, typename TIn, int NST = 4, bool kWaitV = false>
-__device__ __attribute__((always_inline)) inline void softmax_pv(
-    RowState<D> &rs, f4_t (&sc)[NST], const char *vb, float c, const VOff<D> &vo) {
-    using F = Frag<TIn>;
-    using frag = typename F::type;
-    using L = Lds<D>;
+// O^T += V^T P^T with V's rows in a tile-buffer layout, in three parts so
+// that the tile loop can interleave them with the next tile's QK^T:
+// sm_max (row max, lazy rescale), sm_exp (probabilities and row sum, vector
+// work only) and pv (the matrix-core product).  c = scale * log2(e) > 0.
+template <int D, int NST>
+__device__ __attribute__((always_inline)) inline void sm_max(RowState<D> &rs,
+                                                             const f4_t (&sc)[NST], float c) {
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
@@ -308,42 +317,67 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
         const float alpha = grow ? __builtin_amdgcn_exp2f((rs.m - m_new) * c) : 1.f;
         rs.m = m_new;
         rs.mc = grow ? mx * c : rs.mc;  // a growing max is finite
-        rs.l *= alpha;
+        if (kSumOnMfma<D>)
+            rs.lacc *= alpha;
+        else
+            rs.l *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
     }
-    const float mc = rs.mc;
+}
 
-    // P^T as B operand: keys 32u + 4g + j (j < 4), 32u + 16 + 4g + j - 4
+// P^T as B operand: keys 32u + 4g + j (j < 4), 32u + 16 + 4g + j - 4.
+template <int D, typename TIn, int NST>
+__device__ __attribute__((always_inline)) inline void sm_exp(
+    RowState<D> &rs, const f4_t (&sc)[NST], float c,
+    typename Frag<TIn>::type (&pf)[NST / 2]) {
     constexpr int NU = NST / 2;
-    frag pf[NU];
+    const float mc = rs.mc;
 #pragma unroll
     for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             pf[st >> 1][(st & 1) * 4 + i] =
                 (TIn)__builtin_amdgcn_exp2f(fmaf(sc[st][i], c, -mc));
-    float lsum = rs.l;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        uint32_t pw[4];
-        __builtin_memcpy(pw, &pf[u], 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
-    }
-    rs.l = lsum;
-
-    // A operand V^T (rows = output columns 16dt + l%16, slots = keys of
-    // the P^T slots) read with ds_read_b64_tr_b16 from row-major V: within
-    // each 16-lane group, lane j = a + 4q points at V[key0 + q][d0 + 4a]
-    // and lane i receives V[key0 .. key0+3][d0 + i]; key0 = 32u + 4g for
-    // slots 0..3 and 32u + 16 + 4g for slots 4..7.  vo holds the lane's
-    // (q, a) offsets in the swizzled buffer.
-    if (kWaitV) wait_loads();
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    if (!kSumOnMfma<D>) {
+        float lsum = rs.l;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
+            uint32_t pw[4];
+            __builtin_memcpy(pw, &pf[u], 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
+        }
+        rs.l = lsum;
+    }
+}
+
+// A operand V^T (rows = output columns 16dt + l%16, slots = keys of the P^T
+// slots) read with ds_read_b64_tr_b16 from row-major V: within each 16-lane
+// group, lane j = a + 4q points at V[key0 + q][d0 + 4a] and lane i receives
+// V[key0 .. key0+3][d0 + i]; key0 = 32u + 4g for slots 0..3 and 32u + 16 +
+// 4g for slots 4..7.  vo holds the lane's (q, a) offsets in the swizzled
+// buffer.
+template <int D, typename TIn, int NU>
+__device__ __attribute__((always_inline)) inline void pv(
+    RowState<D> &rs, const typename Frag<TIn>::type (&pf)[NU], const char *vb,
+    const VOff<D> &vo) {
+    using F = Frag<TIn>;
+    using frag = typename F::type;
+    using L = Lds<D>;
+    if (kSumOnMfma<D>) {
+        frag ones;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ones[i] = (TIn)1.f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) rs.lacc = F::mfma(ones, pf[u], rs.lacc);
+    }
+    // key half u outer, so that consecutive MFMAs write different
+    // accumulators
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
             const char *p0 = vb + vo.x[dt] + 32 * u * L::CPR * 16;
             const char *p1 = p0 + 16 * L::CPR * 16;
             const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -356,6 +390,18 @@ __device__ __attribute__((always_inline)) inline void softmax_pv(
             rs.acc[dt] = F::mfma(a, pf[u], rs.acc[dt]);
         }
     }
+}
+
+// The three parts in sequence.  kWaitV: wait for this wave's outstanding
+// loads (the V rows it staged itself) before the first V read.
+template <int D, typename TIn, int NST = 4, bool kWaitV = false>
+__device__ __attribute__((always_inline)) inline void softmax_pv(
+    RowState<D> &rs, f4_t (&sc)[NST], const char *vb, float c, const VOff<D> &vo) {
+    typename Frag<TIn>::type pf[NST / 2];
+    sm_max<D, NST>(rs, sc, c);
+    sm_exp<D, TIn, NST>(rs, sc, c, pf);
+    if (kWaitV) wait_loads();
+    pv<D, TIn, NST / 2>(rs, pf, vb, vo);
 }
 
 // The stored tiles of one outer-tile row: full tiles first, then partial.
@@ -394,11 +440,13 @@ struct TileList {
 // into dense and sparse partial tiles (S <= 65536: keys fit 16 bits).
 constexpr int kHybMaxN = 1024;
 
-// LDS of the split: the row's partial tiles, dense ones first, each
-// column << 16 | index in the row's partial list, and per-wavefront counts.
+// LDS of the row beside the tile buffers: the split's partial tiles, dense
+// ones first, each column << 16 | index in the row's partial list, its
+// per-wavefront counts, and the table of partial-tile accumulators.
 struct HybLds {
     uint32_t list[kHybMaxN];
     int wcnt[16];
+    f4_t lut[16];  // starting accumulators of partial tiles (fill_mask_lut)
 };
 
 // The split of an outer-tile row's partial tiles (whole workgroup, two
@@ -488,113 +536,140 @@ __device__ __attribute__((always_inline)) inline void load_q_frags(
 // elements would cost a dense tile's work on the matrix cores, so each
 // wavefront instead streams the row-wise entries of its 16 query rows (the
 // keys some of them see in the row's sparse tiles, with their row sets;
-// built once per mask by the encoder) and computes them in chunks of 32
-// keys with the same MFMA layout and online-softmax state as the tile path.
-// Pipeline, at chunk c: the entries of chunk c + 2 are requested (one
-// register: lane l holds entry l % 32); chunk c + 1's K rows go into one of
-// two register sets and its V rows (global_load_lds) into one of two V
-// slots, chunk-swizzled like a tile buffer so that the tile path's V^T
-// reads serve, its keys and row sets taken from its entry register with
-// ds_bpermute; then chunk c is computed.  The V slots of chunks c and c + 1
-// lie in different LDS objects (the K tile buffers, the V tile buffers),
-// so the V^T reads of one do not wait for the loads landing in the other.
-// Loads past the list re-read its last entry (or key 0), so every wait
-// counts the same loads.
+// built once per mask by the encoder) and computes them in chunks of 16
+// keys with the same online-softmax state as the tile path: S^T = K Q^T
+// with v_mfma_f32_16x16x32 (one 16-key sub-tile), O^T += V^T P^T with
+// v_mfma_f32_16x16x16 (16 keys deep), whose B operand is exactly the four
+// scores a lane holds.
+// The K and V rows of a chunk come into per-wavefront LDS slots by
+// global_load_lds (each instruction whole 256- or 128-byte rows, as the tile
+// loads), laid out like a tile buffer's first 16 rows, so that the tile
+// path's operand offsets (KOff, VOff) serve.  Slots of chunk parity p lie
+// in the tile buffers K_p and V_p, wavefront w's at 16 rows * w, so that
+// the slots being read and the slots being filled are different LDS
+// objects and the compiler does not make the reads wait for the loads.
+// Pipeline, at chunk c: the entries of chunk c + 2 are requested (lane l
+// holds entry l % 16), chunk c + 1's K and V rows are requested (their keys
+// taken from its entry register with ds_bpermute), then chunk c is
+// computed.  Loads past the list re-read its last entry (or key 0), so
+// every wait counts the same loads.
 
-// One chunk in registers: K rows as A operands (entries 16st + lq, st =
-// 0, 1; d = 32s + 8g .. +7) and the lane's score slots that are valid (bit
-// 4st + i: entry 16st + 4g + i is in the chunk and its row set holds the
-// lane's query row).
-template <int D, typename TIn> struct ChunkK {
-    typename Frag<TIn>::type k[2][D / 32];
-    uint32_t ok;
+template <typename TIn> struct Frag4;
+template <> struct Frag4<_Float16> {
+    typedef _Float16 type __attribute__((ext_vector_type(4)));
+    static __device__ inline f4_t mfma(type a, type b, f4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Frag4<__bf16> {
+    typedef short type __attribute__((ext_vector_type(4)));
+    static __device__ inline f4_t mfma(type a, type b, f4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
 };
 
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void gather_stream(
-    RowState<D> &rs, char *vslot0, char *vslot1, const uint32_t *__restrict__ ents,
-    int ne, const typename Frag<TIn>::type (&qf)[D / 32], const TIn *__restrict__ Kh,
-    const TIn *__restrict__ Vh, float c, int S, const VOff<D> &vo) {
+    RowState<D> &rs, char *kslot0, char *kslot1, char *vslot0, char *vslot1,
+    const uint32_t *__restrict__ ents, int ne, const typename Frag<TIn>::type (&qf)[D / 32],
+    const TIn *__restrict__ Kh, const TIn *__restrict__ Vh, float c, int S,
+    const KOff<D> &ko, const VOff<D> &vo) {
     using F = Frag<TIn>;
+    using F4 = Frag4<TIn>;
+    using frag = typename F::type;
     using L = Lds<D>;
     const int lane = threadIdx.x & 63, lq = lane & 15, g = lane >> 4;
-    constexpr int RPI = 1024 / (2 * D);  // V rows per 1 KB load instruction
-    constexpr int NV = 32 / RPI;         // V instructions per chunk
-    constexpr int NK = 2 * (D / 32);     // K loads per chunk
-    const int nch = (ne + 31) >> 5;
+    constexpr int RPI = 1024 / (2 * D);  // rows per 1 KB load instruction
+    constexpr int NI = 16 / RPI;         // load instructions per chunk, K and V each
+    const int nch = (ne + 15) >> 4;
     // the key of entry ei of a chunk of n entries, clamped into the head's
     // rows; past the chunk: key 0
     auto key_of = [&](int ei, int n, uint32_t e) __attribute__((always_inline)) {
         return ei < n ? min((int)(e & 0xFFFFu), S - 1) : 0;
     };
     auto load_e = [&](int ci) __attribute__((always_inline)) {
-        return ents[min(32 * ci + (lane & 31), ne - 1)];
+        return ents[min(16 * ci + lq, ne - 1)];
     };
-    auto issue = [&](int ci, uint32_t e, char *vs, ChunkK<D, TIn> &ck)
-        __attribute__((always_inline)) {
-        // entry idx of the chunk, from lane idx of the entry register
+    // chunk ci's rows into slots ks, vs; returns the lane's valid score
+    // slots (bit i: entry 4g + i is in the chunk and its row set holds the
+    // lane's query row)
+    auto issue = [&](int ci, uint32_t e, char *ks, char *vs) __attribute__((always_inline)) {
         auto ent = [&](int idx) __attribute__((always_inline)) {
             return (uint32_t)__builtin_amdgcn_ds_bpermute(idx << 2, (int)e);
         };
-        const int n = min(32, ne - 32 * ci);
+        const int n = min(16, ne - 16 * ci);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int rr = RPI * i + lane / L::CPR, cp = lane % L::CPR;
+            const size_t off = (size_t)key_of(rr, n, ent(rr)) * D + 8 * (cp ^ L::sw(rr));
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(Kh + off),
+                                             (lds_void_t *)(ks + 1024 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(Vh + off),
+                                             (lds_void_t *)(vs + 1024 * i), 16, 0, 0);
+        }
         uint32_t ok = 0;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int rr = RPI * i + lane / L::CPR, cp = lane % L::CPR;
-            const int key = key_of(rr, n, ent(rr));
-            __builtin_amdgcn_global_load_lds(
-                (gbl_void_t *)(Vh + (size_t)key * D + 8 * (cp ^ L::sw(rr))),
-                (lds_void_t *)(vs + 1024 * i), 16, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t e2 = ent(4 * g + i);
+            ok |= (uint32_t)(4 * g + i < n && ((e2 >> (16 + lq)) & 1u)) << i;
         }
+        return ok;
+    };
+    auto compute = [&](const char *ks, const char *vs, uint32_t ok) __attribute__((always_inline)) {
+        f4_t sc[1];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const typename F::type *krow = reinterpret_cast<const typename F::type *>(
-                Kh + (size_t)key_of(16 * st + lq, n, ent(16 * st + lq)) * D);
+        for (int i = 0; i < 4; ++i) sc[0][i] = (ok >> i) & 1u ? 0.f : -INFINITY;
 #pragma unroll
-            for (int s2 = 0; s2 < D / 32; ++s2) ck.k[st][s2] = krow[4 * s2 + g];
+        for (int s2 = 0; s2 < D / 32; ++s2)
+            sc[0] = F::mfma(*reinterpret_cast<const frag *>(ks + ko.base + ko.x[s2]), qf[s2], sc[0]);
+        sm_max<D, 1>(rs, sc, c);
+        typename F4::type p4;
+        {
+            TIn pv4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t e2 = ent(16 * st + 4 * g + i);
-                ok |= (uint32_t)(16 * st + 4 * g + i < n && ((e2 >> (16 + lq)) & 1u))
-                      << (4 * st + i);
+            for (int i = 0; i < 4; ++i)
+                pv4[i] = (TIn)__builtin_amdgcn_exp2f(fmaf(sc[0][i], c, -rs.mc));
+            __builtin_memcpy(&p4, pv4, 8);
+            uint32_t pw[2];
+            __builtin_memcpy(pw, pv4, 8);
+            if (kSumOnMfma<D>) {
+                typename F4::type ones;
+                TIn o4[4] = {(TIn)1.f, (TIn)1.f, (TIn)1.f, (TIn)1.f};
+                __builtin_memcpy(&ones, o4, 8);
+                rs.lacc = F4::mfma(ones, p4, rs.lacc);
+            } else {
+                rs.l = sum2<TIn>(pw[1], sum2<TIn>(pw[0], rs.l));
             }
         }
-        ck.ok = ok;
-    };
-    auto compute = [&](const char *vs, const ChunkK<D, TIn> &ck)
-        __attribute__((always_inline)) {
-        f4_t sc[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            f4_t c0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c0[i] = (ck.ok >> (4 * st + i)) & 1u ? 0.f : -INFINITY;
-            sc[st] = F::mfma(ck.k[st][0], qf[0], c0);
-#pragma unroll
-            for (int s2 = 1; s2 < D / 32; ++s2) sc[st] = F::mfma(ck.k[st][s2], qf[s2], sc[st]);
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t *)(vs + vo.x[dt]));
+            typename F4::type a;
+            __builtin_memcpy(&a, &v, 8);
+            rs.acc[dt] = F4::mfma(a, p4, rs.acc[dt]);
         }
-        softmax_pv<D, TIn, 2>(rs, sc, vs, c, vo);
     };
     if (nch == 0) return;
-    ChunkK<D, TIn> ka, kb;
     uint32_t ea = load_e(0), eb = load_e(1);
-    issue(0, ea, vslot0, ka);
-    // chunk ci: registers `cur`, V slot vc; chunk ci + 1: entries in `en`,
-    // goes to `nxt` and vn; the entries of ci + 2 replace those of ci in
-    // `ef`.  Loads issued after chunk ci's: the entries of ci + 2 (one) and
-    // chunk ci + 1's (NV + NK).
-    auto iter = [&](int ci, uint32_t &ef, const uint32_t en, char *vc, char *vn,
-                    ChunkK<D, TIn> &cur, ChunkK<D, TIn> &nxt) __attribute__((always_inline)) {
+    uint32_t oka = issue(0, ea, kslot0, vslot0), okb = 0;
+    // chunk ci: slots of parity ci & 1, valid bits `okc`; chunk ci + 1:
+    // entries in `en` (requested before chunk ci's rows, so that reading
+    // them does not wait for those rows), goes to the other slots (valid
+    // bits into `okn`); the entries of ci + 2 replace those of ci in `ef`.
+    // Loads issued after chunk ci's rows: the entries of ci + 2 and chunk
+    // ci + 1's rows, left in flight while chunk ci is computed.
+    auto iter = [&](int ci, uint32_t &ef, const uint32_t en, char *kc, char *vc, char *kn,
+                    char *vn, const uint32_t okc, uint32_t &okn) __attribute__((always_inline)) {
         ef = load_e(ci + 2);
-        issue(ci + 1, en, vn, nxt);
-        wait_loads_but<NV + NK + 1>();
+        okn = issue(ci + 1, en, kn, vn);
+        wait_loads_but<2 * NI + 1>();
         asm volatile("" ::: "memory");
-        compute(vc, cur);
+        compute(kc, vc, okc);
     };
     for (int ci = 0; ci < nch; ci += 2) {
-        iter(ci, ea, eb, vslot0, vslot1, ka, kb);
+        iter(ci, ea, eb, kslot0, vslot0, kslot1, vslot1, oka, okb);
         if (ci + 1 >= nch) break;
-        iter(ci + 1, eb, ea, vslot1, vslot0, kb, ka);
+        iter(ci + 1, eb, ea, kslot1, vslot1, kslot0, vslot0, okb, oka);
     }
     wait_loads();  // the loads past the list land before the slots are left
 }
@@ -625,6 +700,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     // per-tile dispatch: with sparse partial tiles in the encoding, the row's
     // partial tiles are split; the dense ones stay on the tile path below,
     // the sparse ones go to the gather path after it
+    fill_mask_lut(hl.lut);  // read after the barriers that precede any tile
     const bool hyb = a.hybrid && ri.stats[5] > 0 && ri.nP > 0;
     int nD = ri.nP;
     if (hyb) {
@@ -647,6 +723,8 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     rs.m = -INFINITY;
     rs.mc = 0.f;
     rs.l = 0.f;
+    rs.lacc = f4_t{0.f, 0.f, 0.f, 0.f};
+    const f4_t *lut = hl.lut;
 
     // per-lane LDS offsets, the same in every buffer
     const KOff<D> ko = k_offsets<D>(lq, g);
@@ -721,9 +799,10 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
         wait_loads_but<2 * (D / 32) + 4>();
         m_a = nF == 0 ? mask_bits(mk0, nib) : 0u;
         m_b = nT > 1 && nF <= 1 ? mask_bits(mk1, nib) : 0u;
+        wait_lds();  // the accumulator table is written before the barrier
         bare_barrier();
-        qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a);
-        if (nT > 1) qk_tile<D, TIn>(s_b, qf, bufs.k[1], ko, nF <= 1, m_b);
+        qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a, lut);
+        if (nT > 1) qk_tile<D, TIn>(s_b, qf, bufs.k[1], ko, nF <= 1, m_b, lut);
         softmax_pv<D, TIn>(rs, s_a, bufs.v[0], a.c, vo);
         if (nT > 2) {
             const uint32_t m_c = nF <= 2 ? mask_bits(mk2, nib) : 0u;
@@ -731,7 +810,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
             store_tile_regs<D>(bufs.k[0], k2, wu, l);
             store_tile_regs<D>(bufs.v[0], v2, wu, l);
             __syncthreads();
-            qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF <= 2, m_c);
+            qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF <= 2, m_c, lut);
         }
         if (nT > 1) softmax_pv<D, TIn>(rs, s_b, bufs.v[1], a.c, vo);
         if (nT > 2) softmax_pv<D, TIn>(rs, s_a, bufs.v[0], a.c, vo);
@@ -748,7 +827,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
         if (nT > 0 && nF == 0) m_a = mask_bits(mk0, nib);
         if (nT > 1 && 1 >= nF) m_b = mask_bits(mk1, nib);
         __syncthreads();
-        if (nT > 0) qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a);
+        if (nT > 0) qk_tile<D, TIn>(s_a, qf, bufs.k[0], ko, nF == 0, m_a, lut);
         // every wave has read K(0) before tile step 0 loads into its buffer
         __syncthreads();
 
@@ -767,7 +846,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
             if (it + 2 < nT) load_k(bufs.k[cb], mk0, it + 2, jk);
             if (it + 1 < nT) load_v(bufs.v[nb], jv);
             if (it + 1 < nT)
-                qk_tile<D, TIn>(nxt, qf, bufs.k[nb], ko, it + 1 >= nF, mn);
+                qk_tile<D, TIn>(nxt, qf, bufs.k[nb], ko, it + 1 >= nF, mn, lut);
             softmax_pv<D, TIn>(rs, cur, bufs.v[cb], a.c, vo);
             wait_loads();
             mc = it + 2 < nT && it + 2 >= nF ? mask_bits(mk0, nib) : 0u;
@@ -784,20 +863,20 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     }
 
     if (hyb && nD < ri.nP) {
-        // every wave is done with the tile buffers; each takes one as its
-        // slice for the gather path, over its group's row-wise entries
+        // every wave is done with the tile buffers; each takes 16 rows of
+        // each as its slots for the gather path, over its group's row-wise
+        // entries
         if (nT > 0) __syncthreads();
-        // V slot 0 of waves 0-3 in the K buffers, slot 1 in the V buffers
-        constexpr int VSL = 32 * D * 2;
-        char *vs0 = (w < 2 ? bufs.k[0] : bufs.k[1]) + VSL * (w & 1);
-        char *vs1 = (w < 2 ? bufs.v[0] : bufs.v[1]) + VSL * (w & 1);
+        constexpr int SLOT = 16 * D * 2;
         const uint32_t *ents = a.rent + 256 * (size_t)ri.p0 + 64 * (size_t)w * ri.nP;
         const int ne = a.rcnt[4 * (size_t)row + w];
-        gather_stream<D, TIn>(rs, vs0, vs1, ents, ne, qf, Kh, Vh, a.c, a.S, vo);
+        gather_stream<D, TIn>(rs, bufs.k[0] + SLOT * w, bufs.k[1] + SLOT * w,
+                              bufs.v[0] + SLOT * w, bufs.v[1] + SLOT * w, ents, ne, qf,
+                              Kh, Vh, a.c, a.S, ko, vo);
     }
 
     // epilogue: total l over the 4 lanes of this query
-    const float lt = sum_xor32(sum_xor16(rs.l));
+    const float lt = kSumOnMfma<D> ? rs.lacc[0] : sum_xor32(sum_xor16(rs.l));
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qi < a.S) {
         TOut *orow = a.O + head + (size_t)qi * D;

@@ -50,6 +50,8 @@ template <typename TIn, typename TOut> struct FwdArgs {
     // order, used when every workgroup of the launch is resident at once
     // and the order cannot matter (saves a dependent load per workgroup)
     int use_order;
+    // 1: launch slots go to XCDs head by head (slot_at); needs U % 8 == 0
+    int xcd_seq;
     const int32_t *frp, *fci, *prp, *pci;
     const uint64_t *bm;
     const int32_t *row_order;
@@ -105,6 +107,7 @@ inline FwdArgs<TIn, TOut> make_args(const void *q, const void *k,
     a.U = (enc.mask_b > 1 ? 1 : B) * (enc.mask_h > 1 ? 1 : H);
     a.c = scale * kLog2e;
     a.use_order = 1;
+    a.xcd_seq = a.U % 8 == 0;
     a.frp = enc.full_row_ptr;
     a.fci = enc.full_col_idx;
     a.prp = enc.part_row_ptr;
@@ -143,6 +146,24 @@ __device__ inline Slot slot_of(const FwdArgs<TIn, TOut> &a, int oi, int user) {
     const int h = a.mask_h > 1 ? g - (g / a.mask_h) * a.mask_h : user - (user / Hu) * Hu;
     sl.bh = b * a.H + h;
     return sl;
+}
+
+// The slot of launch index b.  Workgroups go round-robin over the 8 XCDs
+// (b % 8), each XCD with its own L2.  Plain order (slot b = oi * U + user)
+// keeps a head on one XCD when U % 8 == 0 but runs U / 8 heads on it at
+// once; with xcd_seq the k-th workgroup of XCD x (b = 8k + x) takes head
+// slot hs = k / R and row position oi = k % R, user = x + 8 hs, so an XCD
+// works through its heads one after another (heavy rows first within each)
+// and its L2 holds one head's K and V at a time.
+template <typename TIn, typename TOut>
+__device__ inline Slot slot_at(const FwdArgs<TIn, TOut> &a, int b) {
+    if (a.xcd_seq) {
+        const int k = b >> 3, x = b & 7;
+        const int hs = k / a.R;
+        return slot_of(a, k - hs * a.R, x + 8 * hs);
+    }
+    const int oi = b / a.U;
+    return slot_of(a, oi, b - oi * a.U);
 }
 
 template <typename T> constexpr int is_bf16() { return __is_same(T, __bf16) ? 1 : 0; }
