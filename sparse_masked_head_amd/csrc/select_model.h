@@ -73,12 +73,12 @@ struct SelectCoef {
 SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                                    double *t_blk) {
     // fitted on MI355X; fp16 and bf16 share coefficients
-    const SelectCoef k64 = {7.5073, 1.5049e-3, 6.6232e-4, 0.52826,
-                            1.1914e-4, 1.2808e-3, 0.49381, 1.6309,
-                            1.7999e-5, 4.8481e-5, 0.020037, 4.664};
-    const SelectCoef k128 = {7.5705, 2.9049e-3, 1.8364e-3, 0.80593,
-                             1.8268e-4, 2.6629e-3, 0.71439, 3.2687,
-                             3.4328e-5, 1.4663e-4, 0.034548, 2.7347};
+    const SelectCoef k64 = {7.3557, 1.4708e-3, 6.0991e-4, 0.46235,
+                            1.5243e-4, 1.1802e-3, 0.39384, 1.6643,
+                            1.3273e-5, 6.1359e-5, 0.02441, 4.4805};
+    const SelectCoef k128 = {7.2023, 2.8306e-3, 1.8716e-3, 0.77483,
+                             3.2719e-4, 2.4591e-3, 0.45524, 3.3562,
+                             2.4479e-5, 2.1138e-4, 0.037198, 2.5491};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
     const double heads = (double)in.heads;
@@ -118,8 +118,9 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
 
 // Row-wise is taken when its predicted time is below this fraction of the
 // block-wise one.  With the split critical path and per-kernel launch
-// costs the plain comparison loses 0.14% (d = 64) and 0.26% (d = 128) of
-// the calibration sweep's total time to wrong picks, so no margin is kept.
+// costs the plain comparison loses 0.08% (d = 64) and 0.05% (d = 128) of
+// the calibration sweep's total time to wrong picks (every pick within 3%
+// of the faster kernel on 178 and 176 of 180 points), so no margin is kept.
 constexpr double kRowMargin = 1.0;
 
 // 1 = row-wise, 2 = block-wise (the smh_kernel values).
