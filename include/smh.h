@@ -210,11 +210,11 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
                             size_t ws_bytes, smh_mask_enc *enc_out,
                             void *stream);
 
-/* Size of the static encoder scratch of smh_encode_masks_noalloc: 100 MiB,
- * enough for one mask of S = 16384 (96.8 MiB) or any stack with as many
+/* Size of the static encoder scratch of smh_encode_masks_noalloc: 40 MiB,
+ * enough for one mask of S = 16384 (33 MiB) or any stack with as many
  * outer tiles.  Every device the library runs on holds one copy of it in
  * the library's code object until the process ends. */
-#define SMH_STATIC_SCRATCH_BYTES ((size_t)100 << 20)
+#define SMH_STATIC_SCRATCH_BYTES ((size_t)40 << 20)
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
@@ -235,8 +235,7 @@ smh_status smh_encode_masks(const uint8_t *masks, int32_t mask_b,
  *   masks, mask_b, mask_h, S, enc_out, stream: as for smh_encode_masks;
  *       the stream must belong to the current device.
  * SMH_EUNSUPPORTED when the scratch the stack needs exceeds
- * SMH_STATIC_SCRATCH_BYTES (about ceil(S/64)^2 * masks * 1544 bytes for
- * S <= 65536, which build the row-wise entries, 520 bytes above).
+ * SMH_STATIC_SCRATCH_BYTES (about ceil(S/64)^2 * masks * 530 bytes).
  * Every call on a device shares that device's scratch (no call needs it
  * cleared, and each call's result depends only on its own inputs): calls
  * that may overlap on one device (different streams, different host

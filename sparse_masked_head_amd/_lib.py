@@ -10,7 +10,7 @@ SMH_F16, SMH_BF16, SMH_F32 = range(3)
 SMH_AUTO, SMH_ROWWISE, SMH_BLOCKWISE, SMH_BLOCKWISE_DENSE = range(4)
 SMH_MAX_S = 131072
 SMH_MAX_ENC_ROWS = 8192
-SMH_STATIC_SCRATCH_BYTES = 100 << 20
+SMH_STATIC_SCRATCH_BYTES = 40 << 20
 SMH_SPARSE_TILE_MAX = 256
 
 # every exported name of include/smh.h

@@ -19,11 +19,13 @@
 //   scan (one workgroup): exclusive prefix of the segments' tile counts,
 //     row pointers, statistics and the heavy-first row order;
 //   placement (one workgroup per segment): copy the segment's columns and
-//     words to their final places, and the columns among its row's first
-//     four stored tiles to the row's summary (row_info).
+//     words to their final places, the columns among its row's first four
+//     stored tiles to the row's summary (row_info), and write the row-wise
+//     entries of its sparse tiles.
 // With at most kFusedMaxSegs segments and kFusedRows rows the scan runs as
-// one extra workgroup of the placement launch and each placement workgroup adds up the counts
-// before it itself (cheap at that size, and one launch fewer).  No
+// one extra workgroup (the first) of the placement launch and each
+// placement workgroup adds up the counts before it itself (cheap at that
+// size, and one launch fewer).  No
 // workgroup ever waits for another.  Every output is a pure function of
 // the mask: the result is deterministic and equals appending tiles row by
 // row, column by column.
@@ -142,7 +144,7 @@ struct Seg {  // per-segment scratch (EncLayout)
     int32_t *fcol, *pcol, *pop;
     uint64_t *words;
     int32_t *ecnt;  // [segment][group]: row-wise entries of its sparse tiles
-    uint32_t *ent;  // [segment][group][64 * cap], or null: no row-wise format
+    int rowfmt;     // the row-wise entries are built (S <= 65536)
     int cap;  // tiles of room per segment
 };
 
@@ -152,63 +154,31 @@ constexpr int kSpShift = 40;
 constexpr uint64_t kSpLow = (1ull << kSpShift) - 1;
 
 // The row-wise entries of the segment's sparse tiles (tkind bit 18), per
-// group q of 16 query rows (inner-tile rows 2q, 2q + 1): for each key that
-// some row of the group sees, rows << 16 | key, in key order (tiles in
-// column order, then inner-tile column, then column in it).  Lane (ir, ic)
-// of the wavefront holding a tile owns word (ir, ic); the lanes of even ir
-// gather their column block's keys for group ir / 2 from their word and
-// the word below it.  Three passes: entries per (tile, group); their prefix
-// over the segment's tiles (wavefront q, lane = tile); the entries, at the
-// segment's scratch for group q.
-__device__ void strip_entries(int s, int nwin, int w0, Seg sg,
-                              uint64_t (*lw)[64], const int *tkind) {
-    __shared__ int ecnt_t[kMaxSegTiles][4];
-    __shared__ int eoff_t[kMaxSegTiles][4];
+// group q of 16 query rows (inner-tile rows 2q, 2q + 1), are one per key
+// that some row of the group sees: rows << 16 | key.  The strip pass only
+// counts them (wavefront w: tiles w, w + 4, ...; lane (ir, ic) owns word
+// (ir, ic), the lanes of even ir count their column block's live keys for
+// group ir / 2 from their word and the word below it) and stores the
+// segment's total per group; the placement pass, which knows where the
+// row's lists start, writes them (place_entries).
+__device__ void strip_entry_counts(int s, int nwin, Seg sg, uint64_t (*lw)[64],
+                                   const int *tkind) {
+    __shared__ int ecnt_t[4][4];  // per wavefront and group
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int ir = lane >> 3, ic = lane & 7, q = ir >> 1;
     const bool top = (ir & 1) == 0;
     const int ntile = kWin * nwin;
-    for (int l = w; l < kMaxSegTiles; l += 4) {
-        int c = 0;
-        if (l < ntile && (tkind[l] & (1 << 18)) && top)
-            c = __popc(live_columns(lw[l][lane] | lw[l][lane + 8]));
-        c += __shfl_xor(c, 1);
-        c += __shfl_xor(c, 2);
-        c += __shfl_xor(c, 4);
-        if (ic == 0 && top) ecnt_t[l][q] = c;
-    }
+    int c = 0;
+    for (int l = w; l < ntile; l += 4)
+        if ((tkind[l] & (1 << 18)) && top)
+            c += __popc(live_columns(lw[l][lane] | lw[l][lane + 8]));
+    c += __shfl_xor(c, 1);
+    c += __shfl_xor(c, 2);
+    c += __shfl_xor(c, 4);
+    c += __shfl_xor(c, 8);  // the two inner-tile rows' lanes: ir and ir ^ 1
+    if (lane == 16 * q) ecnt_t[w][q] = c;
     __syncthreads();
-    {
-        const int v = ecnt_t[lane][w];  // wavefront w: group w, lane: tile
-        int incl = v;
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(incl, d);
-            if (lane >= d) incl += y;
-        }
-        eoff_t[lane][w] = incl - v;
-        if (lane == 63) sg.ecnt[4 * (size_t)s + w] = incl;
-    }
-    __syncthreads();
-    for (int l = w; l < ntile; l += 4) {
-        if (!(tkind[l] & (1 << 18))) continue;  // (uniform in the wavefront)
-        const uint64_t lo = lw[l][lane], hi = lw[l][(lane + 8) & 63];
-        uint32_t live = top ? live_columns(lo | hi) : 0u;
-        const int cnt = __popc(live);
-        int incl = cnt;  // prefix over the 8 lanes of this inner-tile row
-        for (int d = 1; d < 8; d <<= 1) {
-            const int y = __shfl_up(incl, d, 8);
-            if (ic >= d) incl += y;
-        }
-        int pos = eoff_t[l][q] + incl - cnt;
-        const uint32_t key0 = 64u * (uint32_t)(kWin * (w0 + (l >> 3)) + (l & 7)) + 8u * ic;
-        uint32_t *dst = sg.ent + (4 * (size_t)s + q) * (64 * (size_t)sg.cap);
-        while (live) {
-            const int cb = __builtin_ctz(live);
-            live &= live - 1;
-            const uint32_t rows = column_rows(lo, cb) | (column_rows(hi, cb) << 8);
-            dst[pos++] = (rows << 16) | (key0 + (uint32_t)cb);
-        }
-    }
+    if (t < 4) sg.ecnt[4 * (size_t)s + t] = ecnt_t[0][t] + ecnt_t[1][t] + ecnt_t[2][t] + ecnt_t[3][t];
 }
 
 // Shared tail of the strip passes: classify the segment's tiles (wavefront
@@ -260,9 +230,9 @@ __device__ void strip_classify(int s, int nwin, int w0, int n, Seg sg,
         if (k & (1 << 16))
             sg.words[((size_t)s * sg.cap + (k & 0xFFFF)) * 64 + lane] = lw[l][lane];
     }
-    if (sg.ent) {
+    if (sg.rowfmt) {
         if (seg_sparse)
-            strip_entries(s, nwin, w0, sg, lw, tkind);
+            strip_entry_counts(s, nwin, sg, lw, tkind);
         else if (t < 4)
             sg.ecnt[4 * (size_t)s + t] = 0;
     }
@@ -516,7 +486,7 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
             nnz += (long long)sg.nnz[I * C + c];
             an |= sg.any[I * C + c];
             spw += (long long)sg.sp[I * C + c];
-            if (sg.ent) {
+            if (sg.rowfmt) {
                 const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[I * C + c];
                 ents += (long long)e.x + e.y + e.z + e.w;
             }
@@ -641,7 +611,7 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
             nnz += (long long)sg.nnz[lane * C + c];
             an |= sg.any[lane * C + c];
             spw += (long long)sg.sp[lane * C + c];
-            if (sg.ent) {
+            if (sg.rowfmt) {
                 const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[lane * C + c];
                 ents += (long long)e.x + e.y + e.z + e.w;
             }
@@ -703,9 +673,45 @@ __global__ __launch_bounds__(256) void enc_scan(int S, int n, int R, int G,
     scan_body<kScanRows, kScanBins>(S, n, R, G, plan, sg, enc, true);
 }
 
-// Placement of segment blockIdx.x.  kSelf: the workgroup adds up the tile
-// counts of the segments before it; the extra last workgroup runs the scan.
-// Otherwise the offsets come from enc_scan.  The segment's own columns and
+// The row-wise entries of a segment's sparse partial tiles, written at
+// their final places: group q's entries of the segment start at
+// ent_dst[q] (after the row's earlier segments' entries, in the row's region
+// for group q); within it, tiles in column order, then key.  Wavefront q
+// writes group q: per sparse tile, lane k takes key 64J + k, its rows among
+// the group's 16 (bit k % 8 of each byte of the two inner-tile words of
+// column block k / 8), and a ballot over the lanes gives each live key its
+// rank, so a tile's entries are one run of contiguous stores.  Lane t < 64
+// of the workgroup brings partial tile t's column and valid-element count;
+// words: the segment's partial-tile words (64 per tile, in list order, in
+// LDS).
+__device__ void place_entries(int np, int colp, int popp, const uint64_t *words,
+                              uint32_t *__restrict__ row_ent, const size_t *ent_dst) {
+    __shared__ int col_t[kMaxSegTiles];  // column of a sparse tile, -1 otherwise
+    const int t = threadIdx.x, q = t >> 6, lane = t & 63;
+    if (t < kMaxSegTiles)
+        col_t[t] = t < np && popp <= SMH_SPARSE_TILE_MAX ? colp : -1;
+    __syncthreads();  // also: ent_dst from wavefront 0, the words
+    uint32_t *dst = row_ent + ent_dst[q];
+    const int jc = lane >> 3, c = lane & 7;
+    for (int l = 0; l < np; ++l) {
+        const int J = col_t[l];
+        if (J < 0) continue;  // (uniform in the workgroup)
+        const uint64_t wa = words[64 * (size_t)l + 16 * q + jc];
+        const uint64_t wb = words[64 * (size_t)l + 16 * q + 8 + jc];
+        const uint32_t rows = column_rows(wa, c) | (column_rows(wb, c) << 8);
+        const uint64_t live = __builtin_amdgcn_ballot_w64(rows != 0);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(live >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)live, 0u));
+        if (rows) dst[rank] = (rows << 16) | (64u * (uint32_t)J + (uint32_t)lane);
+        dst += __popcll(live);
+    }
+}
+
+// Placement of a segment.  kSelf: workgroup 0 runs the scan (first, so that
+// it is dispatched with the first placements instead of after them) and
+// workgroup s + 1 places segment s, adding up the tile counts of the
+// segments before it.  Otherwise workgroup s places segment s with the
+// offsets from enc_scan.  The segment's own columns and
 // first words are loaded together with its offsets (they do not depend on
 // them), so a small segment is placed after one memory round trip.
 template <bool kSelf>
@@ -714,9 +720,9 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
                                                  smh_mask_enc enc) {
     __shared__ unsigned long long sh_u[4];
     __shared__ size_t ent_dst[4];  // where the segment's entries of group g go
-    const int t = threadIdx.x, s = blockIdx.x;
+    const int t = threadIdx.x, s = (int)blockIdx.x - (kSelf ? 1 : 0);
     if constexpr (kSelf) {
-        if (s == plan.total) {
+        if (s < 0) {
             if (R <= 64) {
                 if (threadIdx.x < 64) scan_small(S, n, R, G, plan, sg, enc);
             } else {
@@ -734,14 +740,14 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
     const int row = s / plan.per_row, s0 = row * plan.per_row;
     const uint64_t rcnt = t < plan.per_row ? sg.cnt[s0 + t] : 0;
     // row-wise entries of the row's segments per group (lane = segment)
-    const int4 recnt = sg.ent && t < plan.per_row
+    const int4 recnt = sg.rowfmt && t < plan.per_row
                            ? reinterpret_cast<const int4 *>(sg.ecnt)[s0 + t]
                            : make_int4(0, 0, 0, 0);
     // columns (t < cap) and the first 256 16-byte chunks of the words
     const int colf = t < sg.cap ? sg.fcol[base + t] : 0;
     const int colp = t < sg.cap ? sg.pcol[base + t] : 0;
     const int popp = t < sg.cap ? sg.pop[base + t] : 0;
-    const int4 ecs = sg.ent ? reinterpret_cast<const int4 *>(sg.ecnt)[s] : make_int4(0, 0, 0, 0);
+    const int4 ecs = sg.rowfmt ? reinterpret_cast<const int4 *>(sg.ecnt)[s] : make_int4(0, 0, 0, 0);
     const bool has_ent = (ecs.x | ecs.y | ecs.z | ecs.w) != 0;
     const u4v *src = reinterpret_cast<const u4v *>(sg.words + base * 64);
     const u4v w0 = t < sg.cap * 32 ? src[t] : u4v{0, 0, 0, 0};
@@ -765,7 +771,7 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
             bp += __shfl_xor(bp, o);
             rf += __shfl_xor(rf, o);
         }
-        if (sg.ent) {
+        if (sg.rowfmt) {
             // the segment's entries go after those of the row's earlier
             // segments, in the row's region of group q; the row's first
             // segment writes the row's counts
@@ -809,18 +815,20 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
         }
     }
     u4v *dst = reinterpret_cast<u4v *>(enc.part_bitmaps + (size_t)pp * 64);
-    if (t < np * 32) dst[t] = w0;
-    for (int e = t + 256; e < np * 32; e += 256) dst[e] = src[e];
-    if (has_ent) {
-        __syncthreads();  // ent_dst from wavefront 0
-        const int cnts[4] = {ecs.x, ecs.y, ecs.z, ecs.w};
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint32_t *es = sg.ent + (4 * (size_t)s + g) * (64 * (size_t)sg.cap);
-            uint32_t *ed = enc.row_ent + ent_dst[g];
-            for (int i = t; i < cnts[g]; i += 256) ed[i] = es[i];
-        }
+    // with row-wise entries to write, the words also go to LDS (dynamic, cap
+    // tiles of room), where place_entries reads them
+    extern __shared__ u4v wl[];
+    if (t < np * 32) {
+        dst[t] = w0;
+        if (has_ent) wl[t] = w0;
     }
+    for (int e = t + 256; e < np * 32; e += 256) {
+        const u4v v = src[e];
+        dst[e] = v;
+        if (has_ent) wl[e] = v;
+    }
+    if (has_ent)
+        place_entries(np, colp, popp, reinterpret_cast<const uint64_t *>(wl), enc.row_ent, ent_dst);
 }
 
 // S == 0: an empty encoding.  Row pointers {0}, all statistics zero.
@@ -863,17 +871,19 @@ hipError_t encode_launches(StripLaunch strip, int32_t S, const EncLayout &L,
     sg.pcol = (int32_t *)(sc + L.seg_pcol);
     sg.pop = (int32_t *)(sc + L.seg_pop);
     sg.ecnt = (int32_t *)(sc + L.seg_ecnt);
-    sg.ent = L.rowfmt ? (uint32_t *)(sc + L.seg_ent) : nullptr;
+    sg.rowfmt = L.rowfmt ? 1 : 0;
     sg.words = (uint64_t *)(sc + L.seg_words);
     sg.cap = (int)L.seg_cap;
     strip(n, plan, sg);
+    // placement's LDS for the segment's words (place_entries)
+    const size_t wl_bytes = L.rowfmt ? sizeof(uint64_t) * 64 * L.seg_cap : 0;
     if (plan.total <= kFusedMaxSegs && R <= kFusedRows) {
-        hipLaunchKernelGGL(enc_place<true>, dim3(plan.total + 1), dim3(256), 0,
+        hipLaunchKernelGGL(enc_place<true>, dim3(plan.total + 1), dim3(256), wl_bytes,
                            stream, S, n, R, G, plan, sg, enc);
     } else {
         hipLaunchKernelGGL(enc_scan, dim3(1), dim3(256), 0, stream, S, n, R, G,
                            plan, sg, enc);
-        hipLaunchKernelGGL(enc_place<false>, dim3(plan.total), dim3(256), 0,
+        hipLaunchKernelGGL(enc_place<false>, dim3(plan.total), dim3(256), wl_bytes,
                            stream, S, n, R, G, plan, sg, enc);
     }
     return hipGetLastError();
