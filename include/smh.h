@@ -67,11 +67,13 @@ typedef enum {
 /* Outer tile edge and inner tile edge, in elements. */
 #define SMH_OT 64
 #define SMH_IT 8
-/* A partial outer tile with at most this many valid elements (1/16 of its
+/* A partial outer tile with at most this many valid elements (2.7% of its
  * 4096) is "sparse": the block-wise kernel computes it on its gather path
  * (each wavefront gathers the keys its 16 query rows see) instead of as a
- * dense 64 x 64 tile, when the mask's length allows (S <= 65536). */
-#define SMH_SPARSE_TILE_MAX 256
+ * dense 64 x 64 tile, when the mask's length allows (S <= 65536).  The
+ * gather path is the faster one below about 105 valid elements per tile on
+ * MI355X (random masks of rising density, d = 64 and 128). */
+#define SMH_SPARSE_TILE_MAX 112
 
 /* The two-level encoding of a stack of S x S masks ([EXP] storage-format
  * items).  A host struct of device pointers into the caller's workspace; it

@@ -11,7 +11,7 @@ SMH_AUTO, SMH_ROWWISE, SMH_BLOCKWISE, SMH_BLOCKWISE_DENSE = range(4)
 SMH_MAX_S = 131072
 SMH_MAX_ENC_ROWS = 8192
 SMH_STATIC_SCRATCH_BYTES = 40 << 20
-SMH_SPARSE_TILE_MAX = 256
+SMH_SPARSE_TILE_MAX = 112
 
 # every exported name of include/smh.h
 EXPORTS = ("smh_encode_workspace_bytes", "smh_encode_masks_workspace_bytes",

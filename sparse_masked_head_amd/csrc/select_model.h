@@ -73,12 +73,12 @@ struct SelectCoef {
 SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                                    double *t_blk) {
     // fitted on MI355X; fp16 and bf16 share coefficients
-    const SelectCoef k64 = {7.3557, 1.4708e-3, 6.0991e-4, 0.46235,
-                            1.5243e-4, 1.1802e-3, 0.39384, 1.6643,
-                            1.3273e-5, 6.1359e-5, 0.02441, 4.4805};
-    const SelectCoef k128 = {7.2023, 2.8306e-3, 1.8716e-3, 0.77483,
-                             3.2719e-4, 2.4591e-3, 0.45524, 3.3562,
-                             2.4479e-5, 2.1138e-4, 0.037198, 2.5491};
+    const SelectCoef k64 = {7.8545, 0.0014456, 1.8493e-4, 0.47247,
+                            1.6135e-4, 0.0011622, 0.41532, 1.6621,
+                            1.3022e-5, 6.2611e-5, 0.024697, 4.7474};
+    const SelectCoef k128 = {7.844, 0.0029088, 5.3013e-4, 0.74578,
+                             3.5921e-4, 0.002399, 0.46418, 3.2985,
+                             2.4037e-5, 2.2114e-4, 0.036547, 3.1329};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
     const double heads = (double)in.heads;
@@ -118,9 +118,9 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
 
 // Row-wise is taken when its predicted time is below this fraction of the
 // block-wise one.  With the split critical path and per-kernel launch
-// costs the plain comparison loses 0.08% (d = 64) and 0.05% (d = 128) of
+// costs the plain comparison loses 0.14% (d = 64) and 0.08% (d = 128) of
 // the calibration sweep's total time to wrong picks (every pick within 3%
-// of the faster kernel on 178 and 176 of 180 points), so no margin is kept.
+// of the faster kernel on 170 and 172 of 180 points), so no margin is kept.
 constexpr double kRowMargin = 1.0;
 
 // 1 = row-wise, 2 = block-wise (the smh_kernel values).

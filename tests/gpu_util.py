@@ -48,7 +48,7 @@ def assert_same_encoding(got, ref):
             "row_info"
 
 
-SPARSE_TILE_MAX = 256   # smh.h SMH_SPARSE_TILE_MAX: a partial tile of at
+SPARSE_TILE_MAX = 112   # smh.h SMH_SPARSE_TILE_MAX: a partial tile of at
                         # most this many valid elements is sparse
 
 

@@ -235,7 +235,7 @@ def test_calibration_model_is_the_library_model():
         B, H, d = int(rng.integers(1, 9)), int(rng.integers(1, 65)), int(rng.choice([64, 128]))
         # sparse partial tiles and their row-wise entries (none, some, all)
         n_sp = int(rng.choice([0, n_part // 2, n_part]))
-        sp_nnz = int(n_sp * rng.integers(1, 257)) if n_sp else 0
+        sp_nnz = int(n_sp * rng.integers(1, L.SMH_SPARSE_TILE_MAX + 1)) if n_sp else 0
         ents = int(rng.integers(n_sp, sp_nnz + 1)) if n_sp else 0
         if rng.random() < 0.2:   # S > 65536 keeps no entries
             ents = 0
