@@ -194,14 +194,7 @@ template <int D> struct RowState {
     f4_t acc[D / 16];
     float m, l;
     float mc;  // m * c, or 0 while m is -inf (the exponent offset)
-    // d = 64: the row sum comes from the matrix cores (P^T times a block of
-    // ones), every element the whole sum of the lane's query; l is unused
-    f4_t lacc;
 };
-// At d = 64 the softmax's vector work outweighs the MFMA work of a tile, so
-// the row sum moves to the matrix cores (two more MFMAs per tile instead of
-// eight v_dot2); at d = 128 the matrix cores are the busier unit.
-template <int D> constexpr bool kSumOnMfma = false;
 
 // S^T = K Q^T for one tile (four 16-key sub-tiles), raw scores.  For a
 // partial tile the accumulators start at 0 for a valid key and -inf for a
@@ -317,10 +310,7 @@ __device__ __attribute__((always_inline)) inline void sm_max(RowState<D> &rs,
         const float alpha = grow ? __builtin_amdgcn_exp2f((rs.m - m_new) * c) : 1.f;
         rs.m = m_new;
         rs.mc = grow ? mx * c : rs.mc;  // a growing max is finite
-        if (kSumOnMfma<D>)
-            rs.lacc *= alpha;
-        else
-            rs.l *= alpha;
+        rs.l *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) rs.acc[i] *= alpha;
     }
@@ -339,17 +329,15 @@ __device__ __attribute__((always_inline)) inline void sm_exp(
         for (int i = 0; i < 4; ++i)
             pf[st >> 1][(st & 1) * 4 + i] =
                 (TIn)__builtin_amdgcn_exp2f(fmaf(sc[st][i], c, -mc));
-    if (!kSumOnMfma<D>) {
-        float lsum = rs.l;
+    float lsum = rs.l;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            uint32_t pw[4];
-            __builtin_memcpy(pw, &pf[u], 16);
+    for (int u = 0; u < NU; ++u) {
+        uint32_t pw[4];
+        __builtin_memcpy(pw, &pf[u], 16);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
-        }
-        rs.l = lsum;
+        for (int j = 0; j < 4; ++j) lsum = sum2<TIn>(pw[j], lsum);
     }
+    rs.l = lsum;
 }
 
 // A operand V^T (rows = output columns 16dt + l%16, slots = keys of the P^T
@@ -365,13 +353,6 @@ __device__ __attribute__((always_inline)) inline void pv(
     using F = Frag<TIn>;
     using frag = typename F::type;
     using L = Lds<D>;
-    if (kSumOnMfma<D>) {
-        frag ones;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ones[i] = (TIn)1.f;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) rs.lacc = F::mfma(ones, pf[u], rs.lacc);
-    }
     // key half u outer, so that consecutive MFMAs write different
     // accumulators
 #pragma unroll
@@ -632,14 +613,7 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
             __builtin_memcpy(&p4, pv4, 8);
             uint32_t pw[2];
             __builtin_memcpy(pw, pv4, 8);
-            if (kSumOnMfma<D>) {
-                typename F4::type ones;
-                TIn o4[4] = {(TIn)1.f, (TIn)1.f, (TIn)1.f, (TIn)1.f};
-                __builtin_memcpy(&ones, o4, 8);
-                rs.lacc = F4::mfma(ones, p4, rs.lacc);
-            } else {
-                rs.l = sum2<TIn>(pw[1], sum2<TIn>(pw[0], rs.l));
-            }
+            rs.l = sum2<TIn>(pw[1], sum2<TIn>(pw[0], rs.l));
         }
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
@@ -723,7 +697,6 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     rs.m = -INFINITY;
     rs.mc = 0.f;
     rs.l = 0.f;
-    rs.lacc = f4_t{0.f, 0.f, 0.f, 0.f};
     const f4_t *lut = hl.lut;
 
     // per-lane LDS offsets, the same in every buffer
@@ -876,7 +849,7 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
     }
 
     // epilogue: total l over the 4 lanes of this query
-    const float lt = kSumOnMfma<D> ? rs.lacc[0] : sum_xor32(sum_xor16(rs.l));
+    const float lt = sum_xor32(sum_xor16(rs.l));
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qi < a.S) {
         TOut *orow = a.O + head + (size_t)qi * D;
