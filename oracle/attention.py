@@ -100,10 +100,12 @@ def attention(q, k, v, mask, scale=None, row_block=1024):
     return out
 
 
-def attention_rows(q, k, v, mask, b, h, rows, scale=None):
+def attention_rows(q, k, v, mask, b, h, rows, scale=None, mask_rows=None):
     """The same definition for selected query rows of one (b, h).
 
-    Used to check full-size workloads on a sample of outputs.  Returns
+    Used to check full-size workloads on a sample of outputs.  mask: as for
+    attention; or None with mask_rows [len(rows), S] bool, the mask rows of
+    those queries alone, for masks too large to hold whole.  Returns
     [len(rows), d] float64.
     """
     rows = np.asarray(rows, dtype=np.int64)
@@ -116,5 +118,9 @@ def attention_rows(q, k, v, mask, b, h, rows, scale=None):
     vb = _as_f64(v[b, h])
     d = qb.shape[1]
     tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    if mask_rows is not None:
+        mask_rows = np.asarray(mask_rows, dtype=bool)
+        assert mask_rows.shape == (len(rows), kb.shape[0])
+        return _rows(qb, kb, vb, mask_rows, tau)
     m = np.asarray(mask_of(mask, b, h), dtype=bool)
     return _rows(qb, kb, vb, m[rows], tau)

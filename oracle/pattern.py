@@ -60,30 +60,45 @@ def draws16(S, rows, seed):
             np.uint64(0xFFFF)).astype(np.int64)
 
 
+def pattern_rows(S, rows, causal=False, window=-1, global_rows=0,
+                 global_cols=0, blocks=None, block_keep=1.0, random_p=0.0,
+                 seed=0):
+    """Rows `rows` (array of query indices) of the [S, S] bool mask the
+    pattern describes: [len(rows), S].  Element (i, j) is valid iff it is
+    in a global row or column, in the band |i - j| <= window, in a block
+    of map value 1, or drawn: u(i, j) < floor(block_keep * 65536) in a
+    block of another nonzero value, u(i, j) < floor(random_p * 65536)
+    elsewhere; then, when causal, only j <= i."""
+    S = int(S)
+    keep16, rand16 = threshold16(block_keep), threshold16(random_p)
+    rows = np.asarray(rows, dtype=np.int64)
+    i = rows[:, None]
+    j = np.arange(S, dtype=np.int64)[None, :]
+    v = (i < global_rows) | (j < global_cols)
+    if window >= 0:
+        v |= np.abs(i - j) <= window
+    blk = (np.asarray(blocks, dtype=np.uint8)[i // 64, j // 64]
+           if blocks is not None else np.zeros((len(rows), S), np.uint8))
+    v |= blk == 1
+    if keep16 > 0 or rand16 > 0:
+        u = draws16(S, rows, seed)
+        v |= (blk != 0) & (blk != 1) & (u < keep16)
+        v |= (blk == 0) & (u < rand16)
+    if causal:
+        v &= j <= i
+    return v
+
+
 def pattern_mask(S, causal=False, window=-1, global_rows=0, global_cols=0,
                  blocks=None, block_keep=1.0, random_p=0.0, seed=0,
                  row_block=512):
-    """The dense [S, S] bool mask the pattern describes."""
+    """The dense [S, S] bool mask the pattern describes (pattern_rows, a
+    block of rows at a time)."""
     S = int(S)
-    keep16, rand16 = threshold16(block_keep), threshold16(random_p)
     m = np.zeros((S, S), dtype=bool)
-    j = np.arange(S, dtype=np.int64)[None, :]
-    if blocks is not None:
-        blocks = np.asarray(blocks, dtype=np.uint8)
     for r0 in range(0, S, row_block):
         rows = np.arange(r0, min(S, r0 + row_block), dtype=np.int64)
-        i = rows[:, None]
-        v = (i < global_rows) | (j < global_cols)
-        if window >= 0:
-            v |= np.abs(i - j) <= window
-        blk = (blocks[i // 64, j // 64] if blocks is not None
-               else np.zeros((len(rows), S), np.uint8))
-        v |= blk == 1
-        if keep16 > 0 or rand16 > 0:
-            u = draws16(S, rows, seed)
-            v |= (blk != 0) & (blk != 1) & (u < keep16)
-            v |= (blk == 0) & (u < rand16)
-        if causal:
-            v &= j <= i
-        m[r0:r0 + len(rows)] = v
+        m[r0:r0 + len(rows)] = pattern_rows(S, rows, causal, window,
+                                            global_rows, global_cols, blocks,
+                                            block_keep, random_p, seed)
     return m

@@ -117,3 +117,36 @@ def test_attention_through_pattern(kernel):
     assert torch.equal(a, b)
     err = float(np.abs(a.double().cpu().numpy() - attention(q, k, v, mask)).max())
     assert err <= TOL["f16"], err
+
+
+@pytest.mark.parametrize("kernel", ["auto", "blockwise", "blockwise_dense", "rowwise"])
+def test_longest_masks_without_row_entries(kernel):
+    """S = 66000 (past 65536 keys: no row-wise entries are built, and 1032
+    outer tiles per side: the block-wise kernel keeps every partial tile on
+    its tile path), encoded from a pattern (its dense mask would take 4.4
+    GB): the statistics say so, and sampled output rows, among them rows in
+    the last outer tile and the last row, match the oracle computed from
+    those rows' mask rows alone."""
+    from oracle.attention import attention_rows
+    from oracle.pattern import pattern_rows
+    dev = need_gpu()
+    S, B, H, d = 66000, 1, 2, 64
+    pat = dict(causal=True, window=100, random_p=0.001, seed=5)
+    print(f"pattern S={S} {pat} kernel {kernel}", flush=True)
+    enc = smh.encode_pattern(S, device=dev, **pat)
+    st = smh.mask_stats_get(enc)
+    assert st["row_entries"] == 0 and st["n_sparse"] > 0
+    q, k, v = make_qkv(B, H, S, d, "f16", seed=66)
+    o = smh.sparse_mha_fwd(q.to(dev), k.to(dev), v.to(dev), enc, kernel=kernel,
+                           stats=None if kernel == "auto" else st)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(67)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 101, 4096, 33000, 65535, 65536,
+                                      65599, 65600, 65983, 65984, S - 1],
+                                     rng.integers(0, S, 18)]))
+    mrows = pattern_rows(S, rows, **pat)
+    for h in range(H):
+        ref = attention_rows(q, k, v, None, 0, h, rows, mask_rows=mrows)
+        got = o[0, h].index_select(0, torch.as_tensor(rows, device=dev)).double().cpu().numpy()
+        err = float(np.abs(got - ref).max())
+        assert err <= TOL["f16"], (h, err)

@@ -172,6 +172,9 @@ def test_rows_entry_matches_full():
     full16 = attention(qt, kt, vt, mask)
     got16 = attention_rows(qt, kt, vt, mask, 0, 1, rows)
     np.testing.assert_allclose(got16, full16[0, 1, rows], rtol=0, atol=1e-13)
+    # the same rows given by their mask rows alone (no [S, S] mask)
+    got_r = attention_rows(q, k, v, None, 1, 0, rows, mask_rows=mask[rows])
+    np.testing.assert_allclose(got_r, full[1, 0, rows], rtol=0, atol=1e-13)
 
 
 @pytest.mark.parametrize("cid", [1, 3])

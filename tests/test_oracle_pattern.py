@@ -131,3 +131,18 @@ def test_bigbird_pattern_blocks_match_workload_blocks():
     br = ref.reshape(nb, 64, nb, 64).any(axis=(1, 3))
     assert np.array_equal(bm, br)
     assert np.array_equal(bm, pat["blocks"] != 0)
+
+
+def test_pattern_rows_are_the_mask_rows():
+    """pattern_rows on any set of query rows (unordered, repeated, the last
+    one) equals those rows of the whole mask, for each kind of term."""
+    from oracle.pattern import pattern_rows
+    S = 300
+    rng = np.random.default_rng(21)
+    blocks = rng.integers(0, 3, size=(5, 5)).astype(np.uint8)
+    rows = np.array([299, 0, 64, 63, 150, 150, 7, 298])
+    for kw in (dict(causal=True, window=20, random_p=0.05, seed=3),
+               dict(global_rows=5, global_cols=9, random_p=0.01, seed=11),
+               dict(blocks=blocks, block_keep=0.3, random_p=0.002, seed=8)):
+        full = pattern_mask(S, **kw)
+        assert np.array_equal(pattern_rows(S, rows, **kw), full[rows]), kw
