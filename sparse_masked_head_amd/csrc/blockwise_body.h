@@ -30,7 +30,8 @@
 //     tile's 64 words the four bytes (one per 16-key sub-tile) that hold
 //     its query row's bits, together with the K tile, carries them in a
 //     register, and starts the tile's QK^T accumulators at 0 / -inf from
-//     them, so the masking costs two VALU operations per score;
+//     them (one 16-byte read per sub-tile from a table in LDS), so masked
+//     scores leave the matrix cores as -inf;
 //   * online softmax in base 2 (running max and sum per query) with lazy
 //     rescaling (the reference max moves only when passed by more than 8
 //     in exponent units); only the 4 lanes sharing a query exchange values
@@ -39,6 +40,11 @@
 //     the score registers rounded to the input type, V^T the A operand from
 //     LDS; the O rows a lane holds belong to the query whose softmax state
 //     it holds, so rescaling is lane-local.
+// Per-tile dispatch: with sparse partial tiles in the encoding (at most
+// SMH_SPARSE_TILE_MAX valid elements), the row's partial tiles are split;
+// the tile loop above runs the full and dense partial ones, then each
+// wavefront runs the row's sparse ones on the gather path (gather_stream)
+// into the same softmax state.
 // Epilogue: O / l (0 for a row with no valid key), stored in the output type.
 #pragma once
 
@@ -284,11 +290,11 @@ template <int D> __device__ inline VOff<D> v_offsets(int lq, int g) {
 }
 
 // Softmax of the scores of NST 16-key sub-tiles (masked ones already -inf;
-// NST = 4 for an outer tile, 2 for a gathered chunk of 32 keys) and
-// O^T += V^T P^T with V's rows in a tile-buffer layout, in three parts so
-// that the tile loop can interleave them with the next tile's QK^T:
-// sm_max (row max, lazy rescale), sm_exp (probabilities and row sum, vector
-// work only) and pv (the matrix-core product).  c = scale * log2(e) > 0.
+// NST = 4 for an outer tile) and O^T += V^T P^T with V's rows in a
+// tile-buffer layout, in three parts: sm_max (row max, lazy rescale; the
+// gather path uses it on one sub-tile), sm_exp (probabilities and row sum,
+// vector work only) and pv (the matrix-core product).  c = scale * log2(e)
+// > 0.
 template <int D, int NST>
 __device__ __attribute__((always_inline)) inline void sm_max(RowState<D> &rs,
                                                              const f4_t (&sc)[NST], float c) {
@@ -373,15 +379,13 @@ __device__ __attribute__((always_inline)) inline void pv(
     }
 }
 
-// The three parts in sequence.  kWaitV: wait for this wave's outstanding
-// loads (the V rows it staged itself) before the first V read.
-template <int D, typename TIn, int NST = 4, bool kWaitV = false>
+// The three parts in sequence.
+template <int D, typename TIn, int NST = 4>
 __device__ __attribute__((always_inline)) inline void softmax_pv(
     RowState<D> &rs, f4_t (&sc)[NST], const char *vb, float c, const VOff<D> &vo) {
     typename Frag<TIn>::type pf[NST / 2];
     sm_max<D, NST>(rs, sc, c);
     sm_exp<D, TIn, NST>(rs, sc, c, pf);
-    if (kWaitV) wait_loads();
     pv<D, TIn, NST / 2>(rs, pf, vb, vo);
 }
 
