@@ -486,10 +486,11 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
             nnz += (long long)sg.nnz[I * C + c];
             an |= sg.any[I * C + c];
             spw += (long long)sg.sp[I * C + c];
-            if (sg.rowfmt) {
-                const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[I * C + c];
-                ents += (long long)e.x + e.y + e.z + e.w;
-            }
+            // read whatever the format (the array is always there; its
+            // sum is dropped without row-wise entries): a load under the
+            // flag became a branch with a wait of its own per segment
+            const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[I * C + c];
+            ents += (long long)e.x + e.y + e.z + e.w;
         }
         const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull);
         rowc[I] = ((uint32_t)f << 16) | (uint32_t)p;
@@ -498,6 +499,7 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
         empty += 64 - __popcll(an);
         own += rc;
     }
+    if (!sg.rowfmt) ents = 0;
     unsigned long long run = block_exclusive_scan(own, sh_u);  // prefix of row r_lo
     for (int I = r_lo; I < r_hi; ++I) {
         enc.full_row_ptr[I] = (int32_t)(run >> 32);
@@ -611,12 +613,11 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
             nnz += (long long)sg.nnz[lane * C + c];
             an |= sg.any[lane * C + c];
             spw += (long long)sg.sp[lane * C + c];
-            if (sg.rowfmt) {
-                const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[lane * C + c];
-                ents += (long long)e.x + e.y + e.z + e.w;
-            }
+            const int4 e = reinterpret_cast<const int4 *>(sg.ecnt)[lane * C + c];
+            ents += (long long)e.x + e.y + e.z + e.w;  // (as in scan_body)
         }
     }
+    if (!sg.rowfmt) ents = 0;
     const int f = (int)(rc >> 32), p = (int)(rc & 0xFFFFFFFFull), cnt = f + p;
     unsigned long long incl = rc;  // inclusive prefix over rows
     for (int d = 1; d < 64; d <<= 1) {
@@ -753,8 +754,18 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
     const u4v w0 = t < sg.cap * 32 ? src[t] : u4v{0, 0, 0, 0};
     unsigned long long off;
     if (kSelf) {
+        // s < kFusedMaxSegs: a fixed number of predicated loads, all issued
+        // before the first is waited for (a loop to s waited for each in
+        // turn: up to 8 memory round trips for the last segments)
+        uint64_t part[kFusedMaxSegs / 256];
+#pragma unroll
+        for (int k = 0; k < kFusedMaxSegs / 256; ++k) {
+            const int j = t + 256 * k;
+            part[k] = j < s ? sg.cnt[j] : 0;
+        }
         unsigned long long x = 0;
-        for (int j = t; j < s; j += 256) x += sg.cnt[j];
+#pragma unroll
+        for (int k = 0; k < kFusedMaxSegs / 256; ++k) x += part[k];
         off = block_sum(x, sh_u);
     } else {
         off = sg.off[s];
@@ -822,10 +833,26 @@ __global__ __launch_bounds__(256) void enc_place(int S, int n, int R, int G,
         dst[t] = w0;
         if (has_ent) wl[t] = w0;
     }
-    for (int e = t + 256; e < np * 32; e += 256) {
-        const u4v v = src[e];
-        dst[e] = v;
-        if (has_ent) wl[e] = v;
+    // the rest of the words (np <= kMaxSegTiles): every load issued before
+    // the first store, which waits for them once (a load-store loop waited
+    // a memory round trip per 256 chunks)
+    // (unconditional loads: lanes past the words read chunk 0, one cache
+    // line for the whole workgroup; a predicated load became a branch with
+    // its own wait)
+    constexpr int kRest = kMaxSegTiles * 32 / 256 - 1;
+    u4v rest[kRest];
+#pragma unroll
+    for (int k = 0; k < kRest; ++k) {
+        const int e = t + 256 * (k + 1);
+        rest[k] = src[e < np * 32 ? e : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < kRest; ++k) {
+        const int e = t + 256 * (k + 1);
+        if (e < np * 32) {
+            dst[e] = rest[k];
+            if (has_ent) wl[e] = rest[k];
+        }
     }
     if (has_ent)
         place_entries(np, colp, popp, reinterpret_cast<const uint64_t *>(wl), enc.row_ent, ent_dst);
