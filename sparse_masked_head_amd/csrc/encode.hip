@@ -69,7 +69,12 @@ enum LoadMode { kAligned64 = 0, kAligned16 = 1, kDwords = 2 };
 // of the strip (strip row 0 = mask row row0), bytes 16*(t & 31) .. +15 of
 // the window (tile (t & 31) >> 2, columns 16*(t & 3) .. +15 of it).  Each
 // wavefront instruction reads two contiguous 512-byte row pieces.  Tiles
-// at or past n, and elements outside the S x S mask, read as zero.
+// at or past n, and elements outside the S x S mask, hold no mask bytes:
+// the aligned modes still load such a piece (from column 0, and the last
+// row, of the strip: in bounds) and window_valid() tells which pieces to
+// zero when they are used; kDwords loads them as zero.  (A load under a
+// per-lane condition became a branch, and the compiler then waited for
+// every outstanding load, the next window's among them, before using any.)
 template <int kMode>
 __device__ __forceinline__ void load_window(u4v (&v)[8], const uint8_t *strip,
                                             int S, int n, int row0, int J0, int t) {
@@ -81,10 +86,10 @@ __device__ __forceinline__ void load_window(u4v (&v)[8], const uint8_t *strip,
         const uint8_t *p = strip + (size_t)(8 * k + r0) * S + col;
         const bool row_ok = row0 + 8 * k + r0 < S;
         if (kMode == kAligned64) {
-            v[k] = ok ? *reinterpret_cast<const u4v *>(p) : u4v{0, 0, 0, 0};
+            v[k] = *reinterpret_cast<const u4v *>(ok ? p : strip + (size_t)(8 * k + r0) * S);
         } else if (kMode == kAligned16) {
-            v[k] = ok && row_ok && col < S ? *reinterpret_cast<const u4v *>(p)
-                                           : u4v{0, 0, 0, 0};
+            const size_t rr = (size_t)min(8 * k + r0, S - 1 - row0);
+            v[k] = *reinterpret_cast<const u4v *>(strip + rr * S + (ok && col < S ? col : 0));
         } else {
             uint32_t wd[4] = {0, 0, 0, 0};
             if (ok && row_ok && col < S) {
@@ -107,6 +112,24 @@ __device__ __forceinline__ void load_window(u4v (&v)[8], const uint8_t *strip,
             v[k] = u4v{wd[0], wd[1], wd[2], wd[3]};
         }
     }
+}
+
+// Bit k: piece k of load_window holds mask bytes (always, for kDwords,
+// whose loads already read zero outside the mask).
+template <int kMode>
+__device__ __forceinline__ uint32_t window_valid(int S, int n, int row0, int J0, int t) {
+    if (kMode == kDwords) return 0xFFu;
+    const int r0 = t >> 5, c = t & 31;
+    const bool ok = J0 + (c >> 2) < n;
+    const int col = 64 * J0 + 16 * c;
+    uint32_t vm = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const bool row_ok = row0 + 8 * k + r0 < S;
+        const bool valid = ok && (kMode == kAligned64 || (row_ok && col < S));
+        vm |= (uint32_t)valid << k;
+    }
+    return vm;
 }
 
 template <typename T> __device__ inline T block_sum(T x, T *sh) {
@@ -261,18 +284,18 @@ __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mas
         uint8_t *wb = reinterpret_cast<uint8_t *>(&lw[0][0]);
         const int r0 = t >> 5, c = t & 31, jj = c >> 2, quarter = c & 3;
         uint32_t any_rows = 0;  // bit k: row 8k + r0 has a valid element
-        u4v cur[8], nxt[8];
-        load_window<kMode>(cur, strip, S, n, 64 * I, kWin * w0, t);
-        for (int wi = 0; wi < nwin; ++wi) {
-            if (wi + 1 < nwin)
-                load_window<kMode>(nxt, strip, S, n, 64 * I, kWin * (w0 + wi + 1), t);
+        // one window's words and counts (window wi of the segment, its
+        // pieces in v; pieces holding no mask bytes count as zero)
+        auto process = [&](const u4v(&v)[8], int wi) __attribute__((always_inline)) {
+            const uint32_t vm = window_valid<kMode>(S, n, 64 * I, kWin * (w0 + wi), t);
             uint8_t *tb = wb + (size_t)(kWin * wi + jj) * 512;
             int cnt = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 // inner tiles (k, 2*quarter) and (k, 2*quarter+1), their row r0
-                const uint32_t b0 = row_bits8(cur[k][0], cur[k][1]);
-                const uint32_t b1 = row_bits8(cur[k][2], cur[k][3]);
+                const uint32_t keep = 0u - ((vm >> k) & 1u);
+                const uint32_t b0 = row_bits8(v[k][0], v[k][1]) & keep;
+                const uint32_t b1 = row_bits8(v[k][2], v[k][3]) & keep;
                 tb[(k * 8 + 2 * quarter) * 8 + r0] = (uint8_t)b0;
                 tb[(k * 8 + 2 * quarter + 1) * 8 + r0] = (uint8_t)b1;
                 cnt += __popc(b0) + __popc(b1);
@@ -284,8 +307,24 @@ __global__ __launch_bounds__(256) void enc_strip(const uint8_t *__restrict__ mas
             cnt += __shfl_xor(cnt, 2);
             cnt += __shfl_xor(cnt, 32);
             if (lane < 32 && quarter == 0) wsum[kWin * wi + jj][w] = cnt;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
+        };
+        // Two register sets, used in turn (the loop unrolled by two): the
+        // next window's loads are issued before this one is processed, and
+        // every path issues the same loads (past the last window, the last
+        // one again: cache hits), so the compiler's waits count exactly the
+        // loads still in flight.  (With one set copied from the other, the
+        // wait at the top of the loop covered the next window's loads too.)
+        u4v va[8], vb[8];
+        auto win_at = [&](int wi) __attribute__((always_inline)) {
+            return kWin * (w0 + min(wi, nwin - 1));
+        };
+        load_window<kMode>(va, strip, S, n, 64 * I, win_at(0), t);
+        for (int wi = 0; wi < nwin; wi += 2) {
+            load_window<kMode>(vb, strip, S, n, 64 * I, win_at(wi + 1), t);
+            process(va, wi);
+            if (wi + 1 >= nwin) break;
+            load_window<kMode>(va, strip, S, n, 64 * I, win_at(wi + 2), t);
+            process(vb, wi + 1);
         }
         // query rows covered in this segment: OR over the 32 lanes sharing r0
         uint32_t a = any_rows;
@@ -456,7 +495,8 @@ template <int kRows, int kBins>
 __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
                           smh_mask_enc enc, bool offsets) {
     constexpr int kH = kBins > 0 ? kBins : 1;
-    __shared__ uint32_t rowc[kRows];  // full << 16 | partial (each <= n <= 2048)
+    // full << 16 | partial (each <= n <= 2048); without bins, then the rank keys
+    __shared__ __attribute__((aligned(16))) uint32_t rowc[kRows];
     __shared__ int above[kH];         // histogram, then rows with a larger count
     __shared__ int seen[kH];          // rows of earlier blocks per count
     __shared__ unsigned long long sh_u[4];
@@ -537,14 +577,24 @@ __device__ void scan_body(int S, int n, int R, int G, SegPlan plan, Seg sg,
     const long long spnz = (long long)((uint64_t)spw & kSpLow);
     auto cnt_of = [&](int J) { return (int)((rowc[J] >> 16) + (rowc[J] & 0xFFFFu)); };
     if constexpr (kBins == 0) {  // (every row's count is in LDS: barriers above)
+        // one key per row, count << 16 | (65535 - row) (row < kRows <= 65536):
+        // a row's rank is the number of rows with a larger key (more tiles,
+        // or as many and earlier), one unsigned compare per pair; the keys
+        // replace the thread's own rows' counts, and are read four at a
+        // time (broadcast LDS reads)
+        for (int I = r_lo; I < r_hi; ++I)
+            rowc[I] = ((uint32_t)cnt_of(I) << 16) | (0xFFFFu - (uint32_t)I);
+        __syncthreads();
+        const int R4 = R & ~3;
         for (int J = t; J < R; J += 256) {
-            const int cj = cnt_of(J);
+            const uint32_t kj = rowc[J];
             int rank = 0;
-#pragma unroll 8
-            for (int J2 = 0; J2 < R; ++J2) {
-                const int c2 = cnt_of(J2);
-                rank += (c2 > cj) || (c2 == cj && J2 < J);
+#pragma unroll 4
+            for (int J2 = 0; J2 < R4; J2 += 4) {
+                const uint4 k4 = *reinterpret_cast<const uint4 *>(&rowc[J2]);
+                rank += (int)(k4.x > kj) + (int)(k4.y > kj) + (int)(k4.z > kj) + (int)(k4.w > kj);
             }
+            for (int J2 = R4; J2 < R; ++J2) rank += (int)(rowc[J2] > kj);
             enc.row_order[rank] = J;
         }
     } else {
@@ -636,11 +686,18 @@ __device__ void scan_small(int S, int n, int R, int G, SegPlan plan, Seg sg,
     }
     const int nsp = (int)((uint64_t)spw >> kSpShift);
     const long long spnz = (long long)((uint64_t)spw & kSpLow);
-    // schedule rank: rows with more stored tiles, then rows before with as many
+    // schedule rank: rows with more stored tiles, then rows before with as
+    // many; as in scan_body, on keys count << 16 | (65535 - row) in LDS
+    // (lanes past R: key 0, never larger), read four at a time.  One
+    // wavefront: its LDS write is done before its reads.
+    __shared__ __attribute__((aligned(16))) uint32_t keys[64];
+    const uint32_t key = lane < R ? ((uint32_t)cnt << 16) | (0xFFFFu - (uint32_t)lane) : 0u;
+    keys[lane] = key;
     int rank = 0;
-    for (int J2 = 0; J2 < R; ++J2) {  // (a scalar read of lane J2 per row)
-        const int c2 = __builtin_amdgcn_readlane(cnt, J2);
-        rank += (c2 > cnt) || (c2 == cnt && J2 < lane);
+#pragma unroll
+    for (int J2 = 0; J2 < 64; J2 += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4 *>(&keys[J2]);
+        rank += (int)(k4.x > key) + (int)(k4.y > key) + (int)(k4.z > key) + (int)(k4.w > key);
     }
     if (lane < R) {
         enc.full_row_ptr[lane] = (int32_t)(run >> 32);
@@ -694,17 +751,30 @@ __device__ void place_entries(int np, int colp, int popp, const uint64_t *words,
     __syncthreads();  // also: ent_dst from wavefront 0, the words
     uint32_t *dst = row_ent + ent_dst[q];
     const int jc = lane >> 3, c = lane & 7;
-    for (int l = 0; l < np; ++l) {
-        const int J = col_t[l];
-        if (J < 0) continue;  // (uniform in the workgroup)
-        const uint64_t wa = words[64 * (size_t)l + 16 * q + jc];
-        const uint64_t wb = words[64 * (size_t)l + 16 * q + 8 + jc];
+    // lane l holds tile l's column; the sparse tiles are the set bits of
+    // `sp`, visited in order with the next one's words read (LDS) before
+    // the current one is placed
+    const int myJ = lane < np ? col_t[lane] : -1;
+    uint64_t sp = __builtin_amdgcn_ballot_w64(myJ >= 0);
+    if (sp == 0) return;
+    int l = __builtin_ctzll(sp);
+    uint64_t wa = words[64 * (size_t)l + 16 * q + jc];
+    uint64_t wb = words[64 * (size_t)l + 16 * q + 8 + jc];
+    while (sp) {
+        const int J = __builtin_amdgcn_readlane(myJ, l);
+        sp &= sp - 1;
+        const int ln = sp ? __builtin_ctzll(sp) : l;
+        const uint64_t na = words[64 * (size_t)ln + 16 * q + jc];
+        const uint64_t nb = words[64 * (size_t)ln + 16 * q + 8 + jc];
         const uint32_t rows = column_rows(wa, c) | (column_rows(wb, c) << 8);
         const uint64_t live = __builtin_amdgcn_ballot_w64(rows != 0);
         const int rank = (int)__builtin_amdgcn_mbcnt_hi(
             (uint32_t)(live >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)live, 0u));
         if (rows) dst[rank] = (rows << 16) | (64u * (uint32_t)J + (uint32_t)lane);
         dst += __popcll(live);
+        wa = na;
+        wb = nb;
+        l = ln;
     }
 }
 
@@ -712,7 +782,9 @@ __device__ void place_entries(int np, int colp, int popp, const uint64_t *words,
 // it is dispatched with the first placements instead of after them) and
 // workgroup s + 1 places segment s, adding up the tile counts of the
 // segments before it.  Otherwise workgroup s places segment s with the
-// offsets from enc_scan.  The segment's own columns and
+// offsets from enc_scan.  (Taking segments from both ends in turn, so that
+// the heavy last rows of a causal mask start early, measured slower on the
+// 16k mask: 79.6 against 76.9 us.)  The segment's own columns and
 // first words are loaded together with its offsets (they do not depend on
 // them), so a small segment is placed after one memory round trip.
 template <bool kSelf>
