@@ -16,6 +16,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TO
     __shared__ __attribute__((aligned(16))) char k0[Lds<D>::KBUF], k1[Lds<D>::KBUF];
     __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
     __shared__ HybLds hl;
+    __shared__ __attribute__((aligned(16))) uint32_t e0[4 * 64], e1[4 * 64];
     const Slot sl = slot_at(a, (int)blockIdx.x);
     // the block-wise path's Q rows, requested before the row summary so that
     // they arrive during its round trip (under the row-wise choice the
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void auto_fwd(FwdArgs<TIn, TO
     // need the summary)
     const RowInfo ri = load_row_info(a, sl.row);
     if (device_choice<D>(a, ri) == 2) {
-        const TileBufs<D> bufs{{k0, k1}, {v0, v1}};
+        const TileBufs<D> bufs{{k0, k1}, {v0, v1}, {e0, e1}};
         blockwise_row<D, TIn, TOut>(a, bufs, sl.row, sl.I, sl.bh, ri, qf, hl);
     } else {
         // each wavefront's slice is one of the tile buffers

@@ -10,7 +10,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void blockwise_fwd(FwdArgs<TI
     __shared__ __attribute__((aligned(16))) char k0[Lds<D>::KBUF], k1[Lds<D>::KBUF];
     __shared__ __attribute__((aligned(16))) char v0[Lds<D>::VBUF], v1[Lds<D>::VBUF];
     __shared__ HybLds hl;
-    const TileBufs<D> bufs{{k0, k1}, {v0, v1}};
+    __shared__ __attribute__((aligned(16))) uint32_t e0[4 * 64], e1[4 * 64];
+    const TileBufs<D> bufs{{k0, k1}, {v0, v1}, {e0, e1}};
     // heavy rows first, heads in sequence per XCD (slot_at)
     const Slot sl = slot_at(a, (int)blockIdx.x);
     typename Frag<TIn>::type qf[D / 32];

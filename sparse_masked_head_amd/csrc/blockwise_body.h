@@ -181,6 +181,13 @@ template <int N> __device__ __attribute__((always_inline)) inline void wait_load
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// The same as an assembly instruction, which the compiler keeps whatever
+// it sees depend on the loads (it may drop the builtin where it sees no
+// use of their results, e.g. before reads in assembly).
+template <int N> __device__ __attribute__((always_inline)) inline void wait_loads_but_asm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
 // Wait for this wave's outstanding LDS operations (global loads are not
 // waited for): vmcnt and expcnt at their maxima, lgkmcnt 0.
 __device__ __attribute__((always_inline)) inline void wait_lds() {
@@ -495,6 +502,7 @@ __device__ inline int split_partials(const FwdArgs<TIn, TOut> &a, const RowInfo 
 // those reads wait for the loads.
 template <int D> struct TileBufs {
     char *k[2], *v[2];
+    uint32_t *e[2];  // gather path: entry rings of chunk parity 0, 1 (64 per wavefront)
 };
 
 // This lane's Q rows as the B operand of S^T = K Q^T for outer-tile row I
@@ -533,11 +541,18 @@ __device__ __attribute__((always_inline)) inline void load_q_frags(
 // in the tile buffers K_p and V_p, wavefront w's at 16 rows * w, so that
 // the slots being read and the slots being filled are different LDS
 // objects and the compiler does not make the reads wait for the loads.
-// Pipeline, at chunk c: the entries of chunk c + 2 are requested (lane l
-// holds entry l % 16), chunk c + 1's K and V rows are requested (their keys
-// taken from its entry register with ds_bpermute), then chunk c is
-// computed.  Loads past the list re-read its last entry (or key 0), so
-// every wait counts the same loads.
+// A chunk's entries come into a per-wavefront LDS ring by global_load_lds
+// as well (rings of chunk parity p in separate LDS arrays E_p), and the
+// keys and row sets are read from there: with every load of the loop an
+// LDS DMA, the compiler counts their completion exactly (an entry load
+// into registers among the DMAs made it wait for all of them before each
+// chunk's first use of its entries, so that only one chunk's rows were in
+// flight at a time).
+// Pipeline, at chunk c: wait for the entries of chunk c + 1 (requested
+// before chunk c's rows), read them, request the entries of chunk c + 2
+// (into chunk c's ring) and chunk c + 1's K and V rows, wait for chunk c's
+// rows and compute chunk c.  Loads past the list re-read its last entry
+// (or key 0), so every wait counts the same loads.
 
 template <typename TIn> struct Frag4;
 template <> struct Frag4<_Float16> {
@@ -556,6 +571,7 @@ template <> struct Frag4<__bf16> {
 template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void gather_stream(
     RowState<D> &rs, char *kslot0, char *kslot1, char *vslot0, char *vslot1,
+    uint32_t *ering0, uint32_t *ering1,
     const uint32_t *__restrict__ ents, int ne, const typename Frag<TIn>::type (&qf)[D / 32],
     const TIn *__restrict__ Kh, const TIn *__restrict__ Vh, float c, int S,
     const KOff<D> &ko, const VOff<D> &vo) {
@@ -567,38 +583,77 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
     constexpr int RPI = 1024 / (2 * D);  // rows per 1 KB load instruction
     constexpr int NI = 16 / RPI;         // load instructions per chunk, K and V each
     const int nch = (ne + 15) >> 4;
-    // the key of entry ei of a chunk of n entries, clamped into the head's
-    // rows; past the chunk: key 0
-    auto key_of = [&](int ei, int n, uint32_t e) __attribute__((always_inline)) {
-        return ei < n ? min((int)(e & 0xFFFFu), S - 1) : 0;
+    // entries 16 ci .. 16 ci + 63 into ring er (lane l's to er[l]; the
+    // chunk's 16 are used); past the list: its last entry
+    auto load_e = [&](int ci, uint32_t *er) __attribute__((always_inline)) {
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(ents + min(16 * ci + lane, ne - 1)),
+                                         (lds_void_t *)er, 4, 0, 0);
     };
-    auto load_e = [&](int ci) __attribute__((always_inline)) {
-        return ents[min(16 * ci + lq, ne - 1)];
+    // chunk ci's keys from its ring: the lane's key for each row load, and
+    // its valid score slots (bit i: entry 4g + i is in the chunk and its row
+    // set holds the lane's query row)
+    struct Keys {
+        uint32_t key[NI];
+        uint32_t ok;
     };
-    // chunk ci's rows into slots ks, vs; returns the lane's valid score
-    // slots (bit i: entry 4g + i is in the chunk and its row set holds the
-    // lane's query row)
-    auto issue = [&](int ci, uint32_t e, char *ks, char *vs) __attribute__((always_inline)) {
-        auto ent = [&](int idx) __attribute__((always_inline)) {
-            return (uint32_t)__builtin_amdgcn_ds_bpermute(idx << 2, (int)e);
-        };
+    // The ring reads are one assembly block that waits for them (and for
+    // nothing else) at its end: as plain reads, the compiler made them wait
+    // for every LDS load in flight (it does not tell the ring from the
+    // slots those fill), and, read only where the lane's row is in the
+    // chunk, each became a branch with a wait of its own.  The caller has
+    // waited for the ring's own load.  Every lane reads: entry rr of the
+    // lane's row load i (RPI rows apart) and entries 4g .. 4g + 3.
+    auto read_keys = [&](int ci, const uint32_t *er) __attribute__((always_inline)) {
+        Keys k;
         const int n = min(16, ne - 16 * ci);
+        const uint32_t rb = (uint32_t)(uintptr_t)(lds_void_t *)(er + lane / L::CPR);
+        const uint32_t ob = (uint32_t)(uintptr_t)(lds_void_t *)(er + 4 * g);
+        uint32_t e[NI];
+        u4_t e4;
+        static_assert(NI == 4 || NI == 2, "row loads per chunk");
+        if constexpr (NI == 4) {
+            asm volatile(
+                "ds_read_b32 %0, %5\n\t"
+                "ds_read_b32 %1, %5 offset:%c7\n\t"
+                "ds_read_b32 %2, %5 offset:%c8\n\t"
+                "ds_read_b32 %3, %5 offset:%c9\n\t"
+                "ds_read_b128 %4, %6\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(e[0]), "=&v"(e[1]), "=&v"(e[2]), "=&v"(e[3]), "=&v"(e4)
+                : "v"(rb), "v"(ob), "i"(4 * RPI), "i"(8 * RPI), "i"(12 * RPI));
+        } else {
+            asm volatile(
+                "ds_read_b32 %0, %3\n\t"
+                "ds_read_b32 %1, %3 offset:%c5\n\t"
+                "ds_read_b128 %2, %4\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(e[0]), "=&v"(e[1]), "=&v"(e4)
+                : "v"(rb), "v"(ob), "i"(4 * RPI));
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int rr = RPI * i + lane / L::CPR;
+            // clamped into the head's rows; past the chunk: key 0
+            k.key[i] = rr < n ? (uint32_t)min((int)(e[i] & 0xFFFFu), S - 1) : 0u;
+        }
+        const uint32_t ev[4] = {e4[0], e4[1], e4[2], e4[3]};
+        k.ok = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            k.ok |= (uint32_t)(4 * g + i < n && ((ev[i] >> (16 + lq)) & 1u)) << i;
+        return k;
+    };
+    // chunk rows into slots ks, vs (whole rows per load instruction)
+    auto issue = [&](const Keys &k, char *ks, char *vs) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int rr = RPI * i + lane / L::CPR, cp = lane % L::CPR;
-            const size_t off = (size_t)key_of(rr, n, ent(rr)) * D + 8 * (cp ^ L::sw(rr));
+            const size_t off = (size_t)k.key[i] * D + 8 * (cp ^ L::sw(rr));
             __builtin_amdgcn_global_load_lds((gbl_void_t *)(Kh + off),
                                              (lds_void_t *)(ks + 1024 * i), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((gbl_void_t *)(Vh + off),
                                              (lds_void_t *)(vs + 1024 * i), 16, 0, 0);
         }
-        uint32_t ok = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t e2 = ent(4 * g + i);
-            ok |= (uint32_t)(4 * g + i < n && ((e2 >> (16 + lq)) & 1u)) << i;
-        }
-        return ok;
     };
     auto compute = [&](const char *ks, const char *vs, uint32_t ok) __attribute__((always_inline)) {
         f4_t sc[1];
@@ -628,26 +683,34 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
         }
     };
     if (nch == 0) return;
-    uint32_t ea = load_e(0), eb = load_e(1);
-    uint32_t oka = issue(0, ea, kslot0, vslot0), okb = 0;
-    // chunk ci: slots of parity ci & 1, valid bits `okc`; chunk ci + 1:
-    // entries in `en` (requested before chunk ci's rows, so that reading
-    // them does not wait for those rows), goes to the other slots (valid
-    // bits into `okn`); the entries of ci + 2 replace those of ci in `ef`.
-    // Loads issued after chunk ci's rows: the entries of ci + 2 and chunk
-    // ci + 1's rows, left in flight while chunk ci is computed.
-    auto iter = [&](int ci, uint32_t &ef, const uint32_t en, char *kc, char *vc, char *kn,
-                    char *vn, const uint32_t okc, uint32_t &okn) __attribute__((always_inline)) {
-        ef = load_e(ci + 2);
-        okn = issue(ci + 1, en, kn, vn);
-        wait_loads_but<2 * NI + 1>();
+    load_e(0, ering0);
+    load_e(1, ering1);
+    wait_loads_but_asm<1>();  // the entries of chunk 0 are in
+    uint32_t oka, okb = 0;
+    {
+        const Keys k0 = read_keys(0, ering0);
+        oka = k0.ok;
+        issue(k0, kslot0, vslot0);
+    }
+    // chunk ci: slots and ring of parity ci & 1 (ec, kc, vc), valid bits
+    // okc; chunk ci + 1: the other parity (en, kn, vn), valid bits to okn.
+    // Outstanding at the start: the entries of ci + 1, then chunk ci's 2NI
+    // row loads.
+    auto iter = [&](int ci, uint32_t *ec, const uint32_t *en, const char *kc, const char *vc,
+                    char *kn, char *vn, const uint32_t okc, uint32_t &okn) __attribute__((always_inline)) {
+        wait_loads_but_asm<2 * NI>();  // the entries of ci + 1 are in
+        const Keys k = read_keys(ci + 1, en);
+        okn = k.ok;
+        load_e(ci + 2, ec);  // chunk ci's ring was read in the previous step
+        issue(k, kn, vn);
+        wait_loads_but<2 * NI + 1>();  // chunk ci's rows are in
         asm volatile("" ::: "memory");
         compute(kc, vc, okc);
     };
     for (int ci = 0; ci < nch; ci += 2) {
-        iter(ci, ea, eb, kslot0, vslot0, kslot1, vslot1, oka, okb);
+        iter(ci, ering0, ering1, kslot0, vslot0, kslot1, vslot1, oka, okb);
         if (ci + 1 >= nch) break;
-        iter(ci + 1, eb, ea, kslot1, vslot1, kslot0, vslot0, okb, oka);
+        iter(ci + 1, ering1, ering0, kslot1, vslot1, kslot0, vslot0, okb, oka);
     }
     wait_loads();  // the loads past the list land before the slots are left
 }
@@ -848,8 +911,8 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
         const uint32_t *ents = a.rent + 256 * (size_t)ri.p0 + 64 * (size_t)w * ri.nP;
         const int ne = a.rcnt[4 * (size_t)row + w];
         gather_stream<D, TIn>(rs, bufs.k[0] + SLOT * w, bufs.k[1] + SLOT * w,
-                              bufs.v[0] + SLOT * w, bufs.v[1] + SLOT * w, ents, ne, qf,
-                              Kh, Vh, a.c, a.S, ko, vo);
+                              bufs.v[0] + SLOT * w, bufs.v[1] + SLOT * w, bufs.e[0] + 64 * w,
+                              bufs.e[1] + 64 * w, ents, ne, qf, Kh, Vh, a.c, a.S, ko, vo);
     }
 
     // epilogue: total l over the 4 lanes of this query
