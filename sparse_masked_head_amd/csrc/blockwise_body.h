@@ -572,9 +572,8 @@ template <int D, typename TIn>
 __device__ __attribute__((always_inline)) inline void gather_stream(
     RowState<D> &rs, char *kslot0, char *kslot1, char *vslot0, char *vslot1,
     uint32_t *ering0, uint32_t *ering1,
-    const uint32_t *__restrict__ ents, int ne, const typename Frag<TIn>::type (&qf)[D / 32],
-    const TIn *__restrict__ Kh, const TIn *__restrict__ Vh, float c, int S,
-    const KOff<D> &ko, const VOff<D> &vo) {
+    const char *ents, int ne, const typename Frag<TIn>::type (&qf)[D / 32],
+    const char *Kb, const char *Vb, float c, int S, const KOff<D> &ko, const VOff<D> &vo) {
     using F = Frag<TIn>;
     using F4 = Frag4<TIn>;
     using frag = typename F::type;
@@ -583,11 +582,15 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
     constexpr int RPI = 1024 / (2 * D);  // rows per 1 KB load instruction
     constexpr int NI = 16 / RPI;         // load instructions per chunk, K and V each
     const int nch = (ne + 15) >> 4;
+    // Addresses: the bases (entry list, K, V, slots, rings) are wave-uniform
+    // (scalar registers, the loads in the scalar-base form), each lane adds
+    // a 32-bit byte offset.
     // entries 16 ci .. 16 ci + 63 into ring er (lane l's to er[l]; the
     // chunk's 16 are used); past the list: its last entry
     auto load_e = [&](int ci, uint32_t *er) __attribute__((always_inline)) {
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(ents + min(16 * ci + lane, ne - 1)),
-                                         (lds_void_t *)er, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (gbl_void_t *)(ents + 4u * (uint32_t)min(16 * ci + lane, ne - 1)),
+            (lds_void_t *)er, 4, 0, 0);
     };
     // chunk ci's keys from its ring: the lane's key for each row load, and
     // its valid score slots (bit i: entry 4g + i is in the chunk and its row
@@ -648,10 +651,11 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int rr = RPI * i + lane / L::CPR, cp = lane % L::CPR;
-            const size_t off = (size_t)k.key[i] * D + 8 * (cp ^ L::sw(rr));
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(Kh + off),
+            // key < 65536, so key * D * 2 < 2^24
+            const uint32_t off = 2u * (k.key[i] * (uint32_t)D + 8u * (uint32_t)(cp ^ L::sw(rr)));
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(Kb + off),
                                              (lds_void_t *)(ks + 1024 * i), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(Vh + off),
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(Vb + off),
                                              (lds_void_t *)(vs + 1024 * i), 16, 0, 0);
         }
     };
@@ -908,11 +912,12 @@ __device__ __attribute__((always_inline)) inline void blockwise_row(
         // entries
         if (nT > 0) __syncthreads();
         constexpr int SLOT = 16 * D * 2;
-        const uint32_t *ents = a.rent + 256 * (size_t)ri.p0 + 64 * (size_t)w * ri.nP;
-        const int ne = a.rcnt[4 * (size_t)row + w];
-        gather_stream<D, TIn>(rs, bufs.k[0] + SLOT * w, bufs.k[1] + SLOT * w,
-                              bufs.v[0] + SLOT * w, bufs.v[1] + SLOT * w, bufs.e[0] + 64 * w,
-                              bufs.e[1] + 64 * w, ents, ne, qf, Kh, Vh, a.c, a.S, ko, vo);
+        const char *ents = reinterpret_cast<const char *>(
+            uniform_ptr(a.rent + 256 * (size_t)ri.p0 + 64 * (size_t)wu * ri.nP));
+        const int ne = __builtin_amdgcn_readfirstlane(a.rcnt[4 * (size_t)row + wu]);
+        gather_stream<D, TIn>(rs, bufs.k[0] + SLOT * wu, bufs.k[1] + SLOT * wu,
+                              bufs.v[0] + SLOT * wu, bufs.v[1] + SLOT * wu, bufs.e[0] + 64 * wu,
+                              bufs.e[1] + 64 * wu, ents, ne, qf, Kb, Vb, a.c, a.S, ko, vo);
     }
 
     // epilogue: total l over the 4 lanes of this query
