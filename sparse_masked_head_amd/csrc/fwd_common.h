@@ -207,6 +207,17 @@ template <typename T> __device__ inline float sum2(uint32_t pair, float acc) {
     return dot2<T>(pair, ones2<T>(), acc);
 }
 
+// Two fp32 values rounded (to nearest even) to T, packed (a in the low
+// half): one packed conversion instruction.
+template <typename T> __device__ inline uint32_t pack2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    const t2 v = __builtin_convertvector(f2{a, b}, t2);
+    uint32_t r;
+    __builtin_memcpy(&r, &v, 4);
+    return r;
+}
+
 // Four fp32 values to the output type, one store.
 template <typename T> __device__ inline void store4(T *p, f4_t x);
 template <> __device__ inline void store4<float>(float *p, f4_t x) {
