@@ -73,12 +73,12 @@ struct SelectCoef {
 SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
                                    double *t_blk) {
     // fitted on MI355X; fp16 and bf16 share coefficients
-    const SelectCoef k64 = {7.8545, 0.0014456, 1.8493e-4, 0.47247,
-                            1.6135e-4, 0.0011622, 0.41532, 1.6621,
-                            1.3022e-5, 6.2611e-5, 0.024697, 4.7474};
-    const SelectCoef k128 = {7.844, 0.0029088, 5.3013e-4, 0.74578,
-                             3.5921e-4, 0.002399, 0.46418, 3.2985,
-                             2.4037e-5, 2.2114e-4, 0.036547, 3.1329};
+    const SelectCoef k64 = {8.0248, 0.0013977, 2.3023e-4, 0.45568,
+                            1.7098e-4, 0.0011503, 0.3563, 1.6753,
+                            8.5026e-6, 6.2755e-5, 0.019472, 4.8561};
+    const SelectCoef k128 = {8.0277, 0.0028768, 5.045e-4, 0.73646,
+                             3.3023e-4, 0.0024028, 0.47397, 3.3185,
+                             1.4585e-5, 1.935e-4, 0.024057, 3.2402};
     const SelectCoef &k = in.d == 128 ? k128 : k64;
     const double tiles = (double)in.n_full + (double)in.n_partial;
     const double heads = (double)in.heads;
@@ -118,7 +118,7 @@ SMH_HD inline void select_costs_us(const SelectInput &in, double *t_row,
 
 // Row-wise is taken when its predicted time is below this fraction of the
 // block-wise one.  With the split critical path and per-kernel launch
-// costs the plain comparison loses 0.14% (d = 64) and 0.08% (d = 128) of
+// costs the plain comparison loses 0.16% (d = 64) and 0.03% (d = 128) of
 // the calibration sweep's total time to wrong picks (every pick within 3%
 // of the faster kernel on 170 and 172 of 180 points), so no margin is kept.
 constexpr double kRowMargin = 1.0;
