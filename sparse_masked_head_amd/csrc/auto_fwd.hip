@@ -47,7 +47,7 @@ hipError_t launch_d(const void *q, const void *k, const void *v, void *o,
     FwdArgs<TIn, TOut> a = make_args<TIn, TOut>(q, k, v, o, B, H, S, scale, enc);
     a.hybrid = hybrid_allowed(S, enc.n_ot);
     const long long slots = (long long)a.R * a.U;  // = n * B * H
-    a.use_order = slots > resident_workgroups(kern, 0);
+    a.use_order = slots > resident_workgroups<auto_fwd<D, TIn, TOut>>(0);
     hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(256), 0, stream, a);
     return hipGetLastError();
 }

@@ -270,28 +270,31 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Raise a kernel's dynamic-LDS limit once per device (the attribute is
+// Raise kernel Kern's dynamic-LDS limit once per device (the attribute is
 // per device; repeated calls are cheap but are kept out of the launch path
-// so that launches can be captured into graphs).
-template <typename Kernel>
-inline hipError_t ensure_lds_limit(Kernel kern, int bytes) {
+// so that launches can be captured into graphs).  The kernel is a template
+// argument so that each kernel has a cache of its own (instances of one
+// kernel template share a function type).
+template <auto Kern>
+inline hipError_t ensure_lds_limit(int bytes) {
     static std::atomic<int> done[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire) >= bytes)
         return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e == hipSuccess && dev >= 0 && dev < 64)
         done[dev].store(bytes, std::memory_order_release);
     return e;
 }
 
-// Workgroups of `kern` (256 threads, `lds` bytes of dynamic LDS) that the
-// current device holds at once; cached per kernel and device.
-template <typename Kernel>
-inline long long resident_workgroups(Kernel kern, int lds) {
+// Workgroups of kernel Kern (256 threads, `lds` bytes of dynamic LDS) that
+// the current device holds at once; cached per kernel and device (a
+// template argument, as for ensure_lds_limit).
+template <auto Kern>
+inline long long resident_workgroups(int lds) {
     static std::atomic<long long> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -299,7 +302,7 @@ inline long long resident_workgroups(Kernel kern, int lds) {
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(kern), 256, lds) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void *>(Kern), 256, lds) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
             hipSuccess)
         return 0;

@@ -399,7 +399,7 @@ template <int BT, int P, typename T>
 hipError_t launch_bt(const ProjArgs<T> &a, hipStream_t stream) {
     auto kern = out_proj<BT, P, T>;
     const int lds = proj_lds_bytes<BT>();
-    hipError_t e = ensure_lds_limit(kern, lds);
+    hipError_t e = ensure_lds_limit<out_proj<BT, P, T>>(lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(a.N / BT), (unsigned)((a.M + BT - 1) / BT));
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, a);
