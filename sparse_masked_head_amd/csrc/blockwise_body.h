@@ -506,7 +506,7 @@ __device__ inline int split_partials(const FwdArgs<TIn, TOut> &a, const RowInfo 
 // those reads wait for the loads.
 template <int D> struct TileBufs {
     char *k[2], *v[2];
-    uint32_t *e[2];  // gather path: entry rings of chunk parity 0, 1 (64 per wavefront)
+    uint32_t *e[2];  // gather path: entry rings of block parity 0, 1 (64 per wavefront)
 };
 
 // This lane's Q rows as the B operand of S^T = K Q^T for outer-tile row I
@@ -545,18 +545,18 @@ __device__ __attribute__((always_inline)) inline void load_q_frags(
 // in the tile buffers K_p and V_p, wavefront w's at 16 rows * w, so that
 // the slots being read and the slots being filled are different LDS
 // objects and the compiler does not make the reads wait for the loads.
-// A chunk's entries come into a per-wavefront LDS ring by global_load_lds
-// as well (rings of chunk parity p in separate LDS arrays E_p), and the
-// keys and row sets are read from there: with every load of the loop an
-// LDS DMA, the compiler counts their completion exactly (an entry load
-// into registers among the DMAs made it wait for all of them before each
-// chunk's first use of its entries, so that only one chunk's rows were in
-// flight at a time).
-// Pipeline, at chunk c: wait for the entries of chunk c + 1 (requested
-// before chunk c's rows), read them, request the entries of chunk c + 2
-// (into chunk c's ring) and chunk c + 1's K and V rows, wait for chunk c's
-// rows and compute chunk c.  Loads past the list re-read its last entry
-// (or key 0), so every wait counts the same loads.
+// The entries come into per-wavefront LDS rings by global_load_lds as
+// well, 64 at a time (an entry block: four chunks), blocks of parity p in
+// the separate LDS array E_p, and the keys and row sets are read from
+// there: with every load of the loop an LDS DMA, the compiler counts their
+// completion exactly (an entry load into registers among the DMAs made it
+// wait for all of them before each chunk's first use of its entries, so
+// that only one chunk's rows were in flight at a time).
+// Pipeline, at chunk c: read the keys of chunk c + 1, request its K and V
+// rows, wait for chunk c's rows and compute chunk c; an entry block is
+// requested four chunks before its first chunk's keys are read, so that
+// only the rows' round trips are waited for.  Loads past the list re-read
+// its last entry (or key 0), so every wait counts the same loads.
 
 template <typename TIn> struct Frag4;
 template <> struct Frag4<_Float16> {
@@ -589,11 +589,12 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
     // Addresses: the bases (entry list, K, V, slots, rings) are wave-uniform
     // (scalar registers, the loads in the scalar-base form), each lane adds
     // a 32-bit byte offset.
-    // entries 16 ci .. 16 ci + 63 into ring er (lane l's to er[l]; the
-    // chunk's 16 are used); past the list: its last entry
-    auto load_e = [&](int ci, uint32_t *er) __attribute__((always_inline)) {
+    // entry block b (entries 64 b .. 64 b + 63, the entries of chunks
+    // 4 b .. 4 b + 3) into ring er (lane l's to er[l]); past the list: its
+    // last entry
+    auto load_eb = [&](int b, uint32_t *er) __attribute__((always_inline)) {
         __builtin_amdgcn_global_load_lds(
-            (gbl_void_t *)(ents + 4u * (uint32_t)min(16 * ci + lane, ne - 1)),
+            (gbl_void_t *)(ents + 4u * (uint32_t)min(64 * b + lane, ne - 1)),
             (lds_void_t *)er, 4, 0, 0);
     };
     // chunk ci's keys from its ring: the lane's key for each row load, and
@@ -613,8 +614,9 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
     auto read_keys = [&](int ci, const uint32_t *er) __attribute__((always_inline)) {
         Keys k;
         const int n = min(16, ne - 16 * ci);
-        const uint32_t rb = (uint32_t)(uintptr_t)(lds_void_t *)(er + lane / L::CPR);
-        const uint32_t ob = (uint32_t)(uintptr_t)(lds_void_t *)(er + 4 * g);
+        const uint32_t *ec = er + 16 * (ci & 3);  // the chunk's 16 entries of its block
+        const uint32_t rb = (uint32_t)(uintptr_t)(lds_void_t *)(ec + lane / L::CPR);
+        const uint32_t ob = (uint32_t)(uintptr_t)(lds_void_t *)(ec + 4 * g);
         uint32_t e[NI];
         u4_t e4;
         static_assert(NI == 4 || NI == 2, "row loads per chunk");
@@ -691,34 +693,46 @@ __device__ __attribute__((always_inline)) inline void gather_stream(
         }
     };
     if (nch == 0) return;
-    load_e(0, ering0);
-    load_e(1, ering1);
-    wait_loads_but_asm<1>();  // the entries of chunk 0 are in
+    load_eb(0, ering0);
+    load_eb(1, ering1);
+    wait_loads_but_asm<1>();  // entry block 0 is in
     uint32_t oka, okb = 0;
     {
         const Keys k0 = read_keys(0, ering0);
         oka = k0.ok;
         issue(k0, kslot0, vslot0);
     }
-    // chunk ci: slots and ring of parity ci & 1 (ec, kc, vc), valid bits
-    // okc; chunk ci + 1: the other parity (en, kn, vn), valid bits to okn.
-    // Outstanding at the start: the entries of ci + 1, then chunk ci's 2NI
-    // row loads.
-    auto iter = [&](int ci, uint32_t *ec, const uint32_t *en, const char *kc, const char *vc,
-                    char *kn, char *vn, const uint32_t okc, uint32_t &okn) __attribute__((always_inline)) {
-        wait_loads_but_asm<2 * NI>();  // the entries of ci + 1 are in
-        const Keys k = read_keys(ci + 1, en);
+    // Step ci (P = ci % 4, a compile-time constant): read the keys of chunk
+    // j = ci + 1 from its block's ring and request its rows (slots of parity
+    // j & 1: kn, vn; valid bits to okn), wait for chunk ci's rows and compute
+    // chunk ci (slots kc, vc, valid bits okc).  When j starts entry block
+    // b = j / 4 (P == 3), wait for that block, requested four chunks
+    // earlier (after it: the 2NI row loads of chunks j - 4 .. j - 1), and
+    // request block b + 1 into the other ring, whose block b - 1 had its
+    // last keys read in the previous step.  So an entry block is in flight
+    // for four steps and a step waits for memory only for its own rows.
+    auto iter = [&](int ci, auto pc, const char *kc, const char *vc, char *kn, char *vn,
+                    const uint32_t okc, uint32_t &okn) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        const int j = ci + 1, b = j >> 2;
+        if constexpr (P == 3) wait_loads_but_asm<8 * NI>();  // entry block b is in
+        const Keys k = read_keys(j, (b & 1) ? ering1 : ering0);
         okn = k.ok;
-        load_e(ci + 2, ec);  // chunk ci's ring was read in the previous step
+        if constexpr (P == 3) load_eb(b + 1, (b & 1) ? ering0 : ering1);
         issue(k, kn, vn);
-        wait_loads_but<2 * NI + 1>();  // chunk ci's rows are in
+        wait_loads_but<2 * NI + (P == 3 ? 1 : 0)>();  // chunk ci's rows are in
         asm volatile("" ::: "memory");
         compute(kc, vc, okc);
     };
-    for (int ci = 0; ci < nch; ci += 2) {
-        iter(ci, ering0, ering1, kslot0, vslot0, kslot1, vslot1, oka, okb);
+    using std::integral_constant;
+    for (int ci = 0; ci < nch; ci += 4) {
+        iter(ci, integral_constant<int, 0>(), kslot0, vslot0, kslot1, vslot1, oka, okb);
         if (ci + 1 >= nch) break;
-        iter(ci + 1, ering1, ering0, kslot1, vslot1, kslot0, vslot0, okb, oka);
+        iter(ci + 1, integral_constant<int, 1>(), kslot1, vslot1, kslot0, vslot0, okb, oka);
+        if (ci + 2 >= nch) break;
+        iter(ci + 2, integral_constant<int, 2>(), kslot0, vslot0, kslot1, vslot1, oka, okb);
+        if (ci + 3 >= nch) break;
+        iter(ci + 3, integral_constant<int, 3>(), kslot1, vslot1, kslot0, vslot0, okb, oka);
     }
     wait_loads();  // the loads past the list land before the slots are left
 }
