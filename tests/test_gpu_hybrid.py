@@ -54,16 +54,21 @@ def threshold_mask(S=512, seed=3):
     return m
 
 
+ENTRY_TARGETS = [0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 80, 130,
+                 63, 64, 65, 0, 127, 128, 129, 1, 192, 193, 2, 3]
+
+
 def entry_count_mask(S=1024, seed=21):
-    """Outer-tile rows 1-3: a full diagonal tile (the tile path runs first),
+    """Outer-tile rows 1-6: a full diagonal tile (the tile path runs first),
     and per 16-row group a set number of row-wise entries (distinct keys
-    two of its rows see, overlapping, in sparse tiles 8-15): 0, 1, 15, 16,
-    17, 31, 32, 33, 48, 49, 80, 130, so that a wavefront's entry list is
-    empty, ends inside, at and just past the 16-entry chunk boundaries, and
-    runs for many chunks."""
+    two of its rows see, overlapping, in sparse tiles 8-15): ENTRY_TARGETS,
+    so that a wavefront's entry list is empty, ends inside, at and just
+    past the 16-entry chunk boundaries and the 64-entry block boundaries
+    (entries are fetched four chunks at a time), and runs for many
+    chunks."""
     rng = np.random.default_rng(seed)
     m = np.zeros((S, S), bool)
-    targets = [0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 80, 130]
+    targets = ENTRY_TARGETS
     cols = np.arange(8 * 64, 16 * 64)
     for idx, n_ent in enumerate(targets):
         I, q = 1 + idx // 4, idx % 4
@@ -91,8 +96,8 @@ CASES = [  # (name, B, H, S, d, dtype, mask builder)
     ("threshold tiles d128", 1, 2, 512, 128, "bf16", threshold_mask),
     ("0.1% random", 1, 4, 4096, 64, "f16",
      lambda: mask_family("sparse_random", 4096, seed=6)),
-    ("entry counts at chunk boundaries", 1, 2, 1024, 64, "f16", entry_count_mask),
-    ("entry counts at chunk boundaries d128", 2, 1, 1024, 128, "bf16", entry_count_mask),
+    ("entry counts at chunk and block boundaries", 1, 2, 1024, 64, "f16", entry_count_mask),
+    ("entry counts at chunk and block boundaries d128", 2, 1, 1024, 128, "bf16", entry_count_mask),
 ]
 
 
@@ -126,12 +131,12 @@ def test_mixed_tiles_whole_output(case, kernel):
 
 
 def test_entry_count_mask_counts():
-    """The chunk-boundary mask has the intended row-wise entry counts per
+    """The chunk- and block-boundary mask has the intended entry counts per
     16-row group (oracle's entry builder; no GPU)."""
     from oracle.encode import row_entries
     ent = row_entries(entry_count_mask(), THETA)
-    counts = [len(ent[(I, q)]) for I in (1, 2, 3) for q in range(4)]
-    assert counts == [0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 80, 130], counts
+    counts = [len(ent[(I, q)]) for I in range(1, 7) for q in range(4)]
+    assert counts == ENTRY_TARGETS, counts
 
 
 def test_threshold_rows_exact():
