@@ -98,6 +98,11 @@ CASES = [  # (name, B, H, S, d, dtype, mask builder)
      lambda: mask_family("sparse_random", 4096, seed=6)),
     ("entry counts at chunk and block boundaries", 1, 2, 1024, 64, "f16", entry_count_mask),
     ("entry counts at chunk and block boundaries d128", 2, 1, 1024, 128, "bf16", entry_count_mask),
+    # the other two (d, input type) instances of the gather path
+    ("band+2% causal d64 bf16", 1, 2, 768, 64, "bf16",
+     lambda: band_or_random(768, 96, 0.02, 41)),
+    ("far random causal 2% d128 f16", 1, 2, 1024, 128, "f16",
+     lambda: mask_family("far_random", 1024, seed=42)),
 ]
 
 
