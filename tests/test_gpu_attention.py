@@ -82,18 +82,31 @@ def test_edge_rows(kernel, dt):
     assert float((o.double().numpy() - ref).__abs__().max()) <= TOL[dt]
 
 
-@pytest.mark.parametrize("kernel", KERNELS)
-def test_in_dtype_output(kernel):
-    """Outputs in the input type: the rounding of O itself is included."""
+@pytest.mark.parametrize("kernel", KERNELS + ["auto"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_in_dtype_output(kernel, d):
+    """Outputs in the input type (the rounding of O itself is included) and
+    in fp32, for both input types and head sizes: every (d, input, output)
+    instance of the kernels, on a mask with sparse partial tiles as well."""
     dev = need_gpu()
-    S, d = 256, 128
-    mask = mask_family("causal", S)
+    S = 256
+    rng = np.random.default_rng(22)
+    mask = mask_family("causal", S) & ((rng.random((S, S)) < 0.02) |
+                                       (np.abs(np.subtract.outer(np.arange(S), np.arange(S))) < 40))
     for dt in ("f16", "bf16"):
         q, k, v = make_qkv(1, 4, S, d, dt, seed=21)
-        o = run(q, k, v, mask, kernel, None, dev)
-        assert o.dtype == TDT[dt]
-        err = maxerr(o, attention(q, k, v, mask))
-        assert err <= TOL[dt], f"{dt}: max abs err {err}"
+        ref = attention(q, k, v, mask)
+        for out_dt in (None, torch.float32):
+            if kernel == "auto":  # the single-launch kernel that decides on the device
+                enc = smh.encode_mask(torch.from_numpy(mask).to(dev))
+                o = smh.sparse_mha_fwd(q.to(dev), k.to(dev), v.to(dev), enc,
+                                       kernel="auto", out_dtype=out_dt)
+                torch.cuda.synchronize()
+            else:
+                o = run(q, k, v, mask, kernel, out_dt, dev)
+            assert o.dtype == (TDT[dt] if out_dt is None else torch.float32)
+            err = maxerr(o, ref)
+            assert err <= TOL[dt], f"{dt} -> {o.dtype}: max abs err {err}"
 
 
 def test_kernels_agree_and_deterministic():
