@@ -474,7 +474,7 @@ def main():
         write_traffic(args, workload(args)[0])
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus "
+        print(f"bench.py: the library runs on one GPU only; --gpus "
               f"{args.gpus} is not supported (the path needs no collective; "
               f"run --gpus 1)", file=sys.stderr)
         sys.exit(2)
